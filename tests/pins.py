@@ -1,0 +1,416 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each pin takes an ``oracle.Oracle`` (the real library, or a planted mutant
+built by the mutation test) and returns a list of failure messages; an empty
+list means the pin holds.  The pins are:
+
+* hand-worked routing cases (tests/golden/route_handworked.json);
+* pure-Python brute force on tiny inputs (tests/bruteforce.py);
+* closed forms and invariants that the mathematics fixes:
+  - softmax weights: sum to 1 and log(w_i) - log(w_j) = key_i - key_j;
+  - selection: every selected key >= every unselected key, ties to lower index;
+  - maps: a bijection on [0, R), stable inside each expert's segment;
+  - expand then combine with identity experts returns x bit for bit;
+  - SwiGLU: gate = 0 gives 0, silu(g) - silu(-g) = g, limits at +-inf,
+    linearity in u, and SciPy's own logistic function over every finite
+    bf16 gate value;
+  - bf16 rounding: torch's fp32 -> bf16 conversion on fp32 inputs, exact
+    table search on fp64 inputs, and the special values.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+import bruteforce as bf
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(tag: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([20260, tag]))
+
+
+def _bf16_vals(bits) -> np.ndarray:
+    return bf.bf16_to_float(bits)
+
+
+def _rand_bf16(rng, shape, scale=1.0) -> np.ndarray:
+    v = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return bf.bf16_round_exact_np(v.astype(np.float64))
+
+
+# ===================================================================== route
+def pin_route_golden(o) -> list:
+    fails = []
+    with open(os.path.join(GOLDEN, "route_handworked.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        logits = np.array(c["logits"], np.float32)
+        bias = None if c["bias"] is None else np.array(c["bias"], np.float32)
+        r = o.route(logits, c["k"], bias)
+        for key in ("topk_ids", "expert_counts", "expert_offsets", "dest_of_src", "src_of_dest"):
+            want = np.array(c[key]).reshape(-1)
+            if not np.array_equal(r[key].reshape(-1), want):
+                fails.append(f"golden {c['name']}: {key} {r[key].reshape(-1).tolist()} != {want.tolist()}")
+        w_want = np.array(c["topk_weights"], np.float64)
+        if not np.allclose(r["topk_weights"], w_want, rtol=1e-6, atol=1e-7):
+            fails.append(f"golden {c['name']}: weights {r['topk_weights'].tolist()} != {w_want.tolist()}")
+    return fails
+
+
+def _tiny_route_cases():
+    rng = _rng(1)
+    cases = []
+    for E in range(1, 7):
+        for k in range(1, E + 1):
+            T = 5
+            cases.append((rng.standard_normal((T, E)).astype(np.float32), k, None))
+            cases.append((rng.integers(-2, 3, (T, E)).astype(np.float32), k, None))  # many ties
+    # bias, signed zeros, all-equal rows
+    cases.append((rng.standard_normal((7, 8)).astype(np.float32), 3,
+                  (0.5 * rng.standard_normal(8)).astype(np.float32)))
+    z = np.where(rng.integers(0, 2, (6, 6)) == 0, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+    cases.append((z, 2, None))
+    cases.append((np.full((4, 6), 0.75, np.float32), 4, None))
+    return cases
+
+
+def pin_route_bruteforce(o) -> list:
+    fails = []
+    for logits, k, bias in _tiny_route_cases():
+        T, E = logits.shape
+        r = o.route(logits, k, bias)
+        ids_bf = bf.route_ids(logits, k, bias)
+        if not np.array_equal(r["topk_ids"], ids_bf):
+            fails.append(f"brute force ids T={T} E={E} k={k}: {r['topk_ids'].tolist()} != {ids_bf.tolist()}")
+            continue
+        counts, offsets, dest = bf.counts_offsets_dest(ids_bf, E)
+        for key, want in (("expert_counts", counts), ("expert_offsets", offsets), ("dest_of_src", dest)):
+            if not np.array_equal(r[key], want):
+                fails.append(f"brute force {key} E={E} k={k}: {r[key].tolist()} != {want.tolist()}")
+        src = np.empty_like(dest)
+        src[dest] = np.arange(dest.size, dtype=np.int32)
+        if not np.array_equal(r["src_of_dest"], src):
+            fails.append(f"brute force src_of_dest E={E} k={k}")
+    return fails
+
+
+def _keys(logits, bias):
+    return logits.astype(np.float32) + (bias.astype(np.float32) if bias is not None else np.float32(0))
+
+
+def check_route_properties(logits, k, bias, r) -> list:
+    """Properties any correct routing satisfies (used for the oracle here and
+    for sampled checks elsewhere)."""
+    fails = []
+    T, E = logits.shape
+    ids, w = r["topk_ids"], r["topk_weights"].astype(np.float64)
+    keys = _keys(logits, bias).astype(np.float64)
+    for t in range(T):
+        sel = [int(e) for e in ids[t]]
+        if len(set(sel)) != k or min(sel) < 0 or max(sel) >= E:
+            fails.append(f"row {t}: ids not k distinct experts: {sel}")
+            continue
+        ks = keys[t, sel]
+        if np.any(np.diff(ks) > 0):
+            fails.append(f"row {t}: slots not in descending key order")
+        for a in range(k - 1):  # equal keys inside the selection: lower index first
+            if ks[a] == ks[a + 1] and sel[a] > sel[a + 1]:
+                fails.append(f"row {t}: tie inside selection not in index order")
+        unsel = [e for e in range(E) if e not in sel]
+        if unsel:
+            mx = keys[t, unsel].max()
+            if ks.min() < mx:
+                fails.append(f"row {t}: an unselected key beats a selected one")
+            elif ks.min() == mx:
+                tied_sel = [e for e in sel if keys[t, e] == mx]
+                tied_un = [e for e in unsel if keys[t, e] == mx]
+                if max(tied_sel) > min(tied_un):
+                    fails.append(f"row {t}: boundary tie not broken toward the lower index")
+        s = w[t].sum()
+        if abs(s - 1.0) > 1e-6:
+            fails.append(f"row {t}: weights sum {s}")
+        if np.any(w[t] <= 0):
+            # exp underflow to zero needs key gaps > 100; not in these inputs
+            fails.append(f"row {t}: non-positive weight")
+            continue
+        lw = np.log(w[t])
+        d = (lw - lw[0]) - (ks - ks[0])
+        if np.max(np.abs(d)) > 2e-6 * max(1.0, np.max(np.abs(ks - ks[0]))):
+            fails.append(f"row {t}: log-weight differences != key differences (max dev {np.max(np.abs(d))})")
+    return fails
+
+
+def check_maps(ids, E, r) -> list:
+    fails = []
+    ids = np.asarray(ids).reshape(-1)
+    R = ids.size
+    counts, offsets = r["expert_counts"], r["expert_offsets"]
+    dest, src = r["dest_of_src"].reshape(-1), r["src_of_dest"].reshape(-1)
+    if counts.sum() != R:
+        fails.append(f"counts sum {counts.sum()} != R {R}")
+    if offsets[0] != 0 or offsets[E] != R or np.any(np.diff(offsets) != counts):
+        fails.append("offsets are not the exclusive prefix sum of counts")
+    if not np.array_equal(np.bincount(ids, minlength=E)[:E], counts):
+        fails.append("counts != histogram of ids")
+    if R and not np.array_equal(np.sort(dest), np.arange(R)):
+        fails.append("dest_of_src is not a permutation of [0,R)")
+        return fails
+    if R and not np.array_equal(src[dest], np.arange(R)):
+        fails.append("src_of_dest is not the inverse of dest_of_src")
+    seg = np.searchsorted(offsets, dest, side="right") - 1
+    if R and not np.array_equal(seg, ids):
+        fails.append("a row lies outside its expert's segment")
+    if R:  # inside each segment, source slots ascend
+        for e in range(E):
+            sl = src[offsets[e]:offsets[e + 1]]
+            if np.any(np.diff(sl) <= 0):
+                fails.append(f"segment of expert {e} is not in ascending slot order")
+                break
+    return fails
+
+
+def pin_route_properties(o) -> list:
+    fails = []
+    rng = _rng(2)
+    for (T, E, k, with_bias) in ((64, 8, 2, False), (40, 128, 8, False), (33, 256, 8, True), (50, 64, 6, False),
+                                 (20, 17, 5, True), (30, 512, 16, False)):
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        bias = (0.5 * rng.standard_normal(E)).astype(np.float32) if with_bias else None
+        r = o.route(logits, k, bias)
+        fails += check_route_properties(logits, k, bias, r)
+        fails += check_maps(r["topk_ids"], E, r)
+    # closed forms: k=1 -> weight exactly 1; all-equal keys -> ids 0..k-1, weights 1/k
+    r = o.route(rng.standard_normal((9, 12)).astype(np.float32), 1)
+    if not np.all(r["topk_weights"] == 1.0):
+        fails.append("k=1 weights are not exactly 1")
+    r = o.route(np.full((3, 10), -2.5, np.float32), 4)
+    if not (np.all(r["topk_ids"] == np.arange(4)) and np.allclose(r["topk_weights"], 0.25, rtol=0, atol=1e-7)):
+        fails.append("all-equal keys: ids != 0..k-1 or weights != 1/k")
+    # k=E -> the ids of a row are all experts sorted by key (desc, index asc)
+    lg = rng.integers(-3, 4, (6, 7)).astype(np.float32)
+    r = o.route(lg, 7)
+    for t in range(6):
+        want = sorted(range(7), key=lambda e: (-float(lg[t, e]), e))
+        if r["topk_ids"][t].tolist() != want:
+            fails.append(f"k=E row {t}: {r['topk_ids'][t].tolist()} != {want}")
+    # T = 0 is a valid empty batch
+    r = o.route(np.zeros((0, 5), np.float32), 2)
+    if r["expert_offsets"].tolist() != [0] * 6:
+        fails.append("T=0: offsets not all zero")
+    return fails
+
+
+# ===================================================================== expand
+def pin_expand(o) -> list:
+    fails = []
+    rng = _rng(3)
+    for (T, H, E, k) in ((13, 16, 8, 2), (9, 24, 5, 5), (20, 8, 64, 6), (1, 40, 3, 1)):
+        x = _rand_bf16(rng, (T, H))
+        r = o.route(rng.standard_normal((T, E)).astype(np.float32), k)
+        xe = o.expand_rows(x, r["dest_of_src"], k)
+        d = r["dest_of_src"]
+        for s in range(T * k):
+            if not np.array_equal(xe[d[s]], x[s // k]):
+                fails.append(f"expand T={T} H={H} k={k}: row {d[s]} != x[{s // k}]")
+                break
+        if not np.array_equal(xe, x[r["src_of_dest"] // k]):
+            fails.append(f"expand T={T}: x_exp[p] != x[src_of_dest[p] / k]")
+    return fails
+
+
+# ===================================================================== SwiGLU
+_FINITE_BF16 = np.array([b for b in range(0x10000) if (b & 0x7F80) != 0x7F80], dtype=np.uint16)
+
+
+def _swiglu_rows(o, gate_bits, up_bits):
+    """Run the oracle with one row per value pair (I=1), return act bits."""
+    h = np.stack([gate_bits, up_bits], axis=1).astype(np.uint16)
+    return o.swiglu(h).reshape(-1)
+
+
+def pin_swiglu_layout_and_identities(o) -> list:
+    fails = []
+    rng = _rng(4)
+    R, I = 6, 16
+    # gate (first I columns) = 0 -> output 0 whatever up holds; up = 0 -> output 0
+    h = _rand_bf16(rng, (R, 2 * I))
+    h0 = h.copy()
+    h0[:, :I] = 0
+    if np.any(_bf16_vals(o.swiglu(h0)) != 0):
+        fails.append("swiglu: gate = 0 (first half) does not give 0")
+    h1 = h.copy()
+    h1[:, I:] = 0
+    if np.any(_bf16_vals(o.swiglu(h1)) != 0):
+        fails.append("swiglu: up = 0 (second half) does not give 0")
+    # linearity in up: doubling up doubles the output exactly (power-of-two scaling)
+    up2 = bf.bf16_round_exact_np(2.0 * _bf16_vals(h[:, I:]))
+    h2 = h.copy()
+    h2[:, I:] = up2
+    a1, a2 = _bf16_vals(o.swiglu(h)), _bf16_vals(o.swiglu(h2))
+    if not np.array_equal(2.0 * a1, a2):
+        fails.append("swiglu: not linear in up")
+    # silu(g) - silu(-g) = g  (u = 1), within two bf16 roundings
+    g = _FINITE_BF16[(np.abs(_bf16_vals(_FINITE_BF16)) < 64) & (_bf16_vals(_FINITE_BF16) > 0)]
+    one = np.full(g.shape, 0x3F80, np.uint16)
+    pos = _bf16_vals(_swiglu_rows(o, g, one))
+    neg = _bf16_vals(_swiglu_rows(o, g ^ np.uint16(0x8000), one))
+    gv = _bf16_vals(g)
+    tol = 2.0 ** -8 * (np.abs(pos) + np.abs(neg)) + 1e-38
+    bad = np.abs((pos - neg) - gv) > tol
+    if np.any(bad):
+        i = int(np.argmax(bad))
+        fails.append(f"swiglu: silu(g)-silu(-g) != g at g={gv[i]} ({pos[i]} - {neg[i]})")
+    # limits: for g >= 32, silu(g) rounds to g; for g <= -128 it is a negative value below 1e-30
+    big = np.array([0x4200, 0x4300, 0x4780], np.uint16)  # 32, 128, 65536
+    if not np.array_equal(_swiglu_rows(o, big, np.full(3, 0x3F80, np.uint16)), big):
+        fails.append("swiglu: silu(g) != g for large g")
+    small = np.array([0xC300, 0xC780], np.uint16)  # -128, -65536
+    sv = _bf16_vals(_swiglu_rows(o, small, np.full(2, 0x3F80, np.uint16)))
+    if np.any(np.abs(sv) > 1e-30) or np.any(~np.signbit(sv)):
+        fails.append(f"swiglu: silu(g) for g -> -inf is not -0/-tiny: {sv}")
+    # slope 1/2 at 0: silu(g) ~= g/2 for tiny g
+    tiny = np.array([0x3A80, 0xBA80], np.uint16)  # +-2^-10
+    tv = _bf16_vals(_swiglu_rows(o, tiny, np.full(2, 0x3F80, np.uint16)))
+    want = _bf16_vals(tiny) / 2
+    if np.any(np.abs(tv - want) > 2.0 ** -8 * np.abs(want)):
+        fails.append(f"swiglu: silu'(0) != 1/2: {tv} vs {want}")
+    return fails
+
+
+def pin_swiglu_expit_exhaustive(o) -> list:
+    """Every finite bf16 gate value x u in {1, -1, 0.5, 3}: against SciPy's logistic."""
+    from scipy.special import expit
+
+    fails = []
+    gv = _bf16_vals(_FINITE_BF16)
+    for u_val, u_bits in ((1.0, 0x3F80), (-1.0, 0xBF80), (0.5, 0x3F00), (3.0, 0x4040)):
+        got = _swiglu_rows(o, _FINITE_BF16, np.full(_FINITE_BF16.shape, u_bits, np.uint16))
+        ref = gv * expit(gv) * u_val
+        want = bf.bf16_round_exact_np(ref)
+        bad = got != want
+        if np.any(bad):
+            # a mismatch is only acceptable if the fp64 value sits on a rounding midpoint
+            gvb, wv = _bf16_vals(got[bad]), _bf16_vals(want[bad])
+            mid = 0.5 * (gvb + wv)
+            near = np.abs(ref[bad] - mid) <= 1e-12 * np.abs(ref[bad])
+            if not np.all(near):
+                i = int(np.argmax(~near))
+                fails.append(f"swiglu vs expit u={u_val}: {int(np.sum(~near))} mismatches, e.g. g={gv[bad][i]} "
+                             f"got {gvb[i]} want {wv[i]}")
+    return fails
+
+
+# ===================================================================== combine
+def pin_combine_identity(o) -> list:
+    """Identity experts: combine(expand(x), w) == x bit for bit (sum w = 1 to
+    within k fp32 ulps, far below half a bf16 ulp)."""
+    fails = []
+    rng = _rng(5)
+    for (T, H, E, k) in ((17, 32, 8, 2), (12, 16, 128, 8), (10, 24, 64, 6), (8, 8, 4, 4), (6, 16, 9, 1)):
+        x = _rand_bf16(rng, (T, H))
+        r = o.route(rng.standard_normal((T, E)).astype(np.float32), k)
+        y = o.expand_rows(x, r["dest_of_src"], k)
+        out = o.combine(y, r["topk_weights"], r["dest_of_src"])
+        if not np.array_equal(out, x):
+            fails.append(f"combine(expand(x)) != x for T={T} H={H} E={E} k={k}")
+        # doubling the weights doubles the output exactly
+        out2 = o.combine(y, 2 * r["topk_weights"], r["dest_of_src"])
+        if not np.array_equal(_bf16_vals(out2), 2 * _bf16_vals(x)):
+            fails.append(f"combine not linear in w for T={T} k={k}")
+    return fails
+
+
+def pin_combine_bruteforce(o) -> list:
+    fails = []
+    rng = _rng(6)
+    for (T, H, E, k) in ((5, 8, 6, 3), (4, 16, 8, 2), (3, 8, 16, 8)):
+        r = o.route(rng.standard_normal((T, E)).astype(np.float32), k)
+        y = _rand_bf16(rng, (T * k, H))
+        w = (np.abs(rng.standard_normal((T, k))) + 0.1).astype(np.float32)  # not normalised on purpose
+        got = o.combine(y, w, r["dest_of_src"])
+        want, exact = bf.combine_exact(y, w, r["dest_of_src"])
+        bad = np.argwhere(got != want)
+        for t, c in bad:
+            # fp64 summation may only differ from the exact sum right at a midpoint
+            s = exact[t][c]
+            gv, wv = float(_bf16_vals(got[t, c])), float(_bf16_vals(want[t, c]))
+            if abs(float(s) - 0.5 * (gv + wv)) > 1e-12 * abs(float(s)):
+                fails.append(f"combine brute force T={T} k={k} at ({t},{c}): got {gv} want {wv}")
+                break
+    return fails
+
+
+# ===================================================================== bf16
+def pin_bf16_rounding(o) -> list:
+    import torch
+
+    fails = []
+    rng = _rng(7)
+    # (1) fp32 inputs: torch's fp32 -> bf16 (round to nearest even) is a library routine
+    f = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-39).astype(np.float32),            # fp32 subnormals
+        (np.clip(rng.standard_normal(2000), -3.3, 3.3) * 1e38).astype(np.float32),  # near overflow
+        np.array([0.0, -0.0, 1.0, -1.0, 1.00390625, 1.01171875, 3.3895314e38, 3.3961776e38], np.float32),
+        (np.arange(1, 2000, dtype=np.uint32) | np.uint32(0x3F800000)).view(np.float32),  # 1 + tiny ulps
+        ((np.arange(0, 4000, dtype=np.uint32) << 15) | np.uint32(0x3F808000)).view(np.float32),  # exact halves
+    ]).astype(np.float32)
+    f = f[np.isfinite(f)]
+    got = o.bf16_from_f64(f.astype(np.float64))
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if not np.array_equal(got, want):
+        i = int(np.argmax(got != want))
+        fails.append(f"bf16 rounding vs torch at {f[i]!r}: {got[i]:#06x} != {want[i]:#06x}")
+    # (2) fp64 inputs that fp32 cannot hold: exact table search
+    d = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-40, 38, 20000),
+                        1.0 + (2 * rng.integers(0, 128, 500) + 1) * 2.0 ** -8 + 2.0 ** -40])
+    got = o.bf16_from_f64(d)
+    want = bf.bf16_round_exact_np(d)
+    if not np.array_equal(got, want):
+        i = int(np.argmax(got != want))
+        fails.append(f"bf16 rounding vs exact at {d[i]!r}: {got[i]:#06x} != {want[i]:#06x}")
+    # (3) specials
+    specials = {float("inf"): 0x7F80, float("-inf"): 0xFF80, 3.5e38: 0x7F80, -3.5e38: 0xFF80, -0.0: 0x8000,
+                2.0 ** -133: 0x0001, 2.0 ** -134: 0x0000, 1.5 * 2.0 ** -133: 0x0002, 2.0 ** -126: 0x0080}
+    for v, b in specials.items():
+        g = int(o.bf16_from_f64(np.array([v]))[0])
+        if g != b:
+            fails.append(f"bf16 special {v!r}: {g:#06x} != {b:#06x}")
+    nan = int(o.bf16_from_f64(np.array([float("nan")]))[0])
+    if (nan & 0x7F80) != 0x7F80 or (nan & 0x7F) == 0:
+        fails.append(f"bf16 of NaN is not a NaN: {nan:#06x}")
+    # (4) bf16 -> f64 is exact on every finite pattern (round trip)
+    back = o.bf16_from_f64(np.array([o.lib.moe_ref_f64_from_bf16(int(b)) for b in _FINITE_BF16[::7]]))
+    if not np.array_equal(back, _FINITE_BF16[::7]):
+        fails.append("bf16 -> f64 -> bf16 is not the identity")
+    return fails
+
+
+ALL_PINS = [
+    pin_route_golden,
+    pin_route_bruteforce,
+    pin_route_properties,
+    pin_expand,
+    pin_swiglu_layout_and_identities,
+    pin_swiglu_expit_exhaustive,
+    pin_combine_identity,
+    pin_combine_bruteforce,
+    pin_bf16_rounding,
+]
+
+
+def run_all(o) -> dict:
+    out = {}
+    for p in ALL_PINS:
+        try:
+            out[p.__name__] = p(o)
+        except Exception as ex:  # a crash in a mutant counts as a caught mistake
+            out[p.__name__] = [f"exception: {type(ex).__name__}: {ex}"]
+    return out
+
+
+__all__ = ["ALL_PINS", "run_all", "check_route_properties", "check_maps"]
