@@ -1,0 +1,262 @@
+"""Benchmark of the MoE glue path on one MI355X.
+
+One step = the whole path on one batch: moe_route -> moe_expand_rows ->
+moe_swiglu -> moe_combine (the GEMM outputs are seeded stand-ins already in
+HBM).  The default workload is the Qwen3-30B-A3B-shaped prefill batch
+(T=4096, H=2048, E=128, k=8, I=768).
+
+Inputs are resident in HBM before the timed region.  Steps rotate over
+several complete input/output sets, so that no step finds its working set in
+the 256 MiB Infinity Cache left behind by the previous step on the same set.
+
+Prints ONE JSON line: whole-job tokens/s, per-call device times from HIP
+events recorded on the launch stream inside the timed region, the roofline of
+the dominant kernel, and the CPU oracle timed on the host as a baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE glue tokens/sec + achieved HBM GB/s (% of MI355X peak), Qwen3-30B-A3B shape"
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "moe_glue_amd", "csrc")
+KERNEL_SOURCES = {"route": "route.hip", "expand": "expand.hip", "swiglu": "swiglu.hip", "combine": "combine.hip"}
+
+
+def algorithmic_bytes(cfg) -> dict:
+    """Bytes each call must move: every input read once, every output written once."""
+    T, H, E, k, I, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.R
+    route = T * E * 4 + (E * 4 if cfg.bias_std > 0 else 0) + R * 4 + R * 4 + R * 4 + R * 4 + (E + 1) * 4 + E * 4
+    expand = T * H * 2 + R * 4 + R * H * 2
+    swiglu = R * 2 * I * 2 + R * I * 2
+    combine = R * H * 2 + R * 4 + R * 4 + T * H * 2
+    return {"route": route, "expand": expand, "swiglu": swiglu, "combine": combine}
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "device_common.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest(kernel):
+        return None
+    return rec.get("traffic_bytes")
+
+
+class Sets:
+    """NSETS complete input/output sets on the device, with ctypes argument tuples."""
+
+    def __init__(self, inp, nsets, dev):
+        import torch
+        import moe_glue_amd as mg
+
+        cfg = inp["cfg"]
+        self.cfg = cfg
+        self.lib = mg.load()
+        stream = torch.cuda.current_stream(dev).cuda_stream
+
+        def dev_bf16(a):
+            return torch.from_numpy(a.view("int16")).to(dev).view(torch.bfloat16)
+
+        base = {
+            "x": dev_bf16(inp["x"]),
+            "logits": torch.from_numpy(inp["logits"]).to(dev),
+            "bias": None if inp["bias"] is None else torch.from_numpy(inp["bias"]).to(dev),
+            "h": dev_bf16(inp["h"]),
+            "y": dev_bf16(inp["y"]),
+        }
+        self.sets = []
+        T, H, E, k, I, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.R
+        for s in range(nsets):
+            d = {key: (None if v is None else v.clone()) for key, v in base.items()}
+            d.update(mg.alloc_route_outputs(T, E, k, dev))
+            d["x_exp"] = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+            d["act"] = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
+            d["out"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            p = lambda key: 0 if d[key] is None else d[key].data_ptr()  # noqa: E731
+            d["args"] = {
+                "route": (p("logits"), p("bias"), T, E, k, p("topk_ids"), p("topk_weights"), p("expert_offsets"),
+                          p("expert_counts"), p("dest_of_src"), p("src_of_dest"), p("workspace"),
+                          d["workspace"].numel(), stream),
+                "expand": (p("x"), p("dest_of_src"), T, H, k, p("x_exp"), stream),
+                "swiglu": (p("h"), R, I, p("act"), stream),
+                "combine": (p("y"), p("topk_weights"), p("dest_of_src"), T, H, k, p("out"), stream),
+            }
+            self.sets.append(d)
+        self.fns = {"route": self.lib.moe_route, "expand": self.lib.moe_expand_rows,
+                    "swiglu": self.lib.moe_swiglu, "combine": self.lib.moe_combine}
+
+    def step(self, s, events=None):
+        a = self.sets[s % len(self.sets)]["args"]
+        f = self.fns
+        if events is not None:
+            events[0].record()
+        rc = f["route"](*a["route"])
+        if events is not None:
+            events[1].record()
+        rc |= f["expand"](*a["expand"])
+        if events is not None:
+            events[2].record()
+        rc |= f["swiglu"](*a["swiglu"])
+        if events is not None:
+            events[3].record()
+        rc |= f["combine"](*a["combine"])
+        if events is not None:
+            events[4].record()
+        if rc:
+            raise RuntimeError(f"a MoE glue call failed: {self.lib.moe_last_error().decode()}")
+
+
+def copy_probe_gbps(dev, nbytes=1 << 30, reps=5):
+    """Achievable HBM bandwidth: the library's 16 B/lane copy over 1 GiB."""
+    import torch
+    import moe_glue_amd as mg
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    mg.copy_probe(src, dst)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        mg.copy_probe(src, dst)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    del src, dst
+    t = sorted(times)[len(times) // 2]
+    return 2 * nbytes / t / 1e9, t
+
+
+def cpu_baseline(inp, passes=3):
+    """The CPU oracle as it stands, single-threaded, on the same workload."""
+    import oracle
+
+    o = oracle.get()
+    o.path(inp)  # warm: page in, build
+    times = []
+    for _ in range(passes):
+        t0 = time.perf_counter()
+        o.path(inp)
+        times.append(time.perf_counter() - t0)
+    t = sum(times) / len(times)
+    return {"value": inp["cfg"].T / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the full {inp['cfg'].name} batch (T={inp['cfg'].T}), route+expand+swiglu+combine, "
+                      f"mean of {passes} passes after one warm pass, single thread, {t:.3f} s per pass"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="qwen3_30b_a3b")
+    ap.add_argument("--sets", type=int, default=4, help="input/output sets rotated across steps")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-events", action="store_true", help="time steps without per-call HIP events")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by tokens, see the design notes)", file=sys.stderr)
+        return 2
+
+    import torch
+    from moe_glue_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    cfg = I.CONFIGS[args.config]
+    inp = I.make_inputs(cfg, args.seed)
+    sets = Sets(inp, args.sets, dev)
+    achievable, _ = copy_probe_gbps(dev)
+
+    for s in range(args.warmup):
+        sets.step(s)
+    torch.cuda.synchronize()
+
+    names = ["route", "expand", "swiglu", "combine"]
+    use_events = not args.no_events
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)] if use_events else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        sets.step(s, ev[s] if use_events else None)
+    host_s = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ab = algorithmic_bytes(cfg)
+    kernels = {}
+    if use_events:
+        for i, n in enumerate(names):
+            ms = [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]
+            us = 1e3 * sum(ms) / len(ms)
+            gbps = ab[n] / (us * 1e-6) / 1e9
+            kernels[n] = {"us": round(us, 3), "bytes": ab[n], "GBps": round(gbps, 1),
+                          "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                          "frac_of_achievable": round(gbps / achievable, 4)}
+    dominant = max(("expand", "swiglu", "combine"), key=lambda n: kernels[n]["us"]) if kernels else "combine"
+    roofline = None
+    if kernels:
+        d = kernels[dominant]
+        roofline = {"kernel": dominant, "bound": "hbm", "achieved": d["GBps"], "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": d["frac_of_peak"], "traffic": measured_traffic(dominant, cfg.name)}
+
+    ms_per_step = 1e3 * elapsed / args.steps
+    rec = {
+        "metric": METRIC,
+        "value": round(cfg.T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}", "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
+                   "input_sets": args.sets, "seed": args.seed},
+        "path_GBps": round(sum(ab.values()) / (elapsed / args.steps) / 1e9, 1),
+        "achievable_copy_GBps": round(achievable, 1),
+        "host_us_per_step": round(1e6 * host_s / args.steps, 2),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

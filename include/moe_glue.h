@@ -1,0 +1,159 @@
+/* moe_glue: the memory-bound data path around the expert GEMMs of a
+ * Mixture-of-Experts layer, for AMD Instinct MI355X (gfx950).
+ *
+ *   moe_route        softmax top-k routing, expert histogram, prefix-sum
+ *                    offsets and the token <-> expert-row permutation maps
+ *   moe_expand_rows  copy each token row to its k expert-contiguous rows
+ *   moe_swiglu       gated SiLU on the first grouped GEMM's output
+ *   moe_combine      routing-weighted sum of each token's k expert outputs
+ *
+ * The problem statement these calls follow:
+ *   - "CuTeDSL at Perplexity" (Perplexity blog), section "Mixture of Experts
+ *     (MoE) dispatch/combine", subsection "Local": dispatch counts the tokens
+ *     of each expert from the routing table and gives each token a unique
+ *     index inside its expert's list, then copies the tokens into a buffer for
+ *     the MoE GEMM; combine accumulates each token's expert outputs in
+ *     registers using those positions and writes the final token.
+ *   - FlashInfer PR analysis "CUTLASS MoE kernel optimisation: vectorisation
+ *     and dynamic thread allocation": expandInputRowsKernel (section 1),
+ *     doActivationKernel (sections 1-2) and the 16-byte row alignment
+ *     requirement (section 3).
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers, row-major and contiguous.
+ *     bf16 tensors are passed as uint16_t* holding raw bf16 bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on that stream and returns without synchronising.
+ *   - The caller allocates and owns every buffer, including the route
+ *     workspace.  The library never allocates or frees device memory and
+ *     keeps no state between calls, so calls on different streams do not
+ *     interfere unless their buffers overlap.
+ *   - Inputs must not alias outputs.
+ *   - Argument errors are detected on the host BEFORE any HIP call: the call
+ *     returns a non-OK status, records a message (moe_last_error) and
+ *     enqueues nothing.  A launch failure returns MOE_ERR_HIP.
+ *   - Notation: T tokens, H hidden size, E experts, k experts per token,
+ *     I expert intermediate size, R = T*k expanded rows, slot s = t*k + j.
+ */
+#ifndef MOE_GLUE_H
+#define MOE_GLUE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,        /* a required pointer is NULL                          */
+    MOE_ERR_SHAPE = 2,       /* a size is negative, zero where it may not be, or k > E */
+    MOE_ERR_ALIGN = 3,       /* a bf16 row is not a multiple of 16 bytes, or a
+                                pointer is not 16-byte aligned                     */
+    MOE_ERR_UNSUPPORTED = 4, /* beyond a limit below (E, k, element counts)         */
+    MOE_ERR_WORKSPACE = 5,   /* route workspace missing or too small                */
+    MOE_ERR_HIP = 6          /* the HIP runtime reported an error at launch         */
+} moe_status;
+
+#define MOE_E_MAX 512        /* experts                                             */
+#define MOE_K_MAX 16         /* experts per token                                   */
+
+/* ------------------------------------------------------------------ route */
+
+/* Bytes of device workspace moe_route needs for (T, E, k); 0 is never
+ * returned for valid arguments, and a negative/invalid argument gives 0.
+ * The workspace needs no initialisation and may be reused by later calls on
+ * the same stream. */
+size_t moe_route_workspace_bytes(int32_t T, int32_t E, int32_t k);
+
+/* Softmax top-k routing plus dispatch bookkeeping ("CuTeDSL at Perplexity",
+ * MoE dispatch/combine > Local: per-expert token counts and a unique index for
+ * each token inside its expert's list).  The pages print no gate function;
+ * this call computes, for every token t:
+ *   key[e]      = fp32(logits[t,e] + bias[e])   (bias may be NULL: key = logit)
+ *   topk_ids[t,j], j = 0..k-1: the experts of the k largest keys, in
+ *                 descending key order; equal keys (-0 == +0) go to the lower
+ *                 expert index.
+ *   topk_weights[t,j] = exp(key_j - key_0) / sum_i exp(key_i - key_0)
+ *                 (softmax over the selected keys; fp32).
+ * and for the whole batch:
+ *   expert_counts[e]  = number of slots s with topk_ids[s] == e   (may be NULL)
+ *   expert_offsets[e] = sum of counts of experts below e; expert_offsets[E] = T*k
+ *   dest_of_src[s]    = expert_offsets[topk_ids[s]] + number of slots s' < s
+ *                       with the same expert (ascending token order inside
+ *                       each expert's segment; no padding)
+ *   src_of_dest[dest_of_src[s]] = s.
+ * Layouts: logits fp32 [T,E]; bias fp32 [E]; topk_ids int32 [T,k];
+ * topk_weights fp32 [T,k]; expert_offsets int32 [E+1]; expert_counts int32 [E];
+ * dest_of_src, src_of_dest int32 [T*k].  logits and bias need 4-byte alignment.
+ * Limits: 1 <= E <= MOE_E_MAX, 1 <= k <= min(E, MOE_K_MAX), T*E < 2^31.
+ * T = 0 is valid: offsets (and counts) become all zeros.
+ * Logits and bias must be finite (NaN ordering is unspecified).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE,
+ * MOE_ERR_HIP. */
+moe_status moe_route(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                     int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                     int32_t* expert_counts, int32_t* dest_of_src, int32_t* src_of_dest,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------- expand */
+
+/* expandInputRows (FlashInfer PR analysis, section 1): the copy of each token
+ * row into the expert-contiguous buffer the grouped GEMM reads:
+ *   x_expanded[dest_of_src[t*k + j], :] = x[t, :]     for j = 0..k-1
+ * x bf16 [T,H]; dest_of_src int32 [T*k] (from moe_route with the same T, k);
+ * x_expanded bf16 [T*k, H].
+ * Alignment (section 3 of the same page): H*2 bytes must be a multiple of 16
+ * (H % 8 == 0) and x, x_expanded 16-byte aligned, else MOE_ERR_ALIGN.
+ * dest_of_src must be a permutation of [0, T*k) (not checked).
+ * T = 0 is a no-op.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN,
+ * MOE_ERR_UNSUPPORTED (T*H/8 >= 2^31), MOE_ERR_HIP. */
+moe_status moe_expand_rows(const uint16_t* x, const int32_t* dest_of_src, int32_t T, int32_t H,
+                           int32_t k, uint16_t* x_expanded, void* stream);
+
+/* ----------------------------------------------------------------- SwiGLU */
+
+/* doActivation (FlashInfer PR analysis, sections 1-2): gated SiLU on the first
+ * grouped GEMM's output, row by row:
+ *   act[r, i] = bf16( silu(g) * u ),  g = h[r, i], u = h[r, I + i],
+ *   silu(g) = g / (1 + exp(-g)), computed in fp32, rounded to nearest even.
+ * h bf16 [R, 2I] (gate columns 0..I-1, up columns I..2I-1); act bf16 [R, I].
+ * I % 8 == 0 and h, act 16-byte aligned, else MOE_ERR_ALIGN.
+ * R = 0 is a no-op.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN,
+ * MOE_ERR_UNSUPPORTED (R*I/8 >= 2^31), MOE_ERR_HIP. */
+moe_status moe_swiglu(const uint16_t* h, int32_t R, int32_t I, uint16_t* act, void* stream);
+
+/* ---------------------------------------------------------------- combine */
+
+/* Combine ("CuTeDSL at Perplexity", MoE dispatch/combine, opening paragraph
+ * and "Local": weighted accumulation in registers using dispatch's positions):
+ *   out[t, :] = bf16( sum_{j=0..k-1} topk_weights[t,j] * y[dest_of_src[t*k+j], :] )
+ * accumulated in fp32 in j order, rounded once to nearest even.
+ * y bf16 [T*k, H]; topk_weights fp32 [T,k]; dest_of_src int32 [T*k];
+ * out bf16 [T, H].  H % 8 == 0 and y, out 16-byte aligned, else MOE_ERR_ALIGN.
+ * dest_of_src entries must lie in [0, T*k) (not checked).
+ * T = 0 is a no-op.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN,
+ * MOE_ERR_UNSUPPORTED (T*H/8 >= 2^31), MOE_ERR_HIP. */
+moe_status moe_combine(const uint16_t* y, const float* topk_weights, const int32_t* dest_of_src,
+                       int32_t T, int32_t H, int32_t k, uint16_t* out, void* stream);
+
+/* -------------------------------------------------------------- utilities */
+
+/* Plain streaming copy of `bytes` bytes (a multiple of 16; both pointers
+ * 16-byte aligned), 16 bytes per lane.  It is the measuring stick for
+ * achievable HBM bandwidth and for calibrating traffic counters; it is not
+ * part of the MoE path.  Errors: MOE_ERR_NULL, MOE_ERR_ALIGN, MOE_ERR_HIP. */
+moe_status moe_copy_probe(const void* src, void* dst, size_t bytes, void* stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status s);
+
+/* Detail text for the last non-OK status returned on the calling thread
+ * ("" if none).  Valid until the next call on the same thread. */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_GLUE_H */

@@ -1,0 +1,160 @@
+"""moe_glue_amd: the memory-bound Mixture-of-Experts glue path on MI355X (gfx950).
+
+Four calls, each a thin wrapper over the C ABI of the HIP library
+(include/moe_glue.h):
+
+    route(logits, k, bias=None)        softmax top-k, expert counts/offsets,
+                                       permutation maps
+    expand_rows(x, dest_of_src, k)     expandInputRows: token rows -> expert rows
+    swiglu(h)                          doActivation: silu(gate) * up
+    combine(y, topk_weights, dest_of_src)  weighted sum back to token order
+
+Tensors are torch CUDA (HIP) tensors; bf16 tensors use torch.bfloat16.  Work
+is enqueued on torch's current stream and nothing synchronises.  Every call
+accepts preallocated outputs (``out=`` / the route output dict) so a caller
+can run the path without allocating.
+"""
+from __future__ import annotations
+
+from ._binding import (E_MAX, EXPORTED, K_MAX, LIB_PATH, MoEGlueArgumentError, MoEGlueError, check,  # noqa: F401
+                       load)
+
+__all__ = ["route", "route_workspace_bytes", "alloc_route_outputs", "expand_rows", "swiglu", "combine",
+           "copy_probe", "MoEGlueError", "MoEGlueArgumentError", "E_MAX", "K_MAX"]
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _need_gpu(name: str, t, dtype=None, ndim=None) -> None:
+    if t is None:
+        raise MoEGlueArgumentError(1, f"{name} is required")
+    if not t.is_cuda:
+        raise MoEGlueArgumentError(2, f"{name} must be a GPU tensor (got device {t.device})")
+    if not t.is_contiguous():
+        raise MoEGlueArgumentError(2, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise MoEGlueArgumentError(2, f"{name} must be {dtype} (got {t.dtype})")
+    if ndim is not None and t.dim() != ndim:
+        raise MoEGlueArgumentError(2, f"{name} must have {ndim} dims (got shape {tuple(t.shape)})")
+
+
+def route_workspace_bytes(T: int, E: int, k: int) -> int:
+    return int(load().moe_route_workspace_bytes(T, E, k))
+
+
+def alloc_route_outputs(T: int, E: int, k: int, device) -> dict:
+    """Device buffers for route(): ids, weights, offsets, counts, maps, workspace."""
+    torch = _torch()
+    i32, f32 = torch.int32, torch.float32
+    return {
+        "topk_ids": torch.empty((T, k), dtype=i32, device=device),
+        "topk_weights": torch.empty((T, k), dtype=f32, device=device),
+        "expert_offsets": torch.empty((E + 1,), dtype=i32, device=device),
+        "expert_counts": torch.empty((E,), dtype=i32, device=device),
+        "dest_of_src": torch.empty((T * k,), dtype=i32, device=device),
+        "src_of_dest": torch.empty((T * k,), dtype=i32, device=device),
+        "workspace": torch.empty((max(16, route_workspace_bytes(T, E, k)),), dtype=torch.uint8, device=device),
+    }
+
+
+def route(logits, k: int, bias=None, out: dict | None = None) -> dict:
+    """Softmax top-k routing and dispatch bookkeeping; see moe_route in include/moe_glue.h."""
+    torch = _torch()
+    _need_gpu("logits", logits, torch.float32, 2)
+    T, E = logits.shape
+    if bias is not None:
+        _need_gpu("bias", bias, torch.float32, 1)
+        if bias.shape[0] != E:
+            raise MoEGlueArgumentError(2, f"bias has {bias.shape[0]} entries, logits has E={E}")
+    if out is None:
+        out = alloc_route_outputs(T, E, k, logits.device)
+    ws = out["workspace"]
+    lib = load()
+    st = lib.moe_route(_ptr(logits), _ptr(bias), T, E, k, _ptr(out["topk_ids"]), _ptr(out["topk_weights"]),
+                       _ptr(out["expert_offsets"]), _ptr(out.get("expert_counts")), _ptr(out["dest_of_src"]),
+                       _ptr(out["src_of_dest"]), _ptr(ws), ws.numel() if ws is not None else 0,
+                       _stream(logits.device))
+    check(st, "moe_route")
+    return out
+
+
+def expand_rows(x, dest_of_src, k: int, out=None):
+    """x_expanded[dest_of_src[t*k+j]] = x[t]; see moe_expand_rows in include/moe_glue.h."""
+    torch = _torch()
+    _need_gpu("x", x, torch.bfloat16, 2)
+    _need_gpu("dest_of_src", dest_of_src, torch.int32)
+    T, H = x.shape
+    if dest_of_src.numel() != T * k:
+        raise MoEGlueArgumentError(2, f"dest_of_src has {dest_of_src.numel()} entries, expected T*k={T * k}")
+    if out is None:
+        out = torch.empty((T * k, H), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need_gpu("out", out, torch.bfloat16, 2)
+        if tuple(out.shape) != (T * k, H):
+            raise MoEGlueArgumentError(2, f"out must be [{T * k}, {H}]")
+    st = load().moe_expand_rows(_ptr(x), _ptr(dest_of_src), T, H, k, _ptr(out), _stream(x.device))
+    check(st, "moe_expand_rows")
+    return out
+
+
+def swiglu(h, out=None):
+    """act = silu(h[:, :I]) * h[:, I:]; see moe_swiglu in include/moe_glue.h."""
+    torch = _torch()
+    _need_gpu("h", h, torch.bfloat16, 2)
+    R, I2 = h.shape
+    if I2 % 2:
+        raise MoEGlueArgumentError(2, f"h has an odd width {I2}; expected [R, 2I]")
+    I = I2 // 2
+    if out is None:
+        out = torch.empty((R, I), dtype=torch.bfloat16, device=h.device)
+    else:
+        _need_gpu("out", out, torch.bfloat16, 2)
+        if tuple(out.shape) != (R, I):
+            raise MoEGlueArgumentError(2, f"out must be [{R}, {I}]")
+    st = load().moe_swiglu(_ptr(h), R, I, _ptr(out), _stream(h.device))
+    check(st, "moe_swiglu")
+    return out
+
+
+def combine(y, topk_weights, dest_of_src, out=None):
+    """out[t] = sum_j w[t,j] * y[dest_of_src[t*k+j]]; see moe_combine in include/moe_glue.h."""
+    torch = _torch()
+    _need_gpu("y", y, torch.bfloat16, 2)
+    _need_gpu("topk_weights", topk_weights, torch.float32, 2)
+    _need_gpu("dest_of_src", dest_of_src, torch.int32)
+    T, k = topk_weights.shape
+    R, H = y.shape
+    if R != T * k or dest_of_src.numel() != R:
+        raise MoEGlueArgumentError(2, f"y has {R} rows and dest_of_src {dest_of_src.numel()}, expected T*k={T * k}")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    else:
+        _need_gpu("out", out, torch.bfloat16, 2)
+        if tuple(out.shape) != (T, H):
+            raise MoEGlueArgumentError(2, f"out must be [{T}, {H}]")
+    st = load().moe_combine(_ptr(y), _ptr(topk_weights), _ptr(dest_of_src), T, H, k, _ptr(out), _stream(y.device))
+    check(st, "moe_combine")
+    return out
+
+
+def copy_probe(src, dst) -> None:
+    """Plain 16-byte-per-lane copy of src's bytes into dst (bandwidth measuring stick)."""
+    _need_gpu("src", src)
+    _need_gpu("dst", dst)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise MoEGlueArgumentError(2, "dst is smaller than src")
+    check(load().moe_copy_probe(_ptr(src), _ptr(dst), nbytes, _stream(src.device)), "moe_copy_probe")

@@ -1,0 +1,170 @@
+// The C ABI of moe_glue (declared in include/moe_glue.h): argument checks on
+// the host, variant choice, launch.  Every check runs before the first HIP
+// call, so a bad argument never reaches the device.
+#include "moe_glue.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+moe_status ok() {
+    g_last_error[0] = '\0';
+    return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+moe_status from_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Route variant override for tests and measurements:
+// MOE_GLUE_ROUTE_VARIANT = auto | single | multi.
+moe::RouteVariant requested_route_variant() {
+    const char* v = std::getenv("MOE_GLUE_ROUTE_VARIANT");
+    if (v == nullptr || std::strcmp(v, "auto") == 0) return moe::RouteVariant::Auto;
+    if (std::strcmp(v, "single") == 0) return moe::RouteVariant::SingleWorkgroup;
+    if (std::strcmp(v, "multi") == 0) return moe::RouteVariant::MultiWorkgroup;
+    return moe::RouteVariant::Auto;
+}
+
+moe_status check_route_sizes(int32_t T, int32_t E, int32_t k) {
+    if (T < 0) return fail(MOE_ERR_SHAPE, "moe_route: T=%d is negative", T);
+    if (E < 1) return fail(MOE_ERR_SHAPE, "moe_route: E=%d must be >= 1", E);
+    if (k < 1 || k > E) return fail(MOE_ERR_SHAPE, "moe_route: k=%d must be in [1, E=%d]", k, E);
+    if (E > MOE_E_MAX) return fail(MOE_ERR_UNSUPPORTED, "moe_route: E=%d exceeds %d", E, MOE_E_MAX);
+    if (k > MOE_K_MAX) return fail(MOE_ERR_UNSUPPORTED, "moe_route: k=%d exceeds %d", k, MOE_K_MAX);
+    if ((int64_t)T * E >= INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "moe_route: T*E=%lld too large",
+                                                 (long long)T * E);
+    return MOE_OK;
+}
+
+// bf16 row tensors: sizes, 16-byte rows (H % 8 == 0), element count in range.
+moe_status check_rows(const char* fn, int32_t rows, int32_t width, const char* wname) {
+    if (rows < 0) return fail(MOE_ERR_SHAPE, "%s: row count %d is negative", fn, rows);
+    if (width < 1) return fail(MOE_ERR_SHAPE, "%s: %s=%d must be >= 1", fn, wname, width);
+    if (width % 8 != 0)
+        return fail(MOE_ERR_ALIGN, "%s: %s=%d: bf16 rows must be a multiple of 16 bytes (%s %% 8 == 0)", fn, wname,
+                    width, wname);
+    if ((int64_t)rows * (width / 8) >= INT32_MAX)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: %lld 16-byte vectors exceed the 2^31 limit", fn,
+                    (long long)rows * (width / 8));
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_NULL: return "MOE_ERR_NULL";
+        case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
+        case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    }
+    return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+size_t moe_route_workspace_bytes(int32_t T, int32_t E, int32_t k) {
+    if (check_route_sizes(T, E, k) != MOE_OK) return 0;
+    return moe::route_workspace_bytes(T, E);
+}
+
+moe_status moe_route(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k, int32_t* topk_ids,
+                     float* topk_weights, int32_t* expert_offsets, int32_t* expert_counts, int32_t* dest_of_src,
+                     int32_t* src_of_dest, void* workspace, size_t workspace_bytes, void* stream) {
+    moe_status s = check_route_sizes(T, E, k);
+    if (s != MOE_OK) return s;
+    if (expert_offsets == nullptr) return fail(MOE_ERR_NULL, "moe_route: expert_offsets is NULL");
+    if (T > 0) {
+        if (!logits || !topk_ids || !topk_weights || !dest_of_src || !src_of_dest)
+            return fail(MOE_ERR_NULL, "moe_route: a required tensor pointer is NULL");
+        if (!aligned4(logits) || (bias && !aligned4(bias)))
+            return fail(MOE_ERR_ALIGN, "moe_route: logits/bias must be 4-byte aligned");
+    }
+    const moe::RouteVariant v = moe::route_pick_variant(T, requested_route_variant());
+    if (v == moe::RouteVariant::MultiWorkgroup) {
+        const size_t need = moe::route_workspace_bytes(T, E);
+        if (workspace == nullptr || workspace_bytes < need)
+            return fail(MOE_ERR_WORKSPACE, "moe_route: workspace of %zu bytes needed, %zu given%s", need,
+                        workspace_bytes, workspace ? "" : " (NULL)");
+        if (!aligned16(workspace)) return fail(MOE_ERR_WORKSPACE, "moe_route: workspace must be 16-byte aligned");
+    }
+    moe::RouteArgs a{logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, expert_counts,
+                     dest_of_src, src_of_dest, workspace};
+    return from_hip(moe::launch_route(a, v, static_cast<hipStream_t>(stream)), "moe_route launch");
+}
+
+moe_status moe_expand_rows(const uint16_t* x, const int32_t* dest_of_src, int32_t T, int32_t H, int32_t k,
+                           uint16_t* x_expanded, void* stream) {
+    moe_status s = check_rows("moe_expand_rows", T, H, "H");
+    if (s != MOE_OK) return s;
+    if (k < 1 || k > MOE_K_MAX) return fail(MOE_ERR_SHAPE, "moe_expand_rows: k=%d must be in [1, %d]", k, MOE_K_MAX);
+    if ((int64_t)T * k >= INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "moe_expand_rows: T*k too large");
+    if (T == 0) return ok();
+    if (!x || !dest_of_src || !x_expanded) return fail(MOE_ERR_NULL, "moe_expand_rows: NULL tensor pointer");
+    if (!aligned16(x) || !aligned16(x_expanded))
+        return fail(MOE_ERR_ALIGN, "moe_expand_rows: x and x_expanded must be 16-byte aligned");
+    return from_hip(moe::launch_expand_rows(x, dest_of_src, T, H, k, x_expanded, static_cast<hipStream_t>(stream)),
+                    "moe_expand_rows launch");
+}
+
+moe_status moe_swiglu(const uint16_t* h, int32_t R, int32_t I, uint16_t* act, void* stream) {
+    moe_status s = check_rows("moe_swiglu", R, I, "I");
+    if (s != MOE_OK) return s;
+    if ((int64_t)R * (2 * (int64_t)I / 8) >= INT32_MAX)
+        return fail(MOE_ERR_UNSUPPORTED, "moe_swiglu: R*2I too large");
+    if (R == 0) return ok();
+    if (!h || !act) return fail(MOE_ERR_NULL, "moe_swiglu: NULL tensor pointer");
+    if (!aligned16(h) || !aligned16(act)) return fail(MOE_ERR_ALIGN, "moe_swiglu: h and act must be 16-byte aligned");
+    return from_hip(moe::launch_swiglu(h, R, I, act, static_cast<hipStream_t>(stream)), "moe_swiglu launch");
+}
+
+moe_status moe_combine(const uint16_t* y, const float* topk_weights, const int32_t* dest_of_src, int32_t T,
+                       int32_t H, int32_t k, uint16_t* out, void* stream) {
+    moe_status s = check_rows("moe_combine", T, H, "H");
+    if (s != MOE_OK) return s;
+    if (k < 1 || k > MOE_K_MAX) return fail(MOE_ERR_SHAPE, "moe_combine: k=%d must be in [1, %d]", k, MOE_K_MAX);
+    if ((int64_t)T * k >= INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "moe_combine: T*k too large");
+    if (T == 0) return ok();
+    if (!y || !topk_weights || !dest_of_src || !out) return fail(MOE_ERR_NULL, "moe_combine: NULL tensor pointer");
+    if (!aligned16(y) || !aligned16(out)) return fail(MOE_ERR_ALIGN, "moe_combine: y and out must be 16-byte aligned");
+    if (!aligned4(topk_weights)) return fail(MOE_ERR_ALIGN, "moe_combine: topk_weights must be 4-byte aligned");
+    return from_hip(moe::launch_combine(y, topk_weights, dest_of_src, T, H, k, out, static_cast<hipStream_t>(stream)),
+                    "moe_combine launch");
+}
+
+moe_status moe_copy_probe(const void* src, void* dst, size_t bytes, void* stream) {
+    if (bytes == 0) return ok();
+    if (!src || !dst) return fail(MOE_ERR_NULL, "moe_copy_probe: NULL pointer");
+    if (bytes % 16 != 0 || !aligned16(src) || !aligned16(dst))
+        return fail(MOE_ERR_ALIGN, "moe_copy_probe: size and pointers must be multiples of 16 bytes");
+    return from_hip(moe::launch_copy_probe(src, dst, bytes, static_cast<hipStream_t>(stream)), "moe_copy_probe launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// moe_combine on gfx950: the weighted accumulation of each token's k expert
+// outputs back into token order ("CuTeDSL at Perplexity", MoE
+// dispatch/combine: accumulation in registers, vectorised, using the
+// positions dispatch computed).
+//
+// Token-major gather: a work item is one 16-byte vector (8 bf16) of one output
+// token row; items are numbered row-major over [T, H/8].  The lane issues the
+// k 16-byte loads of its column from the k expert rows at once (k independent
+// loads in flight), accumulates w_j * y_j in fp32 in j order in registers and
+// stores one rounded 16-byte vector.  No atomics, so the result is
+// deterministic.  When a row is a whole number of waves the token index is
+// wave-uniform and its k weights and k row indices come in by scalar loads.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kKMax = 16;
+
+template <bool ROW_PER_WAVE>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const u32x4* __restrict__ y,
+                                                           const float* __restrict__ w,
+                                                           const int32_t* __restrict__ dest_of_src, uint32_t n,
+                                                           uint32_t H16, FastDiv div_h16, int k,
+                                                           u32x4* __restrict__ out) {
+    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    uint32_t t = fastdiv(i, div_h16);
+    if constexpr (ROW_PER_WAVE) t = uniform(t);
+    const uint32_t c = i - t * H16;
+    const int32_t* d = dest_of_src + (size_t)t * k;
+    const float* wt = w + (size_t)t * k;
+
+    // Fetch all k row indices and weights before the first row load: the
+    // clamped index keeps every fetch unconditional and in bounds, so the
+    // fetches issue back to back under one wait.
+    int32_t dj[kKMax];
+    float wj[kKMax];
+#pragma unroll
+    for (int j = 0; j < kKMax; ++j) {
+        const int jj = j < k ? j : k - 1;
+        dj[j] = d[jj];
+        wj[j] = wt[jj];
+    }
+    u32x4 v[kKMax];
+#pragma unroll
+    for (int j = 0; j < kKMax; ++j)
+        if (j < k) v[j] = load_stream(y + (size_t)dj[j] * H16 + c);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kKMax; ++j) {
+        if (j < k) {
+            float f[8];
+            unpack8(v[j], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(wj[j], f[e], acc[e]);
+        }
+    }
+    store_stream(out + i, pack8(acc));
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* y, const float* topk_weights, const int32_t* dest_of_src, int T, int H,
+                          int k, void* out, hipStream_t stream) {
+    const uint32_t H16 = (uint32_t)H / 8;
+    const uint32_t n = (uint32_t)T * H16;
+    const uint32_t blocks = (n + kThreads - 1) / kThreads;
+    const FastDiv dv = make_fastdiv(H16);
+    const u32x4* ys = static_cast<const u32x4*>(y);
+    u32x4* o = static_cast<u32x4*>(out);
+    if (H16 % kWave == 0)
+        combine_kernel<true><<<blocks, kThreads, 0, stream>>>(ys, topk_weights, dest_of_src, n, H16, dv, k, o);
+    else
+        combine_kernel<false><<<blocks, kThreads, 0, stream>>>(ys, topk_weights, dest_of_src, n, H16, dv, k, o);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,78 @@
+// moe_swiglu on gfx950: doActivation (FlashInfer PR analysis, sections 1-2)
+// -- gated SiLU over the first grouped GEMM's output.
+//
+// The page's fix for this kernel sizes the threads of a row to the
+// intermediate size (a fixed 256 threads per row idled most warps at I=768)
+// and sizes the grid per SM.  On wave64 the natural form of that idea is to
+// drop the per-row thread block altogether: a work item is one 16-byte vector
+// of 8 outputs, items are numbered row-major over [R, I/8] and lanes take
+// consecutive items, so no lane idles whatever I is (I=768 gives 96 items
+// per row; 2 rows fill 3 waves exactly).  Each item reads 16 B of gate and
+// 16 B of up and writes 16 B.  U items per lane keep 2U loads in flight.
+//
+// Arithmetic: silu(g) * u in fp32 with the hardware exp2 and reciprocal
+// (v_exp_f32, v_rcp_f32), one round-to-nearest-even conversion per output
+// (v_cvt_pk_bf16_f32).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    // g / (1 + e^-g); e^-g = 2^(-g * log2 e).  For g << 0 the exponential is
+    // +inf and the quotient is -0; for g >> 0 it is 0 and the quotient is g.
+    const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+template <int U>
+__global__ __launch_bounds__(kThreads) void swiglu_kernel(const u32x4* __restrict__ h, uint32_t n, uint32_t I8,
+                                                          FastDiv div_i8, u32x4* __restrict__ act) {
+    const uint32_t base = blockIdx.x * (kThreads * U) + threadIdx.x;
+    u32x4 gv[U], uv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t i = base + u * kThreads;
+        if (i < n) {
+            const uint32_t r = fastdiv(i, div_i8);
+            const size_t gi = (size_t)r * (2 * I8) + (i - r * I8);
+            gv[u] = load_stream(h + gi);
+            uv[u] = load_stream(h + gi + I8);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t i = base + u * kThreads;
+        if (i < n) {
+            float g[8], up[8], o[8];
+            unpack8(gv[u], g);
+            unpack8(uv[u], up);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = silu_mul(g[e], up[e]);
+            store_stream(act + i, pack8(o));
+        }
+    }
+}
+
+template <int U>
+hipError_t launch_u(const void* h, int R, int I, void* act, hipStream_t stream) {
+    const uint32_t I8 = (uint32_t)I / 8;
+    const uint32_t n = (uint32_t)R * I8;
+    const uint32_t blocks = (n + kThreads * U - 1) / (kThreads * U);
+    swiglu_kernel<U><<<blocks, kThreads, 0, stream>>>(static_cast<const u32x4*>(h), n, I8, make_fastdiv(I8),
+                                                      static_cast<u32x4*>(act));
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_swiglu(const void* h, int R, int I, void* act, hipStream_t stream) {
+    const size_t n = (size_t)R * (I / 8);
+    if (n < (size_t)256 * kThreads * 2) return launch_u<1>(h, R, I, act, stream);
+    return launch_u<2>(h, R, I, act, stream);
+}
+
+}  // namespace moe

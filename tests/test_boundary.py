@@ -1,0 +1,158 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point,
+and rejects bad arguments with the documented status BEFORE any HIP call (so
+these run without a GPU).  Also checks the host-side helpers."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_glue.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from moe_glue_amd import build as mbuild
+    from moe_glue_amd import _binding
+
+    if mbuild.is_stale():
+        mbuild.build(verbose=False)
+    return _binding.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("moe_route", "moe_expand_rows", "moe_swiglu", "moe_combine", "moe_route_workspace_bytes",
+              "moe_status_string", "moe_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in include/moe_glue.h but not exported"
+
+
+def test_binding_names_match_header():
+    from moe_glue_amd import _binding
+
+    assert set(_binding.EXPORTED) == set(declared_functions())
+
+
+FAKE = 0x10000  # a 16-byte-aligned non-NULL address: never dereferenced, since validation fails first
+
+
+def status(lib, rc):
+    return lib.moe_status_string(rc).decode()
+
+
+def test_route_argument_errors(lib):
+    ws = 1 << 20
+    args = lambda T, E, k, ids=FAKE, off=FAKE, wsp=FAKE, logits=FAKE: (
+        logits, None, T, E, k, ids, FAKE, off, None, FAKE, FAKE, wsp, ws, None)
+    assert status(lib, lib.moe_route(*args(-1, 8, 2))) == "MOE_ERR_SHAPE"
+    assert status(lib, lib.moe_route(*args(4, 0, 1))) == "MOE_ERR_SHAPE"
+    assert status(lib, lib.moe_route(*args(4, 8, 0))) == "MOE_ERR_SHAPE"
+    assert status(lib, lib.moe_route(*args(4, 8, 9))) == "MOE_ERR_SHAPE"
+    assert status(lib, lib.moe_route(*args(4, 513, 2))) == "MOE_ERR_UNSUPPORTED"
+    assert status(lib, lib.moe_route(*args(4, 64, 17))) == "MOE_ERR_UNSUPPORTED"
+    assert status(lib, lib.moe_route(*args(2 ** 24, 512, 8))) == "MOE_ERR_UNSUPPORTED"
+    assert status(lib, lib.moe_route(*args(4, 8, 2, ids=None))) == "MOE_ERR_NULL"
+    assert status(lib, lib.moe_route(*args(4, 8, 2, off=None))) == "MOE_ERR_NULL"
+    assert status(lib, lib.moe_route(*args(4, 8, 2, logits=FAKE + 2))) == "MOE_ERR_ALIGN"
+
+
+def test_route_workspace_errors(lib, monkeypatch):
+    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", "multi")
+    T, E, k = 4096, 128, 8
+    need = lib.moe_route_workspace_bytes(T, E, k)
+    assert need == (4096 // 64) * 128 * 4
+    base = (FAKE, None, T, E, k, FAKE, FAKE, FAKE, None, FAKE, FAKE)
+    assert status(lib, lib.moe_route(*base, None, need, None)) == "MOE_ERR_WORKSPACE"
+    assert status(lib, lib.moe_route(*base, FAKE, need - 1, None)) == "MOE_ERR_WORKSPACE"
+    assert status(lib, lib.moe_route(*base, FAKE + 4, need, None)) == "MOE_ERR_WORKSPACE"
+    assert b"workspace" in lib.moe_last_error()
+
+
+def test_route_workspace_size_rules(lib):
+    assert lib.moe_route_workspace_bytes(0, 8, 2) > 0
+    assert lib.moe_route_workspace_bytes(1, 5, 2) == 8 * 4  # one row, experts padded to 8
+    assert lib.moe_route_workspace_bytes(65, 8, 2) == 2 * 8 * 4
+    assert lib.moe_route_workspace_bytes(4, 8, 9) == 0  # invalid
+
+
+@pytest.mark.parametrize("fn", ["expand", "combine"])
+def test_row_kernels_argument_errors(lib, fn):
+    def call(x=FAKE, d=FAKE, T=4, H=256, k=2, o=FAKE):
+        if fn == "expand":
+            return status(lib, lib.moe_expand_rows(x, d, T, H, k, o, None))
+        return status(lib, lib.moe_combine(x, FAKE, d, T, H, k, o, None))
+
+    assert call(T=-1) == "MOE_ERR_SHAPE"
+    assert call(H=0) == "MOE_ERR_SHAPE"
+    assert call(k=0) == "MOE_ERR_SHAPE"
+    assert call(k=17) == "MOE_ERR_SHAPE"
+    assert call(H=100) == "MOE_ERR_ALIGN"  # 200-byte rows are not a multiple of 16 bytes
+    assert call(x=FAKE + 8) == "MOE_ERR_ALIGN"
+    assert call(o=FAKE + 2) == "MOE_ERR_ALIGN"
+    assert call(x=None) == "MOE_ERR_NULL"
+    assert call(d=None) == "MOE_ERR_NULL"
+    assert call(T=2 ** 30, H=16) == "MOE_ERR_UNSUPPORTED"
+    # T = 0 is a no-op that needs no pointers and makes no HIP call
+    assert call(x=None, d=None, o=None, T=0) == "MOE_OK"
+
+
+def test_swiglu_argument_errors(lib):
+    assert status(lib, lib.moe_swiglu(FAKE, -1, 768, FAKE, None)) == "MOE_ERR_SHAPE"
+    assert status(lib, lib.moe_swiglu(FAKE, 4, 0, FAKE, None)) == "MOE_ERR_SHAPE"
+    assert status(lib, lib.moe_swiglu(FAKE, 4, 12, FAKE, None)) == "MOE_ERR_ALIGN"
+    assert status(lib, lib.moe_swiglu(FAKE + 4, 4, 768, FAKE, None)) == "MOE_ERR_ALIGN"
+    assert status(lib, lib.moe_swiglu(None, 4, 768, FAKE, None)) == "MOE_ERR_NULL"
+    assert status(lib, lib.moe_swiglu(FAKE, 2 ** 28, 64, FAKE, None)) == "MOE_ERR_UNSUPPORTED"
+    assert status(lib, lib.moe_swiglu(None, 0, 768, None, None)) == "MOE_OK"
+
+
+def test_copy_probe_argument_errors(lib):
+    assert status(lib, lib.moe_copy_probe(None, FAKE, 32, None)) == "MOE_ERR_NULL"
+    assert status(lib, lib.moe_copy_probe(FAKE, FAKE, 24, None)) == "MOE_ERR_ALIGN"
+    assert status(lib, lib.moe_copy_probe(None, None, 0, None)) == "MOE_OK"
+
+
+def test_status_strings(lib):
+    names = [lib.moe_status_string(i).decode() for i in range(7)]
+    assert names == ["MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_ALIGN", "MOE_ERR_UNSUPPORTED",
+                     "MOE_ERR_WORKSPACE", "MOE_ERR_HIP"]
+
+
+def test_python_binding_maps_errors_to_value_error(lib):
+    from moe_glue_amd import _binding
+
+    rc = lib.moe_swiglu(FAKE, 4, 12, FAKE, None)
+    with pytest.raises(ValueError, match="MOE_ERR_ALIGN"):
+        _binding.check(rc, "moe_swiglu")
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    import moe_glue_amd as mg
+
+    with pytest.raises(ValueError, match="GPU tensor"):
+        mg.swiglu(torch.zeros((4, 16), dtype=torch.bfloat16))
+
+
+def test_fastdiv_host(tmp_path):
+    """The multiply-shift division of the streaming kernels, on the host."""
+    exe = tmp_path / "fastdiv_check"
+    src = os.path.join(ROOT, "tests", "host", "fastdiv_check.cpp")
+    inc = os.path.join(ROOT, "moe_glue_amd", "csrc")
+    subprocess.run(["hipcc", "-O2", "-std=c++17", "-x", "hip", "--offload-arch=gfx950", "-I", inc, src, "-o",
+                    str(exe)], check=True, capture_output=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout + out.stderr

@@ -1,0 +1,227 @@
+"""HIP path vs the CPU oracle on the same seeded inputs (runs on an MI355X).
+
+Integer outputs and copies are compared bit for bit; bf16 activations and
+combined outputs within |err| <= 1e-2*|ref| + 1e-3; routing weights within
+1e-5*|ref| + 1e-6.  Covered: the five workloads at full size (the launch
+configuration the benchmark times), three seeds of the small ones, the token
+sweep {1, 7, 32, 257, 1023} at the Qwen3-30B-A3B shape, both route variants,
+and the edge cases of the method (T = 0, k = 1, k = E, E not a multiple of 4,
+E = 512 with k = 16, exact ties, signed zeros, constant rows, rows that are not
+a whole number of waves, every finite bf16 gate value)."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import compare
+import gpu_util as G
+from moe_glue_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return G.device()
+
+
+def check_path(got, ref, cfg, what):
+    compare.assert_route_equal(got, ref, what)
+    if "x_expanded" in got:
+        compare.assert_equal(got["x_expanded"], ref["x_expanded"], f"{what}.x_expanded")
+    if "act" in got:
+        compare.assert_bf16_close(got["act"], ref["act"], f"{what}.act")
+    if "out" in got:
+        compare.assert_bf16_close(got["out"], ref["out"], f"{what}.out")
+
+
+# ------------------------------------------------------------------ workloads
+@pytest.mark.parametrize("name", inputs.CONFIG_ORDER)
+def test_workload_full_size(dev, oracle_lib, name):
+    cfg = inputs.CONFIGS[name]
+    _log(f"[parity] {inputs.describe(cfg)} seed=0")
+    inp = inputs.make_inputs(cfg, 0)
+    got = G.run_path(inp, dev)
+    ref = oracle_lib.path(inp)
+    check_path(got, ref, cfg, name)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+@pytest.mark.parametrize("name", ["tiny", "decode", "skewed"])
+def test_workload_more_seeds(dev, oracle_lib, name, seed):
+    cfg = inputs.CONFIGS[name]
+    _log(f"[parity] {inputs.describe(cfg)} seed={seed}")
+    inp = inputs.make_inputs(cfg, seed)
+    check_path(G.run_path(inp, dev), oracle_lib.path(inp), cfg, f"{name}/seed{seed}")
+
+
+@pytest.mark.parametrize("T", [1, 7, 32, 257, 1023])
+def test_token_sweep_qwen_shape(dev, oracle_lib, T):
+    cfg = inputs.CONFIGS["qwen3_30b_a3b"].with_tokens(T)
+    _log(f"[parity] {inputs.describe(cfg)}")
+    inp = inputs.make_inputs(cfg, 0)
+    check_path(G.run_path(inp, dev), oracle_lib.path(inp), cfg, cfg.name)
+
+
+# ------------------------------------------------------------------ route
+def _route_gpu(dev, logits, k, bias=None):
+    import moe_glue_amd as mg
+
+    r = mg.route(G.to_dev(logits, dev), k, None if bias is None else G.to_dev(bias, dev))
+    return G.route_host(r)
+
+
+ROUTE_SHAPES = [  # (T, E, k): every lanes-per-token width, odd E, limits
+    (5, 1, 1), (9, 3, 2), (33, 4, 4), (70, 8, 8), (100, 17, 5), (64, 16, 3), (65, 33, 7), (130, 64, 6),
+    (200, 100, 9), (300, 128, 8), (129, 200, 2), (257, 256, 8), (1000, 300, 16), (96, 512, 16), (50, 512, 1),
+]
+
+
+@pytest.mark.parametrize("variant", ["auto", "single", "multi"])
+@pytest.mark.parametrize("T,E,k", ROUTE_SHAPES)
+def test_route_shapes_and_variants(dev, oracle_lib, monkeypatch, variant, T, E, k):
+    if variant == "single" and T > 256:
+        pytest.skip("single-workgroup route covers T <= 256")
+    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
+    _log(f"[route] T={T} E={E} k={k} variant={variant}")
+    rng = np.random.default_rng([T, E, k])
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (0.5 * rng.standard_normal(E)).astype(np.float32) if E % 2 == 0 else None
+    compare.assert_route_equal(_route_gpu(dev, logits, k, bias), oracle_lib.route(logits, k, bias),
+                               f"route T={T} E={E} k={k}")
+
+
+@pytest.mark.parametrize("variant", ["single", "multi"])
+@pytest.mark.parametrize("kind", ["quantized", "signed_zero", "constant", "wide"])
+def test_route_ties_and_special_rows(dev, oracle_lib, monkeypatch, variant, kind):
+    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
+    T, E, k = 200, 64, 6
+    _log(f"[route] {kind} rows T={T} E={E} k={k} variant={variant}")
+    logits = {"quantized": lambda: inputs.quantized_logits(T, E, 3),
+              "signed_zero": lambda: inputs.signed_zero_logits(T, E, 3),
+              "constant": lambda: inputs.constant_logits(T, E),
+              "wide": lambda: inputs.wide_logits(T, E, 3)}[kind]()
+    compare.assert_route_equal(_route_gpu(dev, logits, k), oracle_lib.route(logits, k), f"route {kind}")
+
+
+def test_route_empty_batch(dev, oracle_lib):
+    import torch
+    import moe_glue_amd as mg
+
+    _log("[route] T=0")
+    out = mg.alloc_route_outputs(0, 16, 4, dev)
+    out["expert_offsets"].fill_(-7)
+    out["expert_counts"].fill_(-7)
+    mg.route(torch.empty((0, 16), dtype=torch.float32, device=dev), 4, out=out)
+    torch.cuda.synchronize()
+    assert G.to_host(out["expert_offsets"]).tolist() == [0] * 17
+    assert G.to_host(out["expert_counts"]).tolist() == [0] * 16
+
+
+def test_route_variants_bit_identical_and_deterministic(dev, monkeypatch):
+    T, E, k = 256, 128, 8
+    _log("[route] determinism and variants")
+    logits = inputs.quantized_logits(T, E, 9)
+    results = []
+    for variant in ("single", "multi", "multi", "single"):
+        monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
+        results.append(_route_gpu(dev, logits, k))
+    for r in results[1:]:
+        for key in results[0]:
+            compare.assert_equal(r[key], results[0][key], f"variant/determinism {key}")
+
+
+def test_skewed_tie_rows(dev, oracle_lib):
+    cfg = inputs.CONFIGS["skewed"]
+    _log("[route] skewed workload, injected tie rows")
+    logits, bias = inputs.make_logits(cfg, 0)
+    got, ref = _route_gpu(dev, logits, cfg.k, bias), oracle_lib.route(logits, cfg.k, bias)
+    rows = inputs.tie_rows(cfg, 0)
+    compare.assert_equal(got["topk_ids"][rows], ref["topk_ids"][rows], "tie rows")
+    compare.assert_route_equal(got, ref, "skewed")
+
+
+# ------------------------------------------------------------------ expand / combine
+@pytest.mark.parametrize("T,H,E,k", [(1, 8, 4, 1), (3, 8, 4, 4), (77, 520, 17, 5), (300, 2048, 128, 8),
+                                     (65, 4096, 64, 16), (513, 264, 8, 2)])
+def test_expand_combine_shapes(dev, oracle_lib, T, H, E, k):
+    cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
+    _log(f"[rows] T={T} H={H} E={E} k={k}")
+    inp = inputs.make_inputs(cfg, 4)
+    got = G.run_path(inp, dev, parts=("route", "expand", "combine"))
+    ref = oracle_lib.route(inp["logits"], k)
+    compare.assert_equal(got["x_expanded"], oracle_lib.expand_rows(inp["x"], ref["dest_of_src"], k), "x_expanded")
+    compare.assert_bf16_close(got["out"], oracle_lib.combine(inp["y"], ref["topk_weights"], ref["dest_of_src"]),
+                              "out")
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_30b_a3b", "skewed"])
+def test_combine_of_expand_is_identity(dev, name):
+    """Identity experts: combine(expand(x), w) == x exactly on the GPU (as
+    values: -0 and +0 are the same sum)."""
+    import torch
+    import moe_glue_amd as mg
+
+    cfg = inputs.CONFIGS[name]
+    _log(f"[identity] {name}")
+    inp = inputs.make_inputs(cfg, 5, parts=("x", "logits"))
+    x = G.to_dev(inp["x"], dev)
+    r = mg.route(G.to_dev(inp["logits"], dev), cfg.k,
+                 None if inp["bias"] is None else G.to_dev(inp["bias"], dev))
+    assert np.array_equal(np.sort(G.to_host(r["dest_of_src"])), np.arange(cfg.R)), "dest_of_src not a permutation"
+    out = mg.combine(mg.expand_rows(x, r["dest_of_src"], cfg.k), r["topk_weights"], r["dest_of_src"])
+    torch.cuda.synchronize()
+    # exact as values: the fp32 sum starts from +0, so a -0 in x comes back as +0
+    compare.assert_equal(compare.bf16_to_f64(G.to_host(out)), compare.bf16_to_f64(inp["x"]), "combine(expand(x))")
+
+
+def test_combine_unnormalised_weights(dev, oracle_lib):
+    import torch
+    import moe_glue_amd as mg
+
+    T, H, E, k = 129, 1024, 32, 4
+    _log("[combine] unnormalised weights")
+    rng = np.random.default_rng(11)
+    ref = oracle_lib.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    y = inputs.normal_bf16(3, 99, (T * k, H))
+    w = inputs.make_weights(T, k, 3)
+    got = mg.combine(G.to_dev(y, dev), G.to_dev(w, dev), G.to_dev(ref["dest_of_src"], dev))
+    torch.cuda.synchronize()
+    compare.assert_bf16_close(G.to_host(got), oracle_lib.combine(y, w, ref["dest_of_src"]), "combine")
+
+
+# ------------------------------------------------------------------ SwiGLU
+def test_swiglu_every_finite_bf16_gate(dev, oracle_lib):
+    import torch
+    import moe_glue_amd as mg
+
+    _log("[swiglu] every finite bf16 gate x u in {1, -1, 0.5, 3}")
+    gate = np.array([b for b in range(0x10000) if (b & 0x7F80) != 0x7F80], dtype=np.uint16)
+    n = gate.size - gate.size % 8
+    gate = gate[:n]
+    for u_bits in (0x3F80, 0xBF80, 0x3F00, 0x4040):
+        I8 = 64
+        rows = n // (8 * I8)
+        g = gate[: rows * 8 * I8].reshape(rows, 8 * I8)
+        h = np.concatenate([g, np.full_like(g, u_bits)], axis=1)
+        got = G.to_host(mg.swiglu(G.to_dev(h, dev)))
+        torch.cuda.synchronize()
+        compare.assert_bf16_close(got, oracle_lib.swiglu(h), f"swiglu u={u_bits:#06x}")
+
+
+@pytest.mark.parametrize("R,I", [(1, 8), (3, 16), (257, 768), (1023, 1408), (64, 2048), (7, 2056)])
+def test_swiglu_shapes(dev, oracle_lib, R, I):
+    import torch
+    import moe_glue_amd as mg
+
+    _log(f"[swiglu] R={R} I={I}")
+    hb = inputs.normal_bf16(R, 21, (R, 2 * I))
+    got = G.to_host(mg.swiglu(G.to_dev(hb, dev)))
+    torch.cuda.synchronize()
+    compare.assert_bf16_close(got, oracle_lib.swiglu(hb), f"swiglu R={R} I={I}")
