@@ -53,16 +53,66 @@ def source_digest(kernel: str) -> str:
 
 
 def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when there is none or the kernel source changed since it was taken."""
-    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/traffic_<workload>.md), or None when there is none or the
+    kernel's source changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.md")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f)
-    if rec.get("source_digest") != source_digest(kernel):
+        text = f.read()
+    start = text.find("```json")
+    if start < 0:
+        return None
+    end = text.find("```", start + 7)
+    rec = json.loads(text[start + 7:end]).get("kernels", {}).get(kernel)
+    if not rec or rec.get("source_digest") != source_digest(kernel):
         return None
     return rec.get("traffic_bytes")
+
+
+class HipEvent:
+    """A HIP timing event recorded on the launch stream without the system-scope
+    release fence a default event carries (hipEventDisableSystemFence), so the
+    markers between kernels stay cheap."""
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def hip(cls):
+        if cls._hip is None:
+            import ctypes
+
+            lib = ctypes.CDLL("libamdhip64.so")
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = lib
+        return cls._hip
+
+    def __init__(self, stream: int, flags: int = DISABLE_SYSTEM_FENCE):
+        import ctypes
+
+        self.h = ctypes.c_void_p()
+        self.stream = ctypes.c_void_p(stream)
+        rc = self.hip().hipEventCreateWithFlags(ctypes.byref(self.h), flags)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self._record = self.hip().hipEventRecord
+
+    def record(self):
+        self._record(self.h, self.stream)
+
+    def elapsed_time(self, end: "HipEvent") -> float:
+        import ctypes
+
+        ms = ctypes.c_float()
+        rc = self.hip().hipEventElapsedTime(ctypes.byref(ms), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
 
 
 class Sets:
@@ -177,7 +227,8 @@ def main(argv=None):
     ap.add_argument("--sets", type=int, default=4, help="input/output sets rotated across steps")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-events", action="store_true", help="time steps without per-call HIP events")
+    ap.add_argument("--events", choices=["nofence", "torch", "none"], default="nofence",
+                    help="per-call HIP events inside the timed region (default: without the system fence)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -202,15 +253,33 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     names = ["route", "expand", "swiglu", "combine"]
-    use_events = not args.no_events
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)] if use_events else None
+    # Timed region 1: the path alone, K steps back to back -> value, ms_per_step.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        sets.step(s, ev[s] if use_events else None)
+        sets.step(s)
     host_s = time.perf_counter() - t0
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+
+    # Timed region 2: the same K steps with a HIP event between calls on the
+    # launch stream -> per-call device times (the markers cost a little, so
+    # they stay out of region 1).
+    use_events = args.events != "none"
+    ev = None
+    events_elapsed = None
+    if use_events:
+        if args.events == "torch":
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        else:
+            stream = torch.cuda.current_stream(dev).cuda_stream
+            ev = [[HipEvent(stream) for _ in range(5)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for s in range(args.steps):
+            sets.step(s, ev[s])
+        torch.cuda.synchronize()
+        events_elapsed = time.perf_counter() - t1
 
     ab = algorithmic_bytes(cfg)
     kernels = {}
@@ -221,7 +290,8 @@ def main(argv=None):
             gbps = ab[n] / (us * 1e-6) / 1e9
             kernels[n] = {"us": round(us, 3), "bytes": ab[n], "GBps": round(gbps, 1),
                           "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
-                          "frac_of_achievable": round(gbps / achievable, 4)}
+                          "frac_of_achievable": round(gbps / achievable, 4),
+                          "traffic": measured_traffic(n, cfg.name)}
     dominant = max(("expand", "swiglu", "combine"), key=lambda n: kernels[n]["us"]) if kernels else "combine"
     roofline = None
     if kernels:
@@ -248,6 +318,8 @@ def main(argv=None):
         "path_GBps": round(sum(ab.values()) / (elapsed / args.steps) / 1e9, 1),
         "achievable_copy_GBps": round(achievable, 1),
         "host_us_per_step": round(1e6 * host_s / args.steps, 2),
+        "events": args.events,
+        "ms_per_step_with_events": None if events_elapsed is None else round(1e3 * events_elapsed / args.steps, 4),
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": None,

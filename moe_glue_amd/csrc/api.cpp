@@ -38,12 +38,13 @@ moe_status from_hip(hipError_t e, const char* what) {
 }
 
 // Route variant override for tests and measurements:
-// MOE_GLUE_ROUTE_VARIANT = auto | single | multi.
+// MOE_GLUE_ROUTE_VARIANT = auto | single | two | three (anything else: auto).
 moe::RouteVariant requested_route_variant() {
     const char* v = std::getenv("MOE_GLUE_ROUTE_VARIANT");
-    if (v == nullptr || std::strcmp(v, "auto") == 0) return moe::RouteVariant::Auto;
+    if (v == nullptr) return moe::RouteVariant::Auto;
     if (std::strcmp(v, "single") == 0) return moe::RouteVariant::SingleWorkgroup;
-    if (std::strcmp(v, "multi") == 0) return moe::RouteVariant::MultiWorkgroup;
+    if (std::strcmp(v, "two") == 0) return moe::RouteVariant::TwoPass;
+    if (std::strcmp(v, "three") == 0) return moe::RouteVariant::ThreePass;
     return moe::RouteVariant::Auto;
 }
 
@@ -107,8 +108,8 @@ moe_status moe_route(const float* logits, const float* bias, int32_t T, int32_t 
         if (!aligned4(logits) || (bias && !aligned4(bias)))
             return fail(MOE_ERR_ALIGN, "moe_route: logits/bias must be 4-byte aligned");
     }
-    const moe::RouteVariant v = moe::route_pick_variant(T, requested_route_variant());
-    if (v == moe::RouteVariant::MultiWorkgroup) {
+    const moe::RouteVariant v = moe::route_pick_variant(T, E, requested_route_variant());
+    if (v != moe::RouteVariant::SingleWorkgroup) {
         const size_t need = moe::route_workspace_bytes(T, E);
         if (workspace == nullptr || workspace_bytes < need)
             return fail(MOE_ERR_WORKSPACE, "moe_route: workspace of %zu bytes needed, %zu given%s", need,

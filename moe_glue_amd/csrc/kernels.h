@@ -11,13 +11,16 @@
 namespace moe {
 
 // ---------------------------------------------------------------- route
-// Tokens per workgroup in the multi-workgroup route, and tokens per rank
-// bitmap (one bit per token of a 64-bit word).
-constexpr int kRouteTokensPerBlock = 64;
-// Largest T the single-workgroup route accepts (four 64-token bitmaps).
+// Largest T the single-workgroup route accepts (four 64-token rank bitmaps),
+// and the largest T it is chosen for automatically.
 constexpr int kRouteFusedMaxTokens = 256;
+constexpr int kRouteSingleAutoMaxTokens = 64;
+// Largest histogram matrix (bytes) for which scan and place share one launch.
+constexpr size_t kRouteTwoPassMaxBytes = 128 * 1024;
 
-enum class RouteVariant { Auto = 0, SingleWorkgroup = 1, MultiWorkgroup = 2 };
+// Single workgroup; multi workgroup with the scan and place in one launch
+// (TwoPass) or in two (ThreePass); Auto picks by T and the matrix size.
+enum class RouteVariant { Auto = 0, SingleWorkgroup = 1, TwoPass = 2, ThreePass = 3 };
 
 struct RouteArgs {
     const float* logits;
@@ -32,17 +35,21 @@ struct RouteArgs {
     void* workspace;
 };
 
+// Keys per lane (8 above 32 experts, else 4) and lanes that cooperate on one token.
+int route_keys_per_lane(int E);
+int route_lanes_per_token(int E);
+// Tokens per workgroup of the multi-workgroup top-k (one workspace row each).
+int route_tokens_per_block(int E);
 // Experts padded to a multiple of 4 (one int4 per 4 experts in the workspace).
 inline int route_padded_experts(int E) { return (E + 3) & ~3; }
-inline int route_num_blocks(int T) { return (T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock; }
+// Workspace of the multi-workgroup route: one histogram row per top-k
+// workgroup plus one row of totals.
 inline size_t route_workspace_bytes(int T, int E) {
-    int nb = route_num_blocks(T);
-    if (nb < 1) nb = 1;
-    return (size_t)nb * (size_t)route_padded_experts(E) * sizeof(int32_t);
+    const int tb = route_tokens_per_block(E);
+    const size_t nb = (size_t)(T > 0 ? (T + tb - 1) / tb : 0);
+    return (nb + 1) * (size_t)route_padded_experts(E) * sizeof(int32_t);
 }
-// Lanes that cooperate on one token: 4 keys per lane up to 256 experts, 8 beyond.
-int route_lanes_per_token(int E);
-RouteVariant route_pick_variant(int T, RouteVariant requested);
+RouteVariant route_pick_variant(int T, int E, RouteVariant requested);
 
 hipError_t launch_route(const RouteArgs& a, RouteVariant variant, hipStream_t stream);
 

@@ -8,7 +8,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kU = 4;
+constexpr int kU = 1;
 
 __global__ __launch_bounds__(kThreads) void copy_probe_kernel(const u32x4* __restrict__ src,
                                                               u32x4* __restrict__ dst, size_t n) {

@@ -7,30 +7,39 @@
 // indices are first assigned per block and then combined across blocks through
 // global memory.  Both exist here:
 //
-//   single workgroup (T <= 256): top-k, histogram, scan and maps in one launch;
-//   multi workgroup: kernel 1 (one workgroup per 64 tokens) does top-k, the
-//     block-local histogram and each slot's rank inside the block; kernel 2
-//     sums the per-block histograms (column prefix over blocks + totals),
-//     scans the totals into offsets in LDS and writes the final maps.
+//   single workgroup (small T): top-k, histogram, scan and maps in one launch;
+//   multi workgroup:
+//     1. top-k     one workgroup per 16 tokens (64 below 4 lanes per token),
+//                  so even a few thousand tokens spread over every CU: writes
+//                  the top-k, each slot's rank inside the workgroup and the
+//                  workgroup's expert histogram (one workspace row);
+//     2. scan      one workgroup per 4 experts: exclusive prefix of the
+//                  histogram rows down each expert column, plus the totals;
+//     3. place     per workgroup of step 1: scan the totals into offsets (in
+//                  LDS) and write dest = offset + prefix + rank and its inverse.
+//   Each launch costs a few microseconds on its own, so while the histogram
+//   matrix is small (up to 128 KiB) steps 2 and 3 run as one launch in which
+//   every workgroup reads the whole matrix.
 //
 // The page's blocks claim slots with shared-memory atomic increments, which
 // gives each expert's list in arbitrary order.  Here the order is fixed
-// (ascending token inside each expert): each 64-token chunk builds, per
-// expert, a 64-bit bitmap of the tokens that picked it (LDS atomic OR, which
-// commutes), and a slot's rank is the popcount of the bits below its token.
+// (ascending token inside each expert): the workgroup builds, per expert, a
+// 64-bit bitmap of its tokens that picked it (LDS atomic OR, which commutes),
+// and a slot's rank is the popcount of the bits below its token.
 //
-// Top-k: G lanes cooperate on one token (4 keys per lane, 8 above 256
-// experts).  Each of the k rounds takes the per-lane maximum of a 64-bit key
-// (orderable fp32 key in the high word, ~expert in the low word, so equal
-// keys prefer the lower expert) and a butterfly over the G lanes with
-// ds_swizzle (xor < 32) and ds_bpermute (xor 32).
+// Top-k: G lanes cooperate on one token (8 keys per lane above 32 experts,
+// else 4).  Each of the k rounds finds the group's largest key (fp32 mapped
+// to an order-preserving uint32, -0 folded onto +0) and then the lowest
+// expert holding it, with two DPP/permlane reductions over the G lanes; the
+// lane that owns the winner retires it.  Each lane then computes only the
+// exponentials of the slots it writes, and one more reduction sums them.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int kChunk = 64;     // tokens per rank bitmap
+constexpr int kChunk = 64;  // tokens per rank bitmap
 constexpr int kKMax = 16;
 constexpr int kEMax = 512;
 constexpr int kMaxChunks = kRouteFusedMaxTokens / kChunk;
@@ -49,119 +58,122 @@ __device__ __forceinline__ float unorderable(uint32_t o) {
     return __builtin_bit_cast(float, u);
 }
 
-template <int MASK>
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
-    if constexpr (MASK < 32) {
-        // ds_swizzle bit mode: and_mask = 0x1f, or_mask = 0, xor_mask = MASK
-        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1f | (MASK << 10));
-    } else {
-        return (uint32_t)__shfl_xor((int)v, MASK);
+// Reductions over each aligned group of G lanes (G a power of two <= 64),
+// result in every lane of the group, without the LDS crossbar: DPP quad
+// permutations for lane distance 1 and 2, DPP half-row / row mirrors to join
+// quads into 8 and 16 lanes, and the gfx950 permlane16/permlane32 swaps to
+// join rows into 32 and 64 lanes.  All are VALU operations.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+enum class Op { Max, Min, FAdd };
+
+template <Op OP>
+__device__ __forceinline__ uint32_t apply(uint32_t a, uint32_t b) {
+    if constexpr (OP == Op::Max) return a > b ? a : b;
+    if constexpr (OP == Op::Min) return a < b ? a : b;
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+}
+
+template <int G, Op OP>
+__device__ __forceinline__ uint32_t group_reduce(uint32_t v) {
+    if constexpr (G > 1) v = apply<OP>(v, dpp<kQuadXor1>(v));
+    if constexpr (G > 2) v = apply<OP>(v, dpp<kQuadXor2>(v));
+    if constexpr (G > 4) v = apply<OP>(v, dpp<kRowHalfMirror>(v));
+    if constexpr (G > 8) v = apply<OP>(v, dpp<kRowMirror>(v));
+    if constexpr (G > 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = apply<OP>(p[0], p[1]);
     }
-}
-
-template <int MASK>
-__device__ __forceinline__ uint64_t max_with_lane(uint64_t v) {
-    uint32_t lo = lane_xor<MASK>((uint32_t)v);
-    uint32_t hi = lane_xor<MASK>((uint32_t)(v >> 32));
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    return o > v ? o : v;
-}
-
-// Maximum over each aligned group of G lanes (all lanes of the wave active).
-template <int G>
-__device__ __forceinline__ uint64_t group_max(uint64_t v) {
-    if constexpr (G > 1) v = max_with_lane<1>(v);
-    if constexpr (G > 2) v = max_with_lane<2>(v);
-    if constexpr (G > 4) v = max_with_lane<4>(v);
-    if constexpr (G > 8) v = max_with_lane<8>(v);
-    if constexpr (G > 16) v = max_with_lane<16>(v);
-    if constexpr (G > 32) v = max_with_lane<32>(v);
+    if constexpr (G > 32) {
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        v = apply<OP>(p[0], p[1]);
+    }
     return v;
 }
 
-// Launch shape per lanes-per-token G and keys-per-lane V: P passes of
-// THREADS/G tokens cover one 64-token chunk.  THREADS is at most 512, or
-// 1024 when that keeps the P*V logits each lane preloads within 32 registers.
+// Top-k of token t by the G lanes of one group (lane gl of the group).
+// Every lane of the wave must call this (the reductions cross lanes); lanes
+// with t >= T compute on empty keys and write nothing.  Writes topk_ids and
+// topk_weights, and the ids to ids_lds[tl * k + r].
 template <int G, int V>
-struct Shape {
-    static constexpr int P0 = (kChunk * G / 512) > 1 ? (kChunk * G / 512) : 1;
-    static constexpr int P = (P0 * V > 32) ? (32 / V) : P0;
-    static constexpr int THREADS = kChunk * G / P;
-    static constexpr int TOK_PER_PASS = THREADS / G;
-    static_assert(P * TOK_PER_PASS == kChunk, "one chunk per P passes");
-};
-
-// Top-k of the 64 tokens [tok0, tok0 + 64) of which those below T exist.
-// Writes topk_ids / topk_weights to global memory and the ids to ids_lds
-// ([64][k], token-major).  Every lane of the workgroup must call this.
-template <int G, int V>
-__device__ __forceinline__ void topk_chunk(const float* __restrict__ logits, const float* __restrict__ bias, int T,
-                                           int E, int k, int tok0, int32_t* __restrict__ topk_ids,
+__device__ __forceinline__ void topk_token(const float* __restrict__ logits, const float* __restrict__ bias, int T,
+                                           int E, int k, int t, int tl, int gl, int32_t* __restrict__ topk_ids,
                                            float* __restrict__ topk_weights, int32_t* ids_lds) {
-    using S = Shape<G, V>;
-    const int grp = threadIdx.x / G;
-    const int gl = threadIdx.x % G;
-
-    // all loads of the chunk first, so their latencies overlap
-    float vals[S::P][V];
-#pragma unroll
-    for (int p = 0; p < S::P; ++p) {
-        const int t = tok0 + p * S::TOK_PER_PASS + grp;
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-            const int e = gl + G * i;
-            vals[p][i] = (t < T && e < E) ? logits[(size_t)t * E + e] : 0.0f;
-        }
-    }
-    float bv[V];
+    constexpr int NJ = (kKMax + G - 1) / G;  // slots a lane may own: r = gl + G*j
+    const bool live = t < T;
+    float vals[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         const int e = gl + G * i;
-        bv[i] = (bias != nullptr && e < E) ? bias[e] : 0.0f;
+        vals[i] = (live && e < E) ? logits[(size_t)t * E + e] : 0.0f;
     }
-
+    // key[i] of expert gl + G*i: orderable fp32 key, 0 = absent or taken
+    // (every real key is above 0: orderable(-inf) = 0x007FFFFF)
+    uint32_t key[V];
 #pragma unroll
-    for (int p = 0; p < S::P; ++p) {
-        const int tl = p * S::TOK_PER_PASS + grp;
-        const int t = tok0 + tl;
-        const bool live = t < T;
-        uint64_t key[V];
+    for (int i = 0; i < V; ++i) {
+        const int e = gl + G * i;
+        float kf = vals[i];
+        if (bias != nullptr && e < E) kf = kf + bias[e];
+        key[i] = (live && e < E) ? orderable(kf) : 0u;
+    }
+    uint32_t my_id[NJ];
+    uint32_t my_key[NJ];
+    uint32_t top0 = 0;
 #pragma unroll
-        for (int i = 0; i < V; ++i) {
-            const int e = gl + G * i;
-            float kf = vals[p][i];
-            if (bias != nullptr) kf = kf + bv[i];
-            key[i] = (live && e < E) ? (((uint64_t)orderable(kf) << 32) | (uint32_t)~(uint32_t)e) : 0ull;
-        }
-        uint32_t wid[kKMax];
-        float wkey[kKMax];
+    for (int r = 0; r < kKMax; ++r) {
+        if (r < k) {  // k is uniform: no divergence around the lane exchange
+            // the lane's best: largest key, lowest expert on equal keys
+            uint32_t best = key[0];
+            int bi = 0;
 #pragma unroll
-        for (int r = 0; r < kKMax; ++r) {
-            if (r < k) {  // k is uniform: no divergence around the lane exchange
-                uint64_t best = key[0];
+            for (int i = 1; i < V; ++i)
+                if (key[i] > best) {
+                    best = key[i];
+                    bi = i;
+                }
+            // the group's best key, then the lowest expert holding it
+            const uint32_t top = group_reduce<G, Op::Max>(best);
+            const uint32_t mine = (best == top) ? (uint32_t)(gl + G * bi) : 0xFFFFFFFFu;
+            const uint32_t win = group_reduce<G, Op::Min>(mine);
 #pragma unroll
-                for (int i = 1; i < V; ++i) best = key[i] > best ? key[i] : best;
-                const uint64_t win = group_max<G>(best);
-#pragma unroll
-                for (int i = 0; i < V; ++i)
-                    if (key[i] == win) key[i] = 0ull;
-                wid[r] = ~(uint32_t)win;
-                wkey[r] = unorderable((uint32_t)(win >> 32));
+            for (int i = 0; i < V; ++i)  // the owner retires the winner
+                if ((uint32_t)(gl + G * i) == win) key[i] = 0u;
+            if (r == 0) top0 = top;
+            if ((r % G) == gl) {
+                my_id[r / G] = win;
+                my_key[r / G] = top;
             }
         }
-        if (live) {
-            float denom = 0.0f;
+    }
+    // weights: softmax over the k selected keys, relative to the largest
+    const float key0 = unorderable(top0);
+    float ex[NJ];
+    float part = 0.0f;
 #pragma unroll
-            for (int r = 0; r < kKMax; ++r)
-                if (r < k) denom += expf(wkey[r] - wkey[0]);
+    for (int j = 0; j < NJ; ++j) {
+        const int r = gl + G * j;
+        ex[j] = (r < k) ? expf(unorderable(my_key[j]) - key0) : 0.0f;
+        part += ex[j];
+    }
+    const float denom = __builtin_bit_cast(float, group_reduce<G, Op::FAdd>(__builtin_bit_cast(uint32_t, part)));
+    if (live) {
 #pragma unroll
-            for (int r = 0; r < kKMax; ++r) {
-                if (r < k && (r % G) == gl) {
-                    const size_t s = (size_t)t * k + r;
-                    topk_ids[s] = (int32_t)wid[r];
-                    topk_weights[s] = expf(wkey[r] - wkey[0]) / denom;
-                    ids_lds[tl * k + r] = (int32_t)wid[r];
-                }
+        for (int j = 0; j < NJ; ++j) {
+            const int r = gl + G * j;
+            if (r < k) {
+                const size_t s = (size_t)t * k + r;
+                topk_ids[s] = (int32_t)my_id[j];
+                topk_weights[s] = ex[j] / denom;
+                ids_lds[tl * k + r] = (int32_t)my_id[j];
             }
         }
     }
@@ -223,32 +235,49 @@ __device__ __forceinline__ void wave0_exclusive_scan(const int32_t* in, int32_t*
     if (lane == kWave - 1) out[n] = incl;
 }
 
+// Launch shapes.
+// Multi-workgroup top-k: one token per group of G lanes, one pass, TOK tokens
+// per workgroup: 16 (THREADS = 16*G = 64..1024) for G >= 4, one wave below.
+template <int G>
+struct TopkShape {
+    static constexpr int TOK = (G >= 4) ? 16 : kWave / G;
+    static constexpr int THREADS = TOK * G;
+};
+// Single workgroup: up to 1024 lanes, at most 64 tokens per pass.
+template <int G>
+struct SingleShape {
+    static constexpr int THREADS = (kChunk * G < 1024) ? kChunk * G : 1024;
+    static constexpr int TOK_PER_PASS = THREADS / G;
+};
+
 // ------------------------------------------------------------ single workgroup
 template <int G, int V>
-__global__ __launch_bounds__((Shape<G, V>::THREADS)) void route_single_kernel(
+__global__ __launch_bounds__((SingleShape<G>::THREADS)) void route_single_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ expert_counts, int32_t* __restrict__ dest_of_src, int32_t* __restrict__ src_of_dest) {
-    constexpr int THREADS = Shape<G, V>::THREADS;
+    using S = SingleShape<G>;
     __shared__ int32_t ids_lds[kRouteFusedMaxTokens * kKMax];
     __shared__ unsigned long long masks[kMaxChunks * kEMax];
     __shared__ int32_t s_cnt[kEMax];
     __shared__ int32_t s_off[kEMax + 1];
 
     const int Epad = (E + 3) & ~3;
-    const int nchunks = (T + kChunk - 1) / kChunk;
-    for (int c = 0; c < nchunks; ++c)
-        topk_chunk<G, V>(logits, bias, T, E, k, c * kChunk, topk_ids, topk_weights, ids_lds + c * kChunk * k);
+    const int grp = threadIdx.x / G;
+    const int gl = threadIdx.x % G;
+    for (int t0 = 0; t0 < T; t0 += S::TOK_PER_PASS)
+        topk_token<G, V>(logits, bias, T, E, k, t0 + grp, t0 + grp, gl, topk_ids, topk_weights, ids_lds);
     __syncthreads();
-    build_masks<THREADS>(ids_lds, T, k, Epad, nchunks, masks);
-    for (int e = threadIdx.x; e < E; e += THREADS) s_cnt[e] = mask_count(masks, Epad, nchunks, e);
+    const int nchunks = (T + kChunk - 1) / kChunk;
+    build_masks<S::THREADS>(ids_lds, T, k, Epad, nchunks, masks);
+    for (int e = threadIdx.x; e < E; e += S::THREADS) s_cnt[e] = mask_count(masks, Epad, nchunks, e);
     __syncthreads();
     wave0_exclusive_scan(s_cnt, s_off, E);
     __syncthreads();
-    for (int e = threadIdx.x; e <= E; e += THREADS) expert_offsets[e] = s_off[e];
+    for (int e = threadIdx.x; e <= E; e += S::THREADS) expert_offsets[e] = s_off[e];
     if (expert_counts != nullptr)
-        for (int e = threadIdx.x; e < E; e += THREADS) expert_counts[e] = s_cnt[e];
-    for (int s = threadIdx.x; s < T * k; s += THREADS) {
+        for (int e = threadIdx.x; e < E; e += S::THREADS) expert_counts[e] = s_cnt[e];
+    for (int s = threadIdx.x; s < T * k; s += S::THREADS) {
         const int e = ids_lds[s];
         const int d = s_off[e] + slot_rank(masks, Epad, s / k, e);
         dest_of_src[s] = d;
@@ -257,76 +286,121 @@ __global__ __launch_bounds__((Shape<G, V>::THREADS)) void route_single_kernel(
 }
 
 // ------------------------------------------------------------- multi workgroup
-// Kernel 1: workgroup b owns tokens [64b, 64b + 64).  Writes top-k, each
-// slot's rank inside the workgroup (into dest_of_src, finished by kernel 2)
-// and the workgroup's histogram (workspace row b, Epad ints, zero padded).
+// 1. Workgroup b owns tokens [b*TOK, b*TOK + TOK).  Writes the top-k, each
+// slot's rank inside the workgroup (into dest_of_src, finished by step 3) and
+// the workgroup's histogram (workspace row b, Epad ints, zero padded).
 template <int G, int V>
-__global__ __launch_bounds__((Shape<G, V>::THREADS)) void route_multi_topk_kernel(
+__global__ __launch_bounds__((TopkShape<G>::THREADS)) void route_topk_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights, int32_t* __restrict__ dest_of_src,
     int32_t* __restrict__ block_counts) {
-    constexpr int THREADS = Shape<G, V>::THREADS;
-    __shared__ int32_t ids_lds[kChunk * kKMax];
+    using S = TopkShape<G>;
+    static_assert(S::TOK <= kChunk, "one rank bitmap per workgroup");
+    __shared__ int32_t ids_lds[S::TOK * kKMax];
     __shared__ unsigned long long masks[kEMax];
 
     const int Epad = (E + 3) & ~3;
-    const int tok0 = blockIdx.x * kChunk;
-    const int ntok = min(kChunk, T - tok0);
-    topk_chunk<G, V>(logits, bias, T, E, k, tok0, topk_ids, topk_weights, ids_lds);
+    const int tok0 = blockIdx.x * S::TOK;
+    const int ntok = min(S::TOK, T - tok0);
+    const int grp = threadIdx.x / G;
+    topk_token<G, V>(logits, bias, T, E, k, tok0 + grp, grp, threadIdx.x % G, topk_ids, topk_weights, ids_lds);
     __syncthreads();
-    build_masks<THREADS>(ids_lds, ntok, k, Epad, 1, masks);
-    for (int s = threadIdx.x; s < ntok * k; s += THREADS)
+    build_masks<S::THREADS>(ids_lds, ntok, k, Epad, 1, masks);
+    for (int s = threadIdx.x; s < ntok * k; s += S::THREADS)
         dest_of_src[(size_t)tok0 * k + s] = slot_rank(masks, Epad, s / k, ids_lds[s]);
-    for (int e = threadIdx.x; e < Epad; e += THREADS)
+    for (int e = threadIdx.x; e < Epad; e += S::THREADS)
         block_counts[(size_t)blockIdx.x * Epad + e] = (e < E) ? __popcll(masks[e]) : 0;
 }
 
-// Kernel 2: every workgroup sums the histogram rows of all workgroups (one
-// int4 of experts per lane, rows spread over the lanes) into totals and into
-// the prefix over workgroups before it, scans the totals into offsets, and
-// finishes its own slots: dest = offset[e] + prefix[e] + rank.
-constexpr int kPlaceThreads = 512;
+// Exclusive scan of one int4 per lane over a workgroup of THREADS lanes.
+template <int THREADS>
+__device__ __forceinline__ i32x4 block_exclusive_scan4(i32x4 v, i32x4& total, i32x4* wave_tot) {
+    constexpr int NW = THREADS / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int w = threadIdx.x / kWave;
+    i32x4 incl = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        i32x4 y;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) y[c] = __shfl_up(incl[c], d);
+        if (lane >= d) incl += y;
+    }
+    if (lane == kWave - 1) wave_tot[w] = incl;
+    __syncthreads();
+    i32x4 before = {0, 0, 0, 0};
+    total = (i32x4){0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        if (i < w) before += wave_tot[i];
+        total += wave_tot[i];
+    }
+    __syncthreads();  // wave_tot may be reused by the caller's next tile
+    return before + incl - v;
+}
 
-__global__ __launch_bounds__(kPlaceThreads) void route_multi_place_kernel(
-    const int32_t* __restrict__ block_counts, int nb, int T, int E, int k, const int32_t* __restrict__ topk_ids,
-    int32_t* __restrict__ dest_of_src, int32_t* __restrict__ src_of_dest, int32_t* __restrict__ expert_offsets,
-    int32_t* __restrict__ expert_counts) {
-    __shared__ i32x4 part_tot[kPlaceThreads];
-    __shared__ i32x4 part_pre[kPlaceThreads];
+// 2. Workgroup c scans expert column group c (4 experts, one int4) down the
+// nb histogram rows: rows become exclusive prefixes, totals[4c..4c+3] the sums.
+constexpr int kScanThreads = 256;
+constexpr int kScanRowsPerLane = 8;
+
+__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int32_t* __restrict__ block_counts, int nb,
+                                                                  int Epad, int32_t* __restrict__ totals) {
+    __shared__ i32x4 wave_tot[kScanThreads / kWave];
+    const int Q = Epad / 4;
+    i32x4* col = reinterpret_cast<i32x4*>(block_counts) + blockIdx.x;
+    i32x4 carry = {0, 0, 0, 0};
+    for (int base = 0; base < nb; base += kScanThreads * kScanRowsPerLane) {
+        const int r0 = base + threadIdx.x * kScanRowsPerLane;
+        i32x4 v[kScanRowsPerLane];
+        i32x4 sum = {0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < kScanRowsPerLane; ++u) {
+            v[u] = (r0 + u < nb) ? col[(size_t)(r0 + u) * Q] : (i32x4){0, 0, 0, 0};
+            sum += v[u];
+        }
+        i32x4 tile_total;
+        i32x4 run = carry + block_exclusive_scan4<kScanThreads>(sum, tile_total, wave_tot);
+#pragma unroll
+        for (int u = 0; u < kScanRowsPerLane; ++u) {
+            if (r0 + u < nb) col[(size_t)(r0 + u) * Q] = run;
+            run += v[u];
+        }
+        carry += tile_total;
+    }
+    if (threadIdx.x == 0) reinterpret_cast<i32x4*>(totals)[blockIdx.x] = carry;
+}
+
+// 3. Per workgroup of step 1: offsets from the totals (LDS scan), then
+// dest = offset[e] + prefix[b][e] + rank for each of its slots.
+constexpr int kPlaceThreads = 256;
+constexpr int kPlaceSlots = kChunk * kKMax / kPlaceThreads;  // slots per lane, at most
+
+__global__ __launch_bounds__(kPlaceThreads) void route_place_kernel(
+    const int32_t* __restrict__ prefix, const int32_t* __restrict__ totals, int tok_per_block, int T, int E, int k,
+    const int32_t* __restrict__ topk_ids, int32_t* __restrict__ dest_of_src, int32_t* __restrict__ src_of_dest,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ expert_counts) {
     __shared__ int32_t s_tot[kEMax];
     __shared__ int32_t s_pre[kEMax];
     __shared__ int32_t s_off[kEMax + 1];
 
     const int Epad = (E + 3) & ~3;
-    const int Q = Epad / 4;              // int4 per histogram row (<= 128)
-    const int RP = kPlaceThreads / Q;    // rows read in parallel
     const int b = blockIdx.x;
-    const int q = threadIdx.x % Q;
-    const int rg = threadIdx.x / Q;
-
-    i32x4 tot = {0, 0, 0, 0};
-    i32x4 pre = {0, 0, 0, 0};
-    if (rg < RP) {
-        const i32x4* rows = reinterpret_cast<const i32x4*>(block_counts);
-#pragma unroll 4
-        for (int row = rg; row < nb; row += RP) {
-            const i32x4 c = rows[(size_t)row * Q + q];
-            tot += c;
-            if (row < b) pre += c;
+    const int tok0 = b * tok_per_block;
+    const int nslot = min(tok_per_block, T - tok0) * k;
+    // every load first: the slots (expert, rank), the totals, this row's prefix
+    int my_e[kPlaceSlots], my_r[kPlaceSlots];
+#pragma unroll
+    for (int u = 0; u < kPlaceSlots; ++u) {
+        const int s = threadIdx.x + u * kPlaceThreads;
+        if (s < nslot) {
+            my_e[u] = topk_ids[(size_t)tok0 * k + s];
+            my_r[u] = dest_of_src[(size_t)tok0 * k + s];
         }
     }
-    part_tot[threadIdx.x] = tot;
-    part_pre[threadIdx.x] = pre;
-    __syncthreads();
     for (int e = threadIdx.x; e < E; e += kPlaceThreads) {
-        const int qe = e >> 2, ce = e & 3;
-        int st = 0, sp = 0;
-        for (int g = 0; g < RP; ++g) {
-            st += part_tot[g * Q + qe][ce];
-            sp += part_pre[g * Q + qe][ce];
-        }
-        s_tot[e] = st;
-        s_pre[e] = sp;
+        s_tot[e] = totals[e];
+        s_pre[e] = prefix[(size_t)b * Epad + e];
     }
     __syncthreads();
     wave0_exclusive_scan(s_tot, s_off, E);
@@ -336,64 +410,186 @@ __global__ __launch_bounds__(kPlaceThreads) void route_multi_place_kernel(
         if (expert_counts != nullptr)
             for (int e = threadIdx.x; e < E; e += kPlaceThreads) expert_counts[e] = s_tot[e];
     }
-    const int tok0 = b * kChunk;
-    const int ntok = min(kChunk, T - tok0);
-    for (int s = threadIdx.x; s < ntok * k; s += kPlaceThreads) {
-        const size_t gs = (size_t)tok0 * k + s;
-        const int e = topk_ids[gs];
-        const int d = s_off[e] + s_pre[e] + dest_of_src[gs];
-        dest_of_src[gs] = d;
-        src_of_dest[d] = (int32_t)gs;
+#pragma unroll
+    for (int u = 0; u < kPlaceSlots; ++u) {
+        const int s = threadIdx.x + u * kPlaceThreads;
+        if (s < nslot) {
+            const size_t gs = (size_t)tok0 * k + s;
+            const int d = s_off[my_e[u]] + s_pre[my_e[u]] + my_r[u];
+            dest_of_src[gs] = d;
+            src_of_dest[d] = (int32_t)gs;
+        }
+    }
+}
+
+// 2+3 fused, for a small histogram matrix: workgroup g owns kFusedRows
+// consecutive top-k rows.  It sums every histogram row (one int4 of experts
+// per lane, RP rows in parallel) into the totals and the prefix before its
+// first row, extends that prefix over its own rows, scans the totals into
+// offsets, and writes its slots.  Reading the whole matrix per workgroup costs
+// L2 bandwidth instead of a third launch; the host picks this form only while
+// the matrix is small.
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedRows = 4;
+constexpr int kFusedSlots = kFusedRows * kChunk * kKMax / kFusedThreads;
+
+__global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
+    const int32_t* __restrict__ counts, int nb, int tok_per_row, int T, int E, int k,
+    const int32_t* __restrict__ topk_ids, int32_t* __restrict__ dest_of_src, int32_t* __restrict__ src_of_dest,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ expert_counts) {
+    __shared__ i32x4 part_tot[kFusedThreads];
+    __shared__ i32x4 part_pre[kFusedThreads];
+    __shared__ int32_t s_tot[kEMax];
+    __shared__ int32_t s_off[kEMax + 1];
+    __shared__ int32_t s_pre[kFusedRows][kEMax];
+
+    const int Epad = (E + 3) & ~3;
+    const int Q = Epad / 4;           // int4 per histogram row (<= 128)
+    const int RP = kFusedThreads / Q;  // rows summed in parallel (>= 8)
+    const int q = threadIdx.x % Q;
+    const int rg = threadIdx.x / Q;
+    const int row0 = blockIdx.x * kFusedRows;
+    const int nrows = min(kFusedRows, nb - row0);
+    const int tok0 = row0 * tok_per_row;
+    const int nslot = min(kFusedRows * tok_per_row, T - tok0) * k;
+
+    // every independent load first: the slots, then the histogram columns
+    int my_e[kFusedSlots], my_r[kFusedSlots];
+#pragma unroll
+    for (int u = 0; u < kFusedSlots; ++u) {
+        const int s = threadIdx.x + u * kFusedThreads;
+        if (s < nslot) {
+            my_e[u] = topk_ids[(size_t)tok0 * k + s];
+            my_r[u] = dest_of_src[(size_t)tok0 * k + s];
+        }
+    }
+    i32x4 tot = {0, 0, 0, 0};
+    i32x4 pre = {0, 0, 0, 0};
+    if (rg < RP) {
+        const i32x4* rows = reinterpret_cast<const i32x4*>(counts);
+#pragma unroll 8
+        for (int row = rg; row < nb; row += RP) {
+            const i32x4 c = rows[(size_t)row * Q + q];
+            tot += c;
+            if (row < row0) pre += c;
+        }
+    }
+    part_tot[threadIdx.x] = tot;
+    part_pre[threadIdx.x] = pre;
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kFusedThreads) {
+        const int qe = e >> 2, ce = e & 3;
+        int st = 0, sp = 0;
+        for (int g = 0; g < RP; ++g) {
+            st += part_tot[g * Q + qe][ce];
+            sp += part_pre[g * Q + qe][ce];
+        }
+        s_tot[e] = st;
+        // the prefix at the start of each of this workgroup's rows
+        for (int r = 0; r < nrows; ++r) {
+            s_pre[r][e] = sp;
+            if (r + 1 < nrows) sp += counts[(size_t)(row0 + r) * Epad + e];
+        }
+    }
+    __syncthreads();
+    wave0_exclusive_scan(s_tot, s_off, E);
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        for (int e = threadIdx.x; e <= E; e += kFusedThreads) expert_offsets[e] = s_off[e];
+        if (expert_counts != nullptr)
+            for (int e = threadIdx.x; e < E; e += kFusedThreads) expert_counts[e] = s_tot[e];
+    }
+#pragma unroll
+    for (int u = 0; u < kFusedSlots; ++u) {
+        const int s = threadIdx.x + u * kFusedThreads;
+        if (s < nslot) {
+            const size_t gs = (size_t)tok0 * k + s;
+            const int r = (s / k) / tok_per_row;
+            const int d = s_off[my_e[u]] + s_pre[r][my_e[u]] + my_r[u];
+            dest_of_src[gs] = d;
+            src_of_dest[d] = (int32_t)gs;
+        }
     }
 }
 
 template <int G, int V>
 hipError_t launch_route_gv(const RouteArgs& a, RouteVariant v, hipStream_t stream) {
-    constexpr int THREADS = Shape<G, V>::THREADS;
     if (v == RouteVariant::SingleWorkgroup) {
-        route_single_kernel<G, V><<<1, THREADS, 0, stream>>>(a.logits, a.bias, a.T, a.E, a.k, a.topk_ids,
-                                                             a.topk_weights, a.expert_offsets, a.expert_counts,
-                                                             a.dest_of_src, a.src_of_dest);
+        route_single_kernel<G, V><<<1, SingleShape<G>::THREADS, 0, stream>>>(
+            a.logits, a.bias, a.T, a.E, a.k, a.topk_ids, a.topk_weights, a.expert_offsets, a.expert_counts,
+            a.dest_of_src, a.src_of_dest);
         return hipGetLastError();
     }
-    const int nb = route_num_blocks(a.T);
+    using S = TopkShape<G>;
+    const int nb = (a.T + S::TOK - 1) / S::TOK;
+    const int Epad = route_padded_experts(a.E);
     int32_t* counts = static_cast<int32_t*>(a.workspace);
-    route_multi_topk_kernel<G, V><<<nb, THREADS, 0, stream>>>(a.logits, a.bias, a.T, a.E, a.k, a.topk_ids,
-                                                              a.topk_weights, a.dest_of_src, counts);
+    int32_t* totals = counts + (size_t)nb * Epad;
+    route_topk_kernel<G, V><<<nb, S::THREADS, 0, stream>>>(a.logits, a.bias, a.T, a.E, a.k, a.topk_ids,
+                                                           a.topk_weights, a.dest_of_src, counts);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    route_multi_place_kernel<<<nb, kPlaceThreads, 0, stream>>>(counts, nb, a.T, a.E, a.k, a.topk_ids, a.dest_of_src,
-                                                               a.src_of_dest, a.expert_offsets, a.expert_counts);
+    if (v == RouteVariant::TwoPass) {
+        route_scan_place_kernel<<<(nb + kFusedRows - 1) / kFusedRows, kFusedThreads, 0, stream>>>(
+            counts, nb, S::TOK, a.T, a.E, a.k, a.topk_ids, a.dest_of_src, a.src_of_dest, a.expert_offsets,
+            a.expert_counts);
+        return hipGetLastError();
+    }
+    route_scan_kernel<<<Epad / 4, kScanThreads, 0, stream>>>(counts, nb, Epad, totals);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    route_place_kernel<<<nb, kPlaceThreads, 0, stream>>>(counts, totals, S::TOK, a.T, a.E, a.k, a.topk_ids,
+                                                         a.dest_of_src, a.src_of_dest, a.expert_offsets,
+                                                         a.expert_counts);
     return hipGetLastError();
 }
 
 }  // namespace
 
+int route_keys_per_lane(int E) { return E > 32 ? 8 : 4; }
+
 int route_lanes_per_token(int E) {
-    const int need = (E + 3) / 4;
+    const int V = route_keys_per_lane(E);
+    const int need = (E + V - 1) / V;
     int G = 1;
-    while (G < need && G < 64) G <<= 1;
+    while (G < need) G <<= 1;
     return G;
 }
 
-RouteVariant route_pick_variant(int T, RouteVariant requested) {
+int route_tokens_per_block(int E) {
+    const int G = route_lanes_per_token(E);
+    return G >= 4 ? 16 : kWave / G;
+}
+
+RouteVariant route_pick_variant(int T, int E, RouteVariant requested) {
     if (T <= 0) return RouteVariant::SingleWorkgroup;  // writes the all-zero offsets
-    if (requested == RouteVariant::SingleWorkgroup && T <= kRouteFusedMaxTokens) return requested;
-    if (requested == RouteVariant::MultiWorkgroup) return requested;
-    return T <= kChunk ? RouteVariant::SingleWorkgroup : RouteVariant::MultiWorkgroup;
+    switch (requested) {
+        case RouteVariant::SingleWorkgroup:
+            if (T <= kRouteFusedMaxTokens) return requested;
+            break;
+        case RouteVariant::TwoPass:
+        case RouteVariant::ThreePass:
+            return requested;
+        default:
+            if (T <= kRouteSingleAutoMaxTokens) return RouteVariant::SingleWorkgroup;
+            break;
+    }
+    const int tb = route_tokens_per_block(E);
+    const size_t matrix = (size_t)((T + tb - 1) / tb) * route_padded_experts(E) * sizeof(int32_t);
+    return matrix <= kRouteTwoPassMaxBytes ? RouteVariant::TwoPass : RouteVariant::ThreePass;
 }
 
 hipError_t launch_route(const RouteArgs& a, RouteVariant variant, hipStream_t stream) {
-    const RouteVariant v = route_pick_variant(a.T, variant);
-    if (a.E > 256) return launch_route_gv<64, 8>(a, v, stream);
-    switch (route_lanes_per_token(a.E)) {
-        case 1: return launch_route_gv<1, 4>(a, v, stream);
-        case 2: return launch_route_gv<2, 4>(a, v, stream);
-        case 4: return launch_route_gv<4, 4>(a, v, stream);
-        case 8: return launch_route_gv<8, 4>(a, v, stream);
-        case 16: return launch_route_gv<16, 4>(a, v, stream);
-        case 32: return launch_route_gv<32, 4>(a, v, stream);
-        default: return launch_route_gv<64, 4>(a, v, stream);
+    const RouteVariant v = route_pick_variant(a.T, a.E, variant);
+    switch (route_lanes_per_token(a.E) * 16 + route_keys_per_lane(a.E)) {
+        case 1 * 16 + 4: return launch_route_gv<1, 4>(a, v, stream);
+        case 2 * 16 + 4: return launch_route_gv<2, 4>(a, v, stream);
+        case 4 * 16 + 4: return launch_route_gv<4, 4>(a, v, stream);
+        case 8 * 16 + 4: return launch_route_gv<8, 4>(a, v, stream);
+        case 8 * 16 + 8: return launch_route_gv<8, 8>(a, v, stream);
+        case 16 * 16 + 8: return launch_route_gv<16, 8>(a, v, stream);
+        case 32 * 16 + 8: return launch_route_gv<32, 8>(a, v, stream);
+        default: return launch_route_gv<64, 8>(a, v, stream);
     }
 }
 

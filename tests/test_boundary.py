@@ -70,10 +70,10 @@ def test_route_argument_errors(lib):
 
 
 def test_route_workspace_errors(lib, monkeypatch):
-    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", "multi")
+    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", "three")
     T, E, k = 4096, 128, 8
     need = lib.moe_route_workspace_bytes(T, E, k)
-    assert need == (4096 // 64) * 128 * 4
+    assert need == (4096 // 16 + 1) * 128 * 4  # 16-token histogram rows + one row of totals
     base = (FAKE, None, T, E, k, FAKE, FAKE, FAKE, None, FAKE, FAKE)
     assert status(lib, lib.moe_route(*base, None, need, None)) == "MOE_ERR_WORKSPACE"
     assert status(lib, lib.moe_route(*base, FAKE, need - 1, None)) == "MOE_ERR_WORKSPACE"
@@ -83,8 +83,9 @@ def test_route_workspace_errors(lib, monkeypatch):
 
 def test_route_workspace_size_rules(lib):
     assert lib.moe_route_workspace_bytes(0, 8, 2) > 0
-    assert lib.moe_route_workspace_bytes(1, 5, 2) == 8 * 4  # one row, experts padded to 8
-    assert lib.moe_route_workspace_bytes(65, 8, 2) == 2 * 8 * 4
+    assert lib.moe_route_workspace_bytes(1, 5, 2) == 2 * 8 * 4  # one row + totals, experts padded to 8
+    assert lib.moe_route_workspace_bytes(65, 8, 2) == (3 + 1) * 8 * 4  # 32 tokens per row at E=8
+    assert lib.moe_route_workspace_bytes(33, 512, 16) == (3 + 1) * 512 * 4
     assert lib.moe_route_workspace_bytes(4, 8, 9) == 0  # invalid
 
 

@@ -83,7 +83,7 @@ ROUTE_SHAPES = [  # (T, E, k): every lanes-per-token width, odd E, limits
 ]
 
 
-@pytest.mark.parametrize("variant", ["auto", "single", "multi"])
+@pytest.mark.parametrize("variant", ["auto", "single", "two", "three"])
 @pytest.mark.parametrize("T,E,k", ROUTE_SHAPES)
 def test_route_shapes_and_variants(dev, oracle_lib, monkeypatch, variant, T, E, k):
     if variant == "single" and T > 256:
@@ -97,7 +97,7 @@ def test_route_shapes_and_variants(dev, oracle_lib, monkeypatch, variant, T, E, 
                                f"route T={T} E={E} k={k}")
 
 
-@pytest.mark.parametrize("variant", ["single", "multi"])
+@pytest.mark.parametrize("variant", ["single", "two", "three"])
 @pytest.mark.parametrize("kind", ["quantized", "signed_zero", "constant", "wide"])
 def test_route_ties_and_special_rows(dev, oracle_lib, monkeypatch, variant, kind):
     monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
@@ -129,7 +129,7 @@ def test_route_variants_bit_identical_and_deterministic(dev, monkeypatch):
     _log("[route] determinism and variants")
     logits = inputs.quantized_logits(T, E, 9)
     results = []
-    for variant in ("single", "multi", "multi", "single"):
+    for variant in ("single", "two", "three", "two", "three", "single"):
         monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
         results.append(_route_gpu(dev, logits, k))
     for r in results[1:]:
