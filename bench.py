@@ -31,7 +31,12 @@ METRIC = "MoE glue tokens/sec + achieved HBM GB/s (% of MI355X peak), Qwen3-30B-
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "moe_glue_amd", "csrc")
-KERNEL_SOURCES = {"route": "route.hip", "expand": "expand.hip", "swiglu": "swiglu.hip", "combine": "combine.hip"}
+# Source files each call's kernels are built from (a traffic figure is valid
+# only while these are unchanged).
+KERNEL_SOURCES = {"route": ("route.hip", "route_common.h"), "expand": ("expand.hip",),
+                  "swiglu": ("swiglu.hip",), "combine": ("combine.hip",),
+                  "dispatch": ("dispatch.hip", "route_common.h")}
+SMALL_DISPATCH_MAX_T = 64  # the library's one-launch route + expand limit
 
 
 def algorithmic_bytes(cfg) -> dict:
@@ -41,12 +46,12 @@ def algorithmic_bytes(cfg) -> dict:
     expand = T * H * 2 + R * 4 + R * H * 2
     swiglu = R * 2 * I * 2 + R * I * 2
     combine = R * H * 2 + R * 4 + R * 4 + T * H * 2
-    return {"route": route, "expand": expand, "swiglu": swiglu, "combine": combine}
+    return {"route": route, "expand": expand, "swiglu": swiglu, "combine": combine, "dispatch": route + expand}
 
 
 def source_digest(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "device_common.h"):
+    for f in (*KERNEL_SOURCES[kernel], "device_common.h"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -150,31 +155,32 @@ class Sets:
                 "route": (p("logits"), p("bias"), T, E, k, p("topk_ids"), p("topk_weights"), p("expert_offsets"),
                           p("expert_counts"), p("dest_of_src"), p("src_of_dest"), p("workspace"),
                           d["workspace"].numel(), stream),
+                "dispatch": (p("logits"), p("bias"), T, E, k, p("x"), H, p("topk_ids"), p("topk_weights"),
+                             p("expert_offsets"), p("expert_counts"), p("dest_of_src"), p("src_of_dest"), p("x_exp"),
+                             p("workspace"), d["workspace"].numel(), stream),
                 "expand": (p("x"), p("dest_of_src"), T, H, k, p("x_exp"), stream),
                 "swiglu": (p("h"), R, I, p("act"), stream),
                 "combine": (p("y"), p("topk_weights"), p("dest_of_src"), T, H, k, p("out"), stream),
             }
             self.sets.append(d)
         self.fns = {"route": self.lib.moe_route, "expand": self.lib.moe_expand_rows,
-                    "swiglu": self.lib.moe_swiglu, "combine": self.lib.moe_combine}
+                    "dispatch": self.lib.moe_route_expand, "swiglu": self.lib.moe_swiglu,
+                    "combine": self.lib.moe_combine}
+        # Small (decode) batches take the one-launch dispatch (route + expand);
+        # larger ones call route and expand separately.
+        self.calls = (["dispatch", "swiglu", "combine"] if cfg.T <= SMALL_DISPATCH_MAX_T
+                      else ["route", "expand", "swiglu", "combine"])
 
     def step(self, s, events=None):
         a = self.sets[s % len(self.sets)]["args"]
         f = self.fns
+        rc = 0
         if events is not None:
             events[0].record()
-        rc = f["route"](*a["route"])
-        if events is not None:
-            events[1].record()
-        rc |= f["expand"](*a["expand"])
-        if events is not None:
-            events[2].record()
-        rc |= f["swiglu"](*a["swiglu"])
-        if events is not None:
-            events[3].record()
-        rc |= f["combine"](*a["combine"])
-        if events is not None:
-            events[4].record()
+        for i, name in enumerate(self.calls):
+            rc |= f[name](*a[name])
+            if events is not None:
+                events[i + 1].record()
         if rc:
             raise RuntimeError(f"a MoE glue call failed: {self.lib.moe_last_error().decode()}")
 
@@ -252,7 +258,7 @@ def main(argv=None):
         sets.step(s)
     torch.cuda.synchronize()
 
-    names = ["route", "expand", "swiglu", "combine"]
+    names = sets.calls
     # Timed region 1: the path alone, K steps back to back -> value, ms_per_step.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -270,10 +276,10 @@ def main(argv=None):
     events_elapsed = None
     if use_events:
         if args.events == "torch":
-            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
         else:
             stream = torch.cuda.current_stream(dev).cuda_stream
-            ev = [[HipEvent(stream) for _ in range(5)] for _ in range(args.steps)]
+            ev = [[HipEvent(stream) for _ in range(len(names) + 1)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         for s in range(args.steps):
@@ -292,7 +298,7 @@ def main(argv=None):
                           "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
                           "frac_of_achievable": round(gbps / achievable, 4),
                           "traffic": measured_traffic(n, cfg.name)}
-    dominant = max(("expand", "swiglu", "combine"), key=lambda n: kernels[n]["us"]) if kernels else "combine"
+    dominant = max((n for n in names if n != "route"), key=lambda n: kernels[n]["us"]) if kernels else None
     roofline = None
     if kernels:
         d = kernels[dominant]
@@ -315,7 +321,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}", "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
                    "input_sets": args.sets, "seed": args.seed},
-        "path_GBps": round(sum(ab.values()) / (elapsed / args.steps) / 1e9, 1),
+        "path_GBps": round(sum(ab[n] for n in names) / (elapsed / args.steps) / 1e9, 1),
         "achievable_copy_GBps": round(achievable, 1),
         "host_us_per_step": round(1e6 * host_s / args.steps, 2),
         "events": args.events,

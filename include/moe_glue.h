@@ -6,6 +6,7 @@
  *   moe_expand_rows  copy each token row to its k expert-contiguous rows
  *   moe_swiglu       gated SiLU on the first grouped GEMM's output
  *   moe_combine      routing-weighted sum of each token's k expert outputs
+ *   moe_route_expand route + expand in one launch for small (decode) batches
  *
  * The problem statement these calls follow:
  *   - "CuTeDSL at Perplexity" (Perplexity blog), section "Mixture of Experts
@@ -111,6 +112,25 @@ moe_status moe_route(const float* logits, const float* bias, int32_t T, int32_t 
  * MOE_ERR_UNSUPPORTED (T*H/8 >= 2^31), MOE_ERR_HIP. */
 moe_status moe_expand_rows(const uint16_t* x, const int32_t* dest_of_src, int32_t T, int32_t H,
                            int32_t k, uint16_t* x_expanded, void* stream);
+
+/* ------------------------------------------------ route + expand (dispatch) */
+
+/* The whole dispatch of a small batch in one launch: exactly the results of
+ * moe_route followed by moe_expand_rows on the same arguments (all outputs of
+ * both calls are written).  "CuTeDSL at Perplexity", sections "Grid
+ * synchronization" and MoE dispatch/combine > Local, describes decode
+ * dispatch as routing and copying in a single launch.  For T <= 64 this call
+ * uses one launch in which every workgroup recomputes the routing in LDS and
+ * copies its share of the rows (the workspace is not touched and may be NULL);
+ * for larger T it runs moe_route and then moe_expand_rows, and the workspace
+ * must be as moe_route requires (moe_route_workspace_bytes).
+ * Layouts, limits, alignment and errors: the union of moe_route's and
+ * moe_expand_rows'. */
+moe_status moe_route_expand(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                            const uint16_t* x, int32_t H, int32_t* topk_ids, float* topk_weights,
+                            int32_t* expert_offsets, int32_t* expert_counts, int32_t* dest_of_src,
+                            int32_t* src_of_dest, uint16_t* x_expanded, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* ----------------------------------------------------------------- SwiGLU */
 

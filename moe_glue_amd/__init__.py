@@ -8,6 +8,7 @@ Four calls, each a thin wrapper over the C ABI of the HIP library
     expand_rows(x, dest_of_src, k)     expandInputRows: token rows -> expert rows
     swiglu(h)                          doActivation: silu(gate) * up
     combine(y, topk_weights, dest_of_src)  weighted sum back to token order
+    route_expand(logits, k, x, bias=None)  route + expand, one launch for T <= 64
 
 Tensors are torch CUDA (HIP) tensors; bf16 tensors use torch.bfloat16.  Work
 is enqueued on torch's current stream and nothing synchronises.  Every call
@@ -19,7 +20,7 @@ from __future__ import annotations
 from ._binding import (E_MAX, EXPORTED, K_MAX, LIB_PATH, MoEGlueArgumentError, MoEGlueError, check,  # noqa: F401
                        load)
 
-__all__ = ["route", "route_workspace_bytes", "alloc_route_outputs", "expand_rows", "swiglu", "combine",
+__all__ = ["route", "route_workspace_bytes", "alloc_route_outputs", "expand_rows", "route_expand", "swiglu", "combine",
            "copy_probe", "MoEGlueError", "MoEGlueArgumentError", "E_MAX", "K_MAX"]
 
 
@@ -107,6 +108,35 @@ def expand_rows(x, dest_of_src, k: int, out=None):
             raise MoEGlueArgumentError(2, f"out must be [{T * k}, {H}]")
     st = load().moe_expand_rows(_ptr(x), _ptr(dest_of_src), T, H, k, _ptr(out), _stream(x.device))
     check(st, "moe_expand_rows")
+    return out
+
+
+def route_expand(logits, k: int, x, bias=None, out: dict | None = None) -> dict:
+    """route() and expand_rows() in one call (one launch for T <= 64); see
+    moe_route_expand in include/moe_glue.h.  Returns route()'s dict plus
+    "x_expanded"."""
+    torch = _torch()
+    _need_gpu("logits", logits, torch.float32, 2)
+    _need_gpu("x", x, torch.bfloat16, 2)
+    T, E = logits.shape
+    if x.shape[0] != T:
+        raise MoEGlueArgumentError(2, f"x has {x.shape[0]} rows, logits has T={T}")
+    H = x.shape[1]
+    if bias is not None:
+        _need_gpu("bias", bias, torch.float32, 1)
+        if bias.shape[0] != E:
+            raise MoEGlueArgumentError(2, f"bias has {bias.shape[0]} entries, logits has E={E}")
+    if out is None:
+        out = alloc_route_outputs(T, E, k, logits.device)
+    if out.get("x_expanded") is None:
+        out["x_expanded"] = torch.empty((T * k, H), dtype=torch.bfloat16, device=x.device)
+    ws = out["workspace"]
+    st = load().moe_route_expand(_ptr(logits), _ptr(bias), T, E, k, _ptr(x), H, _ptr(out["topk_ids"]),
+                                 _ptr(out["topk_weights"]), _ptr(out["expert_offsets"]),
+                                 _ptr(out.get("expert_counts")), _ptr(out["dest_of_src"]), _ptr(out["src_of_dest"]),
+                                 _ptr(out["x_expanded"]), _ptr(ws), ws.numel() if ws is not None else 0,
+                                 _stream(logits.device))
+    check(st, "moe_route_expand")
     return out
 
 

@@ -17,8 +17,8 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_UNSUPPORTED, MOE_ERR
 E_MAX = 512
 K_MAX = 16
 
-EXPORTED = ("moe_route_workspace_bytes", "moe_route", "moe_expand_rows", "moe_swiglu", "moe_combine",
-            "moe_copy_probe", "moe_status_string", "moe_last_error")
+EXPORTED = ("moe_route_workspace_bytes", "moe_route", "moe_expand_rows", "moe_route_expand", "moe_swiglu",
+            "moe_combine", "moe_copy_probe", "moe_status_string", "moe_last_error")
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -52,6 +52,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_route.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.moe_expand_rows.restype = ctypes.c_int
     lib.moe_expand_rows.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _vp]
+    lib.moe_route_expand.restype = ctypes.c_int
+    lib.moe_route_expand.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     ctypes.c_size_t, _vp]
     lib.moe_swiglu.restype = ctypes.c_int
     lib.moe_swiglu.argtypes = [_vp, _i32, _i32, _vp, _vp]
     lib.moe_combine.restype = ctypes.c_int

@@ -72,6 +72,46 @@ moe_status check_rows(const char* fn, int32_t rows, int32_t width, const char* w
     return MOE_OK;
 }
 
+// Route argument checks shared by moe_route and moe_route_expand.
+moe_status check_route_args(const char* fn, const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                            const int32_t* topk_ids, const float* topk_weights, const int32_t* expert_offsets,
+                            const int32_t* dest_of_src, const int32_t* src_of_dest) {
+    moe_status s = check_route_sizes(T, E, k);
+    if (s != MOE_OK) return s;
+    if (expert_offsets == nullptr) return fail(MOE_ERR_NULL, "%s: expert_offsets is NULL", fn);
+    if (T > 0) {
+        if (!logits || !topk_ids || !topk_weights || !dest_of_src || !src_of_dest)
+            return fail(MOE_ERR_NULL, "%s: a required tensor pointer is NULL", fn);
+        if (!aligned4(logits) || (bias && !aligned4(bias)))
+            return fail(MOE_ERR_ALIGN, "%s: logits/bias must be 4-byte aligned", fn);
+    }
+    return MOE_OK;
+}
+
+moe_status check_route_workspace(const char* fn, int32_t T, int32_t E, moe::RouteVariant v, const void* workspace,
+                                 size_t workspace_bytes) {
+    if (v == moe::RouteVariant::SingleWorkgroup) return MOE_OK;
+    const size_t need = moe::route_workspace_bytes(T, E);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given%s", fn, need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    if (!aligned16(workspace)) return fail(MOE_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", fn);
+    return MOE_OK;
+}
+
+moe_status check_expand_args(const char* fn, const uint16_t* x, const int32_t* dest_of_src, int32_t T, int32_t H,
+                             int32_t k, const uint16_t* x_expanded) {
+    moe_status s = check_rows(fn, T, H, "H");
+    if (s != MOE_OK) return s;
+    if (k < 1 || k > MOE_K_MAX) return fail(MOE_ERR_SHAPE, "%s: k=%d must be in [1, %d]", fn, k, MOE_K_MAX);
+    if ((int64_t)T * k >= INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "%s: T*k too large", fn);
+    if (T == 0) return MOE_OK;
+    if (!x || !dest_of_src || !x_expanded) return fail(MOE_ERR_NULL, "%s: NULL tensor pointer", fn);
+    if (!aligned16(x) || !aligned16(x_expanded))
+        return fail(MOE_ERR_ALIGN, "%s: x and x_expanded must be 16-byte aligned", fn);
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -96,26 +136,16 @@ size_t moe_route_workspace_bytes(int32_t T, int32_t E, int32_t k) {
     return moe::route_workspace_bytes(T, E);
 }
 
+
 moe_status moe_route(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k, int32_t* topk_ids,
                      float* topk_weights, int32_t* expert_offsets, int32_t* expert_counts, int32_t* dest_of_src,
                      int32_t* src_of_dest, void* workspace, size_t workspace_bytes, void* stream) {
-    moe_status s = check_route_sizes(T, E, k);
+    moe_status s = check_route_args("moe_route", logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets,
+                                    dest_of_src, src_of_dest);
     if (s != MOE_OK) return s;
-    if (expert_offsets == nullptr) return fail(MOE_ERR_NULL, "moe_route: expert_offsets is NULL");
-    if (T > 0) {
-        if (!logits || !topk_ids || !topk_weights || !dest_of_src || !src_of_dest)
-            return fail(MOE_ERR_NULL, "moe_route: a required tensor pointer is NULL");
-        if (!aligned4(logits) || (bias && !aligned4(bias)))
-            return fail(MOE_ERR_ALIGN, "moe_route: logits/bias must be 4-byte aligned");
-    }
     const moe::RouteVariant v = moe::route_pick_variant(T, E, requested_route_variant());
-    if (v != moe::RouteVariant::SingleWorkgroup) {
-        const size_t need = moe::route_workspace_bytes(T, E);
-        if (workspace == nullptr || workspace_bytes < need)
-            return fail(MOE_ERR_WORKSPACE, "moe_route: workspace of %zu bytes needed, %zu given%s", need,
-                        workspace_bytes, workspace ? "" : " (NULL)");
-        if (!aligned16(workspace)) return fail(MOE_ERR_WORKSPACE, "moe_route: workspace must be 16-byte aligned");
-    }
+    s = check_route_workspace("moe_route", T, E, v, workspace, workspace_bytes);
+    if (s != MOE_OK) return s;
     moe::RouteArgs a{logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, expert_counts,
                      dest_of_src, src_of_dest, workspace};
     return from_hip(moe::launch_route(a, v, static_cast<hipStream_t>(stream)), "moe_route launch");
@@ -123,16 +153,36 @@ moe_status moe_route(const float* logits, const float* bias, int32_t T, int32_t 
 
 moe_status moe_expand_rows(const uint16_t* x, const int32_t* dest_of_src, int32_t T, int32_t H, int32_t k,
                            uint16_t* x_expanded, void* stream) {
-    moe_status s = check_rows("moe_expand_rows", T, H, "H");
+    moe_status s = check_expand_args("moe_expand_rows", x, dest_of_src, T, H, k, x_expanded);
     if (s != MOE_OK) return s;
-    if (k < 1 || k > MOE_K_MAX) return fail(MOE_ERR_SHAPE, "moe_expand_rows: k=%d must be in [1, %d]", k, MOE_K_MAX);
-    if ((int64_t)T * k >= INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "moe_expand_rows: T*k too large");
     if (T == 0) return ok();
-    if (!x || !dest_of_src || !x_expanded) return fail(MOE_ERR_NULL, "moe_expand_rows: NULL tensor pointer");
-    if (!aligned16(x) || !aligned16(x_expanded))
-        return fail(MOE_ERR_ALIGN, "moe_expand_rows: x and x_expanded must be 16-byte aligned");
     return from_hip(moe::launch_expand_rows(x, dest_of_src, T, H, k, x_expanded, static_cast<hipStream_t>(stream)),
                     "moe_expand_rows launch");
+}
+
+moe_status moe_route_expand(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                            const uint16_t* x, int32_t H, int32_t* topk_ids, float* topk_weights,
+                            int32_t* expert_offsets, int32_t* expert_counts, int32_t* dest_of_src,
+                            int32_t* src_of_dest, uint16_t* x_expanded, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    moe_status s = check_route_args("moe_route_expand", logits, bias, T, E, k, topk_ids, topk_weights,
+                                    expert_offsets, dest_of_src, src_of_dest);
+    if (s != MOE_OK) return s;
+    s = check_expand_args("moe_route_expand", x, dest_of_src, T, H, k, x_expanded);
+    if (s != MOE_OK) return s;
+    const moe::RouteVariant requested = requested_route_variant();
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    moe::RouteArgs a{logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, expert_counts,
+                     dest_of_src, src_of_dest, workspace};
+    if (T <= moe::kRouteSmallDispatchMaxTokens && requested == moe::RouteVariant::Auto)
+        return from_hip(moe::launch_route_expand_small(a, x, H, x_expanded, st), "moe_route_expand launch");
+    const moe::RouteVariant v = moe::route_pick_variant(T, E, requested);
+    s = check_route_workspace("moe_route_expand", T, E, v, workspace, workspace_bytes);
+    if (s != MOE_OK) return s;
+    s = from_hip(moe::launch_route(a, v, st), "moe_route_expand launch (route)");
+    if (s != MOE_OK || T == 0) return s;
+    return from_hip(moe::launch_expand_rows(x, dest_of_src, T, H, k, x_expanded, st),
+                    "moe_route_expand launch (expand)");
 }
 
 moe_status moe_swiglu(const uint16_t* h, int32_t R, int32_t I, uint16_t* act, void* stream) {

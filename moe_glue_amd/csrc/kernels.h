@@ -53,6 +53,11 @@ RouteVariant route_pick_variant(int T, int E, RouteVariant requested);
 
 hipError_t launch_route(const RouteArgs& a, RouteVariant variant, hipStream_t stream);
 
+// Route + expand in one launch for T <= kRouteSmallDispatchMaxTokens: every
+// workgroup recomputes the routing in LDS and copies its share of the rows.
+constexpr int kRouteSmallDispatchMaxTokens = 64;
+hipError_t launch_route_expand_small(const RouteArgs& a, const void* x, int H, void* x_expanded, hipStream_t stream);
+
 // ---------------------------------------------------- streaming row kernels
 hipError_t launch_expand_rows(const void* x, const int32_t* dest_of_src, int T, int H, int k, void* x_expanded,
                               hipStream_t stream);

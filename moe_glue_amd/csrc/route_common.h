@@ -1,0 +1,264 @@
+// Device-side building blocks of the routing kernels (moe_route and the
+// fused small-batch route+expand): order-preserving keys, DPP/permlane group
+// reductions, the per-token top-k, the per-expert token bitmaps that give
+// each slot its stable rank, and the LDS exclusive scan.  See route.hip for
+// how they are put together.
+#pragma once
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace route_detail {
+
+constexpr int kChunk = 64;  // tokens per rank bitmap
+constexpr int kKMax = 16;
+constexpr int kEMax = 512;
+constexpr int kMaxChunks = kRouteFusedMaxTokens / kChunk;
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// fp32 -> uint32 whose unsigned order is the float order, with -0 == +0.
+__device__ __forceinline__ uint32_t orderable(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7FFFFFFFu) == 0) u = 0;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float unorderable(uint32_t o) {
+    uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+    return __builtin_bit_cast(float, u);
+}
+
+// Reductions over each aligned group of G lanes (G a power of two <= 64),
+// result in every lane of the group, without the LDS crossbar: DPP quad
+// permutations for lane distance 1 and 2, DPP half-row / row mirrors to join
+// quads into 8 and 16 lanes, and the gfx950 permlane16/permlane32 swaps to
+// join rows into 32 and 64 lanes.  All are VALU operations.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+enum class Op { Max, Min, FAdd };
+
+template <Op OP>
+__device__ __forceinline__ uint32_t apply(uint32_t a, uint32_t b) {
+    if constexpr (OP == Op::Max) return a > b ? a : b;
+    if constexpr (OP == Op::Min) return a < b ? a : b;
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+}
+
+template <int G, Op OP>
+__device__ __forceinline__ uint32_t group_reduce(uint32_t v) {
+    if constexpr (G > 1) v = apply<OP>(v, dpp<kQuadXor1>(v));
+    if constexpr (G > 2) v = apply<OP>(v, dpp<kQuadXor2>(v));
+    if constexpr (G > 4) v = apply<OP>(v, dpp<kRowHalfMirror>(v));
+    if constexpr (G > 8) v = apply<OP>(v, dpp<kRowMirror>(v));
+    if constexpr (G > 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = apply<OP>(p[0], p[1]);
+    }
+    if constexpr (G > 32) {
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        v = apply<OP>(p[0], p[1]);
+    }
+    return v;
+}
+
+// Top-k of token t by the G lanes of one group (lane gl of the group).
+// Every lane of the wave must call this (the reductions cross lanes); lanes
+// with t >= T compute on empty keys and write nothing.  Writes the ids to
+// ids_lds[tl * k + r], and topk_ids / topk_weights unless topk_ids is null.
+template <int G, int V>
+__device__ __forceinline__ void topk_token(const float* __restrict__ logits, const float* __restrict__ bias, int T,
+                                           int E, int k, int t, int tl, int gl, int32_t* __restrict__ topk_ids,
+                                           float* __restrict__ topk_weights, int32_t* ids_lds) {
+    constexpr int NJ = (kKMax + G - 1) / G;  // slots a lane may own: r = gl + G*j
+    const bool live = t < T;
+    float vals[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int e = gl + G * i;
+        vals[i] = (live && e < E) ? logits[(size_t)t * E + e] : 0.0f;
+    }
+    // key[i] of expert gl + G*i: orderable fp32 key, 0 = absent or taken
+    // (every real key is above 0: orderable(-inf) = 0x007FFFFF)
+    uint32_t key[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int e = gl + G * i;
+        float kf = vals[i];
+        if (bias != nullptr && e < E) kf = kf + bias[e];
+        key[i] = (live && e < E) ? orderable(kf) : 0u;
+    }
+    uint32_t my_id[NJ];
+    uint32_t my_key[NJ];
+    uint32_t top0 = 0;
+#pragma unroll
+    for (int r = 0; r < kKMax; ++r) {
+        if (r < k) {  // k is uniform: no divergence around the lane exchange
+            // the lane's best: largest key, lowest expert on equal keys
+            uint32_t best = key[0];
+            int bi = 0;
+#pragma unroll
+            for (int i = 1; i < V; ++i)
+                if (key[i] > best) {
+                    best = key[i];
+                    bi = i;
+                }
+            // the group's best key, then the lowest expert holding it
+            const uint32_t top = group_reduce<G, Op::Max>(best);
+            const uint32_t mine = (best == top) ? (uint32_t)(gl + G * bi) : 0xFFFFFFFFu;
+            const uint32_t win = group_reduce<G, Op::Min>(mine);
+#pragma unroll
+            for (int i = 0; i < V; ++i)  // the owner retires the winner
+                if ((uint32_t)(gl + G * i) == win) key[i] = 0u;
+            if (r == 0) top0 = top;
+            if ((r % G) == gl) {
+                my_id[r / G] = win;
+                my_key[r / G] = top;
+            }
+        }
+    }
+    // weights: softmax over the k selected keys, relative to the largest
+    const float key0 = unorderable(top0);
+    float ex[NJ];
+    float part = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int r = gl + G * j;
+        ex[j] = (r < k) ? expf(unorderable(my_key[j]) - key0) : 0.0f;
+        part += ex[j];
+    }
+    const float denom = __builtin_bit_cast(float, group_reduce<G, Op::FAdd>(__builtin_bit_cast(uint32_t, part)));
+    if (live) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int r = gl + G * j;
+            if (r < k) {
+                if (topk_ids != nullptr) {
+                    const size_t s = (size_t)t * k + r;
+                    topk_ids[s] = (int32_t)my_id[j];
+                    topk_weights[s] = ex[j] / denom;
+                }
+                ids_lds[tl * k + r] = (int32_t)my_id[j];
+            }
+        }
+    }
+}
+
+// Per-expert token bitmaps of `ntok` tokens (ids in ids_lds, token-major [ntok][k]):
+// masks[c * Epad + e] bit b set <=> token c*64 + b picked expert e.
+template <int THREADS>
+__device__ __forceinline__ void build_masks(const int32_t* ids_lds, int ntok, int k, int Epad, int nchunks,
+                                            unsigned long long* masks) {
+    for (int i = threadIdx.x; i < nchunks * Epad; i += THREADS) masks[i] = 0ull;
+    __syncthreads();
+    for (int s = threadIdx.x; s < ntok * k; s += THREADS) {
+        const int tl = s / k;
+        const int e = ids_lds[s];
+        atomicOr(&masks[(tl >> 6) * Epad + e], 1ull << (tl & 63));
+    }
+    __syncthreads();
+}
+
+// Rank of token tl among the block's tokens that picked expert e.
+__device__ __forceinline__ int slot_rank(const unsigned long long* masks, int Epad, int tl, int e) {
+    const int c = tl >> 6;
+    const unsigned long long below = (1ull << (tl & 63)) - 1ull;
+    int r = __popcll(masks[c * Epad + e] & below);
+    for (int c2 = 0; c2 < c; ++c2) r += __popcll(masks[c2 * Epad + e]);
+    return r;
+}
+
+__device__ __forceinline__ int mask_count(const unsigned long long* masks, int Epad, int nchunks, int e) {
+    int n = 0;
+    for (int c = 0; c < nchunks; ++c) n += __popcll(masks[c * Epad + e]);
+    return n;
+}
+
+// Exclusive prefix sum of in[0..n) into out[0..n], out[n] = total; n <= 512.
+// Run by wave 0 only: each lane owns ceil(n/64) consecutive entries.
+__device__ __forceinline__ void wave0_exclusive_scan(const int32_t* in, int32_t* out, int n) {
+    if (threadIdx.x >= kWave) return;
+    const int lane = threadIdx.x;
+    const int per = (n + kWave - 1) / kWave;
+    const int base = lane * per;
+    int local = 0;
+    for (int i = 0; i < per; ++i)
+        if (base + i < n) local += in[base + i];
+    int incl = local;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+    }
+    int run = incl - local;
+    for (int i = 0; i < per; ++i) {
+        if (base + i < n) {
+            out[base + i] = run;
+            run += in[base + i];
+        }
+    }
+    if (lane == kWave - 1) out[n] = incl;
+}
+
+// Launch shapes.
+// Multi-workgroup top-k: one token per group of G lanes, one pass, TOK tokens
+// per workgroup: 16 (THREADS = 16*G = 64..1024) for G >= 4, one wave below.
+template <int G>
+struct TopkShape {
+    static constexpr int TOK = (G >= 4) ? 16 : kWave / G;
+    static constexpr int THREADS = TOK * G;
+};
+// Single workgroup: up to 1024 lanes, at most 64 tokens per pass.
+template <int G>
+struct SingleShape {
+    static constexpr int THREADS = (kChunk * G < 1024) ? kChunk * G : 1024;
+    static constexpr int TOK_PER_PASS = THREADS / G;
+};
+
+
+// Top-k, histogram, offsets and ranks of T <= kRouteFusedMaxTokens tokens by
+// one workgroup, all in LDS: ids_lds [T][k], masks [nchunks][Epad],
+// s_cnt [E], s_off [E+1].  Waves whose tokens all lie at or past T skip the
+// top-k.  When `write` is set the workgroup also writes topk_ids,
+// topk_weights, expert_offsets and expert_counts (not the maps).
+template <int G, int V>
+__device__ __forceinline__ void route_small(const float* __restrict__ logits, const float* __restrict__ bias, int T,
+                                            int E, int k, bool write, int32_t* __restrict__ topk_ids,
+                                            float* __restrict__ topk_weights, int32_t* __restrict__ expert_offsets,
+                                            int32_t* __restrict__ expert_counts, int32_t* ids_lds,
+                                            unsigned long long* masks, int32_t* s_cnt, int32_t* s_off) {
+    using S = SingleShape<G>;
+    const int Epad = (E + 3) & ~3;
+    const int grp = threadIdx.x / G;
+    const int gl = threadIdx.x % G;
+    const int wave_first = (threadIdx.x / kWave) * (kWave / G);  // first token slot of this wave in a pass
+    for (int t0 = 0; t0 < T; t0 += S::TOK_PER_PASS) {
+        if (t0 + wave_first < T)  // wave-uniform: the lane exchange stays whole-wave
+            topk_token<G, V>(logits, bias, T, E, k, t0 + grp, t0 + grp, gl, write ? topk_ids : nullptr,
+                             topk_weights, ids_lds);
+    }
+    __syncthreads();
+    const int nchunks = (T + kChunk - 1) / kChunk;
+    build_masks<S::THREADS>(ids_lds, T, k, Epad, nchunks, masks);
+    for (int e = threadIdx.x; e < E; e += S::THREADS) s_cnt[e] = mask_count(masks, Epad, nchunks, e);
+    __syncthreads();
+    wave0_exclusive_scan(s_cnt, s_off, E);
+    __syncthreads();
+    if (write) {
+        for (int e = threadIdx.x; e <= E; e += S::THREADS) expert_offsets[e] = s_off[e];
+        if (expert_counts != nullptr)
+            for (int e = threadIdx.x; e < E; e += S::THREADS) expert_counts[e] = s_cnt[e];
+    }
+}
+
+}  // namespace route_detail
+}  // namespace moe

@@ -157,3 +157,20 @@ def test_fastdiv_host(tmp_path):
                     str(exe)], check=True, capture_output=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout + out.stderr
+
+
+def test_route_expand_argument_errors(lib):
+    def call(T=4, E=8, k=2, x=FAKE, H=256, ids=FAKE, xe=FAKE, ws=None, wsb=0):
+        return status(lib, lib.moe_route_expand(FAKE, None, T, E, k, x, H, ids, FAKE, FAKE, None, FAKE, FAKE, xe,
+                                                ws, wsb, None))
+
+    assert call(k=9) == "MOE_ERR_SHAPE"
+    assert call(E=600) == "MOE_ERR_UNSUPPORTED"
+    assert call(ids=None) == "MOE_ERR_NULL"
+    assert call(x=None) == "MOE_ERR_NULL"
+    assert call(xe=None) == "MOE_ERR_NULL"
+    assert call(H=12) == "MOE_ERR_ALIGN"
+    assert call(x=FAKE + 8) == "MOE_ERR_ALIGN"
+    # above the one-launch size the route workspace is required
+    assert call(T=65) == "MOE_ERR_WORKSPACE"
+    assert call(T=4096, E=128, k=8, ws=FAKE, wsb=16) == "MOE_ERR_WORKSPACE"

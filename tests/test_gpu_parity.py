@@ -225,3 +225,42 @@ def test_swiglu_shapes(dev, oracle_lib, R, I):
     got = G.to_host(mg.swiglu(G.to_dev(hb, dev)))
     torch.cuda.synchronize()
     compare.assert_bf16_close(got, oracle_lib.swiglu(hb), f"swiglu R={R} I={I}")
+
+
+# ------------------------------------------------------------------ route + expand
+@pytest.mark.parametrize("T,E,k,H", [(0, 16, 4, 256), (1, 8, 2, 8), (7, 128, 8, 2048), (32, 128, 8, 2048),
+                                     (64, 256, 8, 7168), (64, 512, 16, 264), (33, 64, 6, 4096), (20, 3, 3, 520),
+                                     (65, 128, 8, 2048), (300, 64, 6, 256)])
+def test_route_expand_matches_oracle(dev, oracle_lib, T, E, k, H):
+    import torch
+    import moe_glue_amd as mg
+
+    _log(f"[route_expand] T={T} E={E} k={k} H={H}")
+    cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8, bias_std=0.5 if E % 2 == 0 else 0.0)
+    inp = inputs.make_inputs(cfg, 6, parts=("x", "logits"))
+    bias = None if inp["bias"] is None else G.to_dev(inp["bias"], dev)
+    r = mg.route_expand(G.to_dev(inp["logits"], dev), k, G.to_dev(inp["x"], dev), bias)
+    torch.cuda.synchronize()
+    got = G.route_host(r)
+    ref = oracle_lib.route(inp["logits"], k, inp["bias"])
+    compare.assert_route_equal(got, ref, f"route_expand T={T} E={E} k={k}")
+    compare.assert_equal(got["x_expanded"], oracle_lib.expand_rows(inp["x"], ref["dest_of_src"], k), "x_expanded")
+
+
+@pytest.mark.parametrize("variant", ["single", "two", "three"])
+def test_route_expand_equals_separate_calls(dev, monkeypatch, variant):
+    import torch
+    import moe_glue_amd as mg
+
+    T, E, k, H = 48, 128, 8, 2048
+    _log(f"[route_expand] fused vs separate, forced variant {variant}")
+    cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
+    inp = inputs.make_inputs(cfg, 8, parts=("x", "logits"))
+    logits, x = G.to_dev(inp["logits"], dev), G.to_dev(inp["x"], dev)
+    fused = G.route_host(mg.route_expand(logits, k, x))
+    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
+    r = mg.route_expand(logits, k, x)
+    torch.cuda.synchronize()
+    sep = G.route_host(r)
+    for key in fused:
+        compare.assert_equal(sep[key], fused[key], f"fused vs {variant}: {key}")
