@@ -40,6 +40,9 @@ class Oracle:
         lib.moe_ref_route.restype = ctypes.c_int
         lib.moe_ref_route.argtypes = [_f32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       _i32p, _f32p, _i32p, _i32p, _i32p, _i32p]
+        lib.moe_ref_route_padded.restype = ctypes.c_int
+        lib.moe_ref_route_padded.argtypes = [_f32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             _i32p, _f32p, _i32p, _i32p, _i32p, _i32p]
         lib.moe_ref_expand_rows.restype = None
         lib.moe_ref_expand_rows.argtypes = [_u16p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u16p]
         lib.moe_ref_swiglu.restype = None
@@ -78,12 +81,38 @@ class Oracle:
         return {"topk_ids": ids, "topk_weights": w, "expert_offsets": offsets, "expert_counts": counts,
                 "dest_of_src": dest, "src_of_dest": src}
 
-    def expand_rows(self, x: np.ndarray, dest_of_src: np.ndarray, k: int) -> np.ndarray:
+    def route_padded(self, logits: np.ndarray, k: int, pad_to: int, bias: np.ndarray | None = None) -> dict:
+        """Route with each expert's segment padded to a multiple of pad_to rows;
+        src_of_dest has expert_offsets[E] entries, -1 on padding rows."""
+        logits = np.ascontiguousarray(logits, dtype=np.float32)
+        T, E = logits.shape
+        R = T * k
+        bound = R + E * (pad_to - 1)
+        ids = np.zeros((T, k), np.int32)
+        w = np.zeros((T, k), np.float32)
+        offsets = np.zeros(E + 1, np.int32)
+        counts = np.zeros(E, np.int32)
+        dest = np.zeros(R, np.int32)
+        src = np.full(max(bound, 1), -7, np.int32)
+        b = None
+        if bias is not None:
+            bias = np.ascontiguousarray(bias, dtype=np.float32)
+            b = _ptr(bias, _f32p)
+        rc = self.lib.moe_ref_route_padded(_ptr(logits, _f32p), b, T, E, k, pad_to, _ptr(ids, _i32p),
+                                           _ptr(w, _f32p), _ptr(offsets, _i32p), _ptr(counts, _i32p),
+                                           _ptr(dest, _i32p), _ptr(src, _i32p))
+        if rc != 0:
+            raise ValueError(f"moe_ref_route_padded rejected T={T} E={E} k={k} pad_to={pad_to} (rc={rc})")
+        return {"topk_ids": ids, "topk_weights": w, "expert_offsets": offsets, "expert_counts": counts,
+                "dest_of_src": dest, "src_of_dest": src[:offsets[E]]}
+
+    def expand_rows(self, x: np.ndarray, dest_of_src: np.ndarray, k: int, rows: int | None = None) -> np.ndarray:
+        """rows: height of the expanded buffer (T*k, or the padded total)."""
         x = np.ascontiguousarray(x, dtype=np.uint16)
         dest_of_src = np.ascontiguousarray(dest_of_src, dtype=np.int32).reshape(-1)
         T, H = x.shape
         assert dest_of_src.size == T * k
-        out = np.zeros((T * k, H), np.uint16)
+        out = np.zeros((T * k if rows is None else rows, H), np.uint16)
         self.lib.moe_ref_expand_rows(_ptr(x, _u16p), _ptr(dest_of_src, _i32p), T, H, k, _ptr(out, _u16p))
         return out
 
@@ -101,7 +130,7 @@ class Oracle:
         T, k = w.shape
         dest_of_src = np.ascontiguousarray(dest_of_src, dtype=np.int32).reshape(-1)
         R, H = y.shape
-        assert R == T * k and dest_of_src.size == R
+        assert R >= T * k and dest_of_src.size == T * k
         out = np.zeros((T, H), np.uint16)
         self.lib.moe_ref_combine(_ptr(y, _u16p), _ptr(w, _f32p), _ptr(dest_of_src, _i32p), T, H, k,
                                  _ptr(out, _u16p))

@@ -10,7 +10,9 @@
  *     broken toward the lower expert index; slots in descending key order;
  *   - inside an expert's list, rows are in ascending source slot order
  *     (ascending token, since a token never picks an expert twice);
- *   - segments are not padded: expert_offsets[E] = T*k;
+ *   - segments are not padded (expert_offsets[E] = T*k), except in
+ *     moe_ref_route_padded, which rounds each segment up to a multiple of
+ *     pad_to rows and marks the extra rows -1 in src_of_dest;
  *   - SwiGLU gate is the first I columns of the first GEMM's output, up the
  *     last I; act = silu(gate) * up with silu(g) = g / (1 + exp(-g));
  *   - every conversion to bf16 rounds to nearest, ties to even.
@@ -136,6 +138,49 @@ int moe_ref_route(const float* logits, const float* bias, int T, int E, int k,
     free(row);
     free(cursor);
     return 0;
+}
+
+/* Padded expert segments.  "CuTeDSL at Perplexity", MoE dispatch/combine >
+ * Local: after routing, tokens are copied into an optionally padded buffer
+ * for the MoE GEMM.  Reading: each expert's segment is rounded up to a
+ * multiple of pad_to rows (the grouped GEMM's row tile), the extra rows are
+ * padding that no token maps to:
+ *   offsets[e+1] = offsets[e] + pad_to * ceil(counts[e] / pad_to)
+ *   dest[s]      = offsets[ids[s]] + number of earlier slots with the same expert
+ *   src[p]       = s where dest[s] = p, and -1 on padding rows, p < offsets[E]
+ * ids, weights and counts are those of moe_ref_route.  pad_to = 1 is the
+ * unpadded layout. */
+int moe_ref_route_padded(const float* logits, const float* bias, int T, int E, int k, int pad_to,
+                         int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                         int32_t* expert_counts, int32_t* dest_of_src, int32_t* src_of_dest) {
+    if (pad_to < 1) return -1;
+    const int64_t R = (int64_t)T * k;
+    int32_t* plain_offsets = (int32_t*)malloc(sizeof(int32_t) * ((size_t)E + 1));
+    int32_t* plain_src = (int32_t*)malloc(sizeof(int32_t) * (size_t)(R > 0 ? R : 1));
+    int32_t* next_row = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+    if (!plain_offsets || !plain_src || !next_row) {
+        free(plain_offsets);
+        free(plain_src);
+        free(next_row);
+        return -2;
+    }
+    int rc = moe_ref_route(logits, bias, T, E, k, topk_ids, topk_weights, plain_offsets, expert_counts,
+                           dest_of_src, plain_src);
+    if (rc == 0) {
+        expert_offsets[0] = 0;
+        for (int e = 0; e < E; ++e) {
+            const int64_t padded = (int64_t)pad_to * ((expert_counts[e] + pad_to - 1) / pad_to);
+            expert_offsets[e + 1] = (int32_t)(expert_offsets[e] + padded);
+        }
+        for (int e = 0; e < E; ++e) next_row[e] = expert_offsets[e];
+        for (int64_t slot = 0; slot < R; ++slot) dest_of_src[slot] = next_row[topk_ids[slot]]++;
+        for (int64_t p = 0; p < expert_offsets[E]; ++p) src_of_dest[p] = -1;
+        for (int64_t slot = 0; slot < R; ++slot) src_of_dest[dest_of_src[slot]] = (int32_t)slot;
+    }
+    free(plain_offsets);
+    free(plain_src);
+    free(next_row);
+    return rc;
 }
 
 /* ---------------------------------------------------------------- expand */

@@ -40,6 +40,14 @@ int moe_ref_route(const float* logits, const float* bias, int T, int E, int k,
                   int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
                   int32_t* expert_counts, int32_t* dest_of_src, int32_t* src_of_dest);
 
+/* As moe_ref_route, with each expert's segment padded to a multiple of
+ * pad_to rows: expert_offsets are padded, dest_of_src points into the padded
+ * layout and src_of_dest (expert_offsets[E] entries, at most
+ * T*k + E*(pad_to-1)) holds -1 on padding rows.  Returns 0, or -1 on bad sizes. */
+int moe_ref_route_padded(const float* logits, const float* bias, int T, int E, int k, int pad_to,
+                         int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                         int32_t* expert_counts, int32_t* dest_of_src, int32_t* src_of_dest);
+
 /* x_exp[dest_of_src[t*k+j], :] = x[t, :] ; x [T,H], x_exp [T*k,H] (bf16 bits). */
 void moe_ref_expand_rows(const uint16_t* x, const int32_t* dest_of_src, int T, int H, int k,
                          uint16_t* x_exp);

@@ -146,3 +146,24 @@ def combine_exact(y: np.ndarray, w: np.ndarray, dest: np.ndarray):
             exact[t][c] = s
             out[t, c] = bf16_round_exact(s)
     return out, exact
+
+
+def padded_layout(ids: np.ndarray, E: int, pad_to: int):
+    """Build the padded expert-contiguous layout constructively: for each
+    expert in turn append its slots in ascending order, then append padding
+    (-1) until the segment length is a multiple of pad_to.  Returns
+    (offsets, dest_of_src, src_of_dest)."""
+    flat = [int(v) for v in np.asarray(ids).reshape(-1)]
+    layout = []
+    offsets = [0]
+    for e in range(E):
+        seg = [s for s in range(len(flat)) if flat[s] == e]
+        while len(seg) % pad_to != 0:
+            seg.append(-1)
+        layout.extend(seg)
+        offsets.append(len(layout))
+    dest = [0] * len(flat)
+    for p, s in enumerate(layout):
+        if s >= 0:
+            dest[s] = p
+    return np.array(offsets, np.int32), np.array(dest, np.int32), np.array(layout, np.int32)

@@ -204,6 +204,35 @@ def pin_route_properties(o) -> list:
     return fails
 
 
+def pin_route_padded(o) -> list:
+    """Padded segments: brute-force constructive layout on tiny inputs;
+    pad_to = 1 reproduces the unpadded route; segment invariants."""
+    fails = []
+    rng = _rng(8)
+    for (T, E, k, M) in ((5, 4, 2, 1), (5, 4, 2, 4), (7, 6, 3, 3), (9, 8, 2, 16), (3, 5, 5, 2), (0, 4, 2, 8),
+                         (12, 3, 1, 5)):
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        r = o.route_padded(logits, k, M)
+        ids_bf = bf.route_ids(logits, k) if T else np.zeros((0, k), np.int32)
+        offs, dest, src = bf.padded_layout(ids_bf, E, M)
+        for key, want in (("expert_offsets", offs), ("dest_of_src", dest), ("src_of_dest", src)):
+            if not np.array_equal(r[key], want):
+                fails.append(f"padded brute force T={T} E={E} k={k} M={M}: {key} {r[key].tolist()} != {want.tolist()}")
+        cnt = r["expert_counts"]
+        seg = np.diff(r["expert_offsets"])
+        if np.any(seg % M) or np.any(seg < cnt) or np.any(seg - cnt >= M):
+            fails.append(f"padded segments T={T} E={E} k={k} M={M}: lengths {seg.tolist()} counts {cnt.tolist()}")
+        if int((r["src_of_dest"] == -1).sum()) != int(seg.sum() - cnt.sum()):
+            fails.append(f"padded T={T} M={M}: padding rows are not all -1")
+    # pad_to = 1 is the unpadded route
+    logits = rng.standard_normal((40, 16)).astype(np.float32)
+    a, b = o.route_padded(logits, 4, 1), o.route(logits, 4)
+    for key in ("topk_ids", "expert_offsets", "expert_counts", "dest_of_src", "src_of_dest"):
+        if not np.array_equal(a[key], b[key]):
+            fails.append(f"pad_to=1 differs from the unpadded route in {key}")
+    return fails
+
+
 # ===================================================================== expand
 def pin_expand(o) -> list:
     fails = []
@@ -395,6 +424,7 @@ ALL_PINS = [
     pin_route_golden,
     pin_route_bruteforce,
     pin_route_properties,
+    pin_route_padded,
     pin_expand,
     pin_swiglu_layout_and_identities,
     pin_swiglu_expit_exhaustive,

@@ -55,6 +55,15 @@ MUTANTS = [
     ("src_of_dest_not_inverted",
      "for (int64_t s = 0; s < R; ++s) src_of_dest[dest_of_src[s]] = (int32_t)s;",
      "for (int64_t s = 0; s < R; ++s) src_of_dest[s] = dest_of_src[s];"),
+    ("padding_always_adds_a_tile",
+     "const int64_t padded = (int64_t)pad_to * ((expert_counts[e] + pad_to - 1) / pad_to);",
+     "const int64_t padded = (int64_t)pad_to * (expert_counts[e] / pad_to + 1);"),
+    ("padding_rows_not_marked",
+     "for (int64_t p = 0; p < expert_offsets[E]; ++p) src_of_dest[p] = -1;",
+     "for (int64_t p = 0; p < 0; ++p) src_of_dest[p] = -1;"),
+    ("padded_placement_uses_plain_offsets",
+     "for (int e = 0; e < E; ++e) next_row[e] = expert_offsets[e];",
+     "for (int e = 0; e < E; ++e) next_row[e] = plain_offsets[e];"),
     ("expand_not_permuted",
      "int64_t d = dest_of_src[(size_t)t * k + j];",
      "int64_t d = (int64_t)t * k + j;"),
