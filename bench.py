@@ -123,7 +123,7 @@ class HipEvent:
 class Sets:
     """NSETS complete input/output sets on the device, with ctypes argument tuples."""
 
-    def __init__(self, inp, nsets, dev):
+    def __init__(self, inp, nsets, dev, pad_to=1):
         import torch
         import moe_glue_amd as mg
 
@@ -144,17 +144,24 @@ class Sets:
         }
         self.sets = []
         T, H, E, k, I, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.R
+        P = mg.padded_rows(T, E, k, pad_to) if pad_to > 1 else R  # rows of the expert-contiguous buffers
         for s in range(nsets):
             d = {key: (None if v is None else v.clone()) for key, v in base.items()}
             d.update(mg.alloc_route_outputs(T, E, k, dev))
-            d["x_exp"] = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+            if pad_to > 1:
+                d["src_of_dest"] = torch.empty((P,), dtype=torch.int32, device=dev)
+                y = torch.empty((P, H), dtype=torch.bfloat16, device=dev)
+                y[:R].copy_(d["y"])
+                d["y"] = y
+            d["x_exp"] = torch.empty((P, H), dtype=torch.bfloat16, device=dev)
             d["act"] = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
             d["out"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
             p = lambda key: 0 if d[key] is None else d[key].data_ptr()  # noqa: E731
+            route_args = (p("topk_ids"), p("topk_weights"), p("expert_offsets"), p("expert_counts"),
+                          p("dest_of_src"), p("src_of_dest"), p("workspace"), d["workspace"].numel(), stream)
             d["args"] = {
-                "route": (p("logits"), p("bias"), T, E, k, p("topk_ids"), p("topk_weights"), p("expert_offsets"),
-                          p("expert_counts"), p("dest_of_src"), p("src_of_dest"), p("workspace"),
-                          d["workspace"].numel(), stream),
+                "route": ((p("logits"), p("bias"), T, E, k) + route_args if pad_to == 1
+                          else (p("logits"), p("bias"), T, E, k, pad_to) + route_args),
                 "dispatch": (p("logits"), p("bias"), T, E, k, p("x"), H, p("topk_ids"), p("topk_weights"),
                              p("expert_offsets"), p("expert_counts"), p("dest_of_src"), p("src_of_dest"), p("x_exp"),
                              p("workspace"), d["workspace"].numel(), stream),
@@ -163,12 +170,13 @@ class Sets:
                 "combine": (p("y"), p("topk_weights"), p("dest_of_src"), T, H, k, p("out"), stream),
             }
             self.sets.append(d)
-        self.fns = {"route": self.lib.moe_route, "expand": self.lib.moe_expand_rows,
+        self.fns = {"route": self.lib.moe_route if pad_to == 1 else self.lib.moe_route_padded,
+                    "expand": self.lib.moe_expand_rows,
                     "dispatch": self.lib.moe_route_expand, "swiglu": self.lib.moe_swiglu,
                     "combine": self.lib.moe_combine}
         # Small (decode) batches take the one-launch dispatch (route + expand);
         # larger ones call route and expand separately.
-        self.calls = (["dispatch", "swiglu", "combine"] if cfg.T <= SMALL_DISPATCH_MAX_T
+        self.calls = (["dispatch", "swiglu", "combine"] if cfg.T <= SMALL_DISPATCH_MAX_T and pad_to == 1
                       else ["route", "expand", "swiglu", "combine"])
 
     def step(self, s, events=None):
@@ -232,6 +240,7 @@ def main(argv=None):
     ap.add_argument("--config", default="qwen3_30b_a3b")
     ap.add_argument("--sets", type=int, default=4, help="input/output sets rotated across steps")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--pad", type=int, default=1, help="pad expert segments to a multiple of this many rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--events", choices=["nofence", "torch", "none"], default="nofence",
                     help="per-call HIP events inside the timed region (default: without the system fence)")
@@ -251,7 +260,7 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     cfg = I.CONFIGS[args.config]
     inp = I.make_inputs(cfg, args.seed)
-    sets = Sets(inp, args.sets, dev)
+    sets = Sets(inp, args.sets, dev, args.pad)
     achievable, _ = copy_probe_gbps(dev)
 
     for s in range(args.warmup):
@@ -320,7 +329,7 @@ def main(argv=None):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}", "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
-                   "input_sets": args.sets, "seed": args.seed},
+                   "input_sets": args.sets, "seed": args.seed, "pad_to": args.pad},
         "path_GBps": round(sum(ab[n] for n in names) / (elapsed / args.steps) / 1e9, 1),
         "achievable_copy_GBps": round(achievable, 1),
         "host_us_per_step": round(1e6 * host_s / args.steps, 2),

@@ -7,6 +7,7 @@
  *   moe_swiglu       gated SiLU on the first grouped GEMM's output
  *   moe_combine      routing-weighted sum of each token's k expert outputs
  *   moe_route_expand route + expand in one launch for small (decode) batches
+ *   moe_route_padded route with expert segments padded to a row multiple
  *
  * The problem statement these calls follow:
  *   - "CuTeDSL at Perplexity" (Perplexity blog), section "Mixture of Experts
@@ -59,6 +60,7 @@ typedef enum moe_status {
 
 #define MOE_E_MAX 512        /* experts                                             */
 #define MOE_K_MAX 16         /* experts per token                                   */
+#define MOE_PAD_MAX 4096     /* row multiple of padded expert segments              */
 
 /* ------------------------------------------------------------------ route */
 
@@ -97,6 +99,27 @@ moe_status moe_route(const float* logits, const float* bias, int32_t T, int32_t 
                      int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
                      int32_t* expert_counts, int32_t* dest_of_src, int32_t* src_of_dest,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Padded expert segments.  "CuTeDSL at Perplexity", MoE dispatch/combine >
+ * Local: the routed tokens are copied into an optionally padded buffer for the
+ * MoE GEMM.  Same as moe_route except that each expert's segment is rounded up
+ * to a multiple of pad_to rows (the grouped GEMM's row tile):
+ *   expert_offsets[e+1] = expert_offsets[e] + pad_to * ceil(expert_counts[e] / pad_to)
+ *   dest_of_src[s]      = expert_offsets[topk_ids[s]] + number of slots s' < s
+ *                         with the same expert
+ *   src_of_dest[p]      = s if dest_of_src[s] == p, and -1 on padding rows,
+ *                         for p < expert_offsets[E].
+ * src_of_dest must have room for moe_route_padded_rows(T, E, k, pad_to) =
+ * T*k + E*(pad_to-1) entries (the exact count is expert_offsets[E], on the
+ * device).  moe_expand_rows and moe_combine work unchanged on the padded
+ * layout with buffers of that many rows; expand does not write padding rows.
+ * pad_to = 1 is moe_route.  Limits: 1 <= pad_to <= MOE_PAD_MAX and the row
+ * bound below 2^31.  Workspace and errors as moe_route. */
+size_t moe_route_padded_rows(int32_t T, int32_t E, int32_t k, int32_t pad_to);
+moe_status moe_route_padded(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                            int32_t pad_to, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                            int32_t* expert_counts, int32_t* dest_of_src, int32_t* src_of_dest,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------- expand */
 

@@ -9,6 +9,7 @@ Four calls, each a thin wrapper over the C ABI of the HIP library
     swiglu(h)                          doActivation: silu(gate) * up
     combine(y, topk_weights, dest_of_src)  weighted sum back to token order
     route_expand(logits, k, x, bias=None)  route + expand, one launch for T <= 64
+    route_padded(logits, k, pad_to)    route with expert segments padded to pad_to rows
 
 Tensors are torch CUDA (HIP) tensors; bf16 tensors use torch.bfloat16.  Work
 is enqueued on torch's current stream and nothing synchronises.  Every call
@@ -20,7 +21,8 @@ from __future__ import annotations
 from ._binding import (E_MAX, EXPORTED, K_MAX, LIB_PATH, MoEGlueArgumentError, MoEGlueError, check,  # noqa: F401
                        load)
 
-__all__ = ["route", "route_workspace_bytes", "alloc_route_outputs", "expand_rows", "route_expand", "swiglu", "combine",
+__all__ = ["route", "route_workspace_bytes", "alloc_route_outputs", "route_padded", "padded_rows", "expand_rows",
+           "route_expand", "swiglu", "combine",
            "copy_probe", "MoEGlueError", "MoEGlueArgumentError", "E_MAX", "K_MAX"]
 
 
@@ -92,6 +94,33 @@ def route(logits, k: int, bias=None, out: dict | None = None) -> dict:
     return out
 
 
+def padded_rows(T: int, E: int, k: int, pad_to: int) -> int:
+    """Upper bound on the rows of the padded layout: T*k + E*(pad_to-1)."""
+    return int(load().moe_route_padded_rows(T, E, k, pad_to))
+
+
+def route_padded(logits, k: int, pad_to: int, bias=None, out: dict | None = None) -> dict:
+    """route() with each expert's segment padded to a multiple of pad_to rows;
+    src_of_dest has padded_rows() entries (-1 on padding rows, valid up to
+    expert_offsets[E]).  See moe_route_padded in include/moe_glue.h."""
+    torch = _torch()
+    _need_gpu("logits", logits, torch.float32, 2)
+    T, E = logits.shape
+    if bias is not None:
+        _need_gpu("bias", bias, torch.float32, 1)
+    if out is None:
+        out = alloc_route_outputs(T, E, k, logits.device)
+        out["src_of_dest"] = torch.empty((max(1, padded_rows(T, E, k, pad_to)),), dtype=torch.int32,
+                                         device=logits.device)
+    ws = out["workspace"]
+    st = load().moe_route_padded(_ptr(logits), _ptr(bias), T, E, k, pad_to, _ptr(out["topk_ids"]),
+                                 _ptr(out["topk_weights"]), _ptr(out["expert_offsets"]),
+                                 _ptr(out.get("expert_counts")), _ptr(out["dest_of_src"]), _ptr(out["src_of_dest"]),
+                                 _ptr(ws), ws.numel() if ws is not None else 0, _stream(logits.device))
+    check(st, "moe_route_padded")
+    return out
+
+
 def expand_rows(x, dest_of_src, k: int, out=None):
     """x_expanded[dest_of_src[t*k+j]] = x[t]; see moe_expand_rows in include/moe_glue.h."""
     torch = _torch()
@@ -104,8 +133,8 @@ def expand_rows(x, dest_of_src, k: int, out=None):
         out = torch.empty((T * k, H), dtype=torch.bfloat16, device=x.device)
     else:
         _need_gpu("out", out, torch.bfloat16, 2)
-        if tuple(out.shape) != (T * k, H):
-            raise MoEGlueArgumentError(2, f"out must be [{T * k}, {H}]")
+        if out.shape[0] < T * k or out.shape[1] != H:
+            raise MoEGlueArgumentError(2, f"out must be [>= {T * k}, {H}] (more rows for a padded layout)")
     st = load().moe_expand_rows(_ptr(x), _ptr(dest_of_src), T, H, k, _ptr(out), _stream(x.device))
     check(st, "moe_expand_rows")
     return out
@@ -167,8 +196,9 @@ def combine(y, topk_weights, dest_of_src, out=None):
     _need_gpu("dest_of_src", dest_of_src, torch.int32)
     T, k = topk_weights.shape
     R, H = y.shape
-    if R != T * k or dest_of_src.numel() != R:
-        raise MoEGlueArgumentError(2, f"y has {R} rows and dest_of_src {dest_of_src.numel()}, expected T*k={T * k}")
+    if R < T * k or dest_of_src.numel() != T * k:
+        raise MoEGlueArgumentError(2, f"y has {R} rows and dest_of_src {dest_of_src.numel()}; expected T*k={T * k} "
+                                      "entries and at least as many rows")
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
     else:

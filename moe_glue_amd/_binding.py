@@ -16,9 +16,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "lib
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(7)
 E_MAX = 512
 K_MAX = 16
+PAD_MAX = 4096
 
-EXPORTED = ("moe_route_workspace_bytes", "moe_route", "moe_expand_rows", "moe_route_expand", "moe_swiglu",
-            "moe_combine", "moe_copy_probe", "moe_status_string", "moe_last_error")
+EXPORTED = ("moe_route_workspace_bytes", "moe_route", "moe_route_padded_rows", "moe_route_padded",
+            "moe_expand_rows", "moe_route_expand", "moe_swiglu", "moe_combine", "moe_copy_probe",
+            "moe_status_string", "moe_last_error")
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -50,6 +52,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_route_workspace_bytes.argtypes = [_i32, _i32, _i32]
     lib.moe_route.restype = ctypes.c_int
     lib.moe_route.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.moe_route_padded_rows.restype = ctypes.c_size_t
+    lib.moe_route_padded_rows.argtypes = [_i32, _i32, _i32, _i32]
+    lib.moe_route_padded.restype = ctypes.c_int
+    lib.moe_route_padded.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     ctypes.c_size_t, _vp]
     lib.moe_expand_rows.restype = ctypes.c_int
     lib.moe_expand_rows.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _vp]
     lib.moe_route_expand.restype = ctypes.c_int

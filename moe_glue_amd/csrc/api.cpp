@@ -112,6 +112,31 @@ moe_status check_expand_args(const char* fn, const uint16_t* x, const int32_t* d
     return MOE_OK;
 }
 
+moe_status check_pad(const char* fn, int32_t T, int32_t E, int32_t k, int32_t pad_to) {
+    if (pad_to < 1) return fail(MOE_ERR_SHAPE, "%s: pad_to=%d must be >= 1", fn, pad_to);
+    if (pad_to > MOE_PAD_MAX) return fail(MOE_ERR_UNSUPPORTED, "%s: pad_to=%d exceeds %d", fn, pad_to, MOE_PAD_MAX);
+    if ((int64_t)T * k + (int64_t)E * (pad_to - 1) >= INT32_MAX)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: padded rows exceed the 2^31 limit", fn);
+    return MOE_OK;
+}
+
+moe_status route_impl(const char* fn, const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                      int32_t pad_to, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                      int32_t* expert_counts, int32_t* dest_of_src, int32_t* src_of_dest, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    moe_status s = check_route_args(fn, logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, dest_of_src,
+                                    src_of_dest);
+    if (s != MOE_OK) return s;
+    s = check_pad(fn, T, E, k, pad_to);
+    if (s != MOE_OK) return s;
+    const moe::RouteVariant v = moe::route_pick_variant(T, E, requested_route_variant());
+    s = check_route_workspace(fn, T, E, v, workspace, workspace_bytes);
+    if (s != MOE_OK) return s;
+    moe::RouteArgs a{logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, expert_counts,
+                     dest_of_src, src_of_dest, workspace, pad_to};
+    return from_hip(moe::launch_route(a, v, static_cast<hipStream_t>(stream)), fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -140,15 +165,22 @@ size_t moe_route_workspace_bytes(int32_t T, int32_t E, int32_t k) {
 moe_status moe_route(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k, int32_t* topk_ids,
                      float* topk_weights, int32_t* expert_offsets, int32_t* expert_counts, int32_t* dest_of_src,
                      int32_t* src_of_dest, void* workspace, size_t workspace_bytes, void* stream) {
-    moe_status s = check_route_args("moe_route", logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets,
-                                    dest_of_src, src_of_dest);
-    if (s != MOE_OK) return s;
-    const moe::RouteVariant v = moe::route_pick_variant(T, E, requested_route_variant());
-    s = check_route_workspace("moe_route", T, E, v, workspace, workspace_bytes);
-    if (s != MOE_OK) return s;
-    moe::RouteArgs a{logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, expert_counts,
-                     dest_of_src, src_of_dest, workspace};
-    return from_hip(moe::launch_route(a, v, static_cast<hipStream_t>(stream)), "moe_route launch");
+    return route_impl("moe_route", logits, bias, T, E, k, 1, topk_ids, topk_weights, expert_offsets, expert_counts,
+                      dest_of_src, src_of_dest, workspace, workspace_bytes, stream);
+}
+
+size_t moe_route_padded_rows(int32_t T, int32_t E, int32_t k, int32_t pad_to) {
+    if (check_route_sizes(T, E, k) != MOE_OK || check_pad("moe_route_padded_rows", T, E, k, pad_to) != MOE_OK)
+        return 0;
+    return (size_t)T * k + (size_t)E * (pad_to - 1);
+}
+
+moe_status moe_route_padded(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k, int32_t pad_to,
+                            int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets, int32_t* expert_counts,
+                            int32_t* dest_of_src, int32_t* src_of_dest, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    return route_impl("moe_route_padded", logits, bias, T, E, k, pad_to, topk_ids, topk_weights, expert_offsets,
+                      expert_counts, dest_of_src, src_of_dest, workspace, workspace_bytes, stream);
 }
 
 moe_status moe_expand_rows(const uint16_t* x, const int32_t* dest_of_src, int32_t T, int32_t H, int32_t k,
@@ -173,7 +205,7 @@ moe_status moe_route_expand(const float* logits, const float* bias, int32_t T, i
     const moe::RouteVariant requested = requested_route_variant();
     const hipStream_t st = static_cast<hipStream_t>(stream);
     moe::RouteArgs a{logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, expert_counts,
-                     dest_of_src, src_of_dest, workspace};
+                     dest_of_src, src_of_dest, workspace, /*pad_to=*/1};
     if (T <= moe::kRouteSmallDispatchMaxTokens && requested == moe::RouteVariant::Auto)
         return from_hip(moe::launch_route_expand_small(a, x, H, x_expanded, st), "moe_route_expand launch");
     const moe::RouteVariant v = moe::route_pick_variant(T, E, requested);

@@ -39,8 +39,8 @@ __global__ __launch_bounds__((SingleShape<G>::THREADS)) void route_expand_small_
     if (i < n) v = load_stream(x + i);
 
     const bool writer = blockIdx.x == 0;
-    route_small<G, V>(logits, bias, T, E, k, writer, topk_ids, topk_weights, expert_offsets, expert_counts, ids_lds,
-                      masks, s_cnt, s_off);
+    route_small<G, V>(logits, bias, T, E, k, 1, writer, topk_ids, topk_weights, expert_offsets, expert_counts,
+                      ids_lds, masks, s_cnt, s_off);
     const int Epad = (E + 3) & ~3;
     for (int s = threadIdx.x; s < T * k; s += S::THREADS) {
         const int e = ids_lds[s];

@@ -33,6 +33,7 @@ struct RouteArgs {
     int32_t* dest_of_src;
     int32_t* src_of_dest;
     void* workspace;
+    int pad_to;  // expert segments padded to a multiple of pad_to rows (1: unpadded)
 };
 
 // Keys per lane (8 above 32 experts, else 4) and lanes that cooperate on one token.

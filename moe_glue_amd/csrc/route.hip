@@ -43,7 +43,7 @@ using namespace route_detail;
 // ------------------------------------------------------------ single workgroup
 template <int G, int V>
 __global__ __launch_bounds__((SingleShape<G>::THREADS)) void route_single_kernel(
-    const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
+    const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k, int pad,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ expert_counts, int32_t* __restrict__ dest_of_src, int32_t* __restrict__ src_of_dest) {
     using S = SingleShape<G>;
@@ -52,9 +52,10 @@ __global__ __launch_bounds__((SingleShape<G>::THREADS)) void route_single_kernel
     __shared__ int32_t s_cnt[kEMax];
     __shared__ int32_t s_off[kEMax + 1];
 
-    route_small<G, V>(logits, bias, T, E, k, true, topk_ids, topk_weights, expert_offsets, expert_counts, ids_lds,
-                      masks, s_cnt, s_off);
+    route_small<G, V>(logits, bias, T, E, k, pad, true, topk_ids, topk_weights, expert_offsets, expert_counts,
+                      ids_lds, masks, s_cnt, s_off);
     const int Epad = (E + 3) & ~3;
+    mark_padding<S::THREADS>(s_cnt, s_off, E, pad, 0, 1, src_of_dest);
     for (int s = threadIdx.x; s < T * k; s += S::THREADS) {
         const int e = ids_lds[s];
         const int d = s_off[e] + slot_rank(masks, Epad, s / k, e);
@@ -156,6 +157,7 @@ constexpr int kPlaceSlots = kChunk * kKMax / kPlaceThreads;  // slots per lane, 
 
 __global__ __launch_bounds__(kPlaceThreads) void route_place_kernel(
     const int32_t* __restrict__ prefix, const int32_t* __restrict__ totals, int tok_per_block, int T, int E, int k,
+    int pad,
     const int32_t* __restrict__ topk_ids, int32_t* __restrict__ dest_of_src, int32_t* __restrict__ src_of_dest,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ expert_counts) {
     __shared__ int32_t s_tot[kEMax];
@@ -181,13 +183,14 @@ __global__ __launch_bounds__(kPlaceThreads) void route_place_kernel(
         s_pre[e] = prefix[(size_t)b * Epad + e];
     }
     __syncthreads();
-    wave0_exclusive_scan(s_tot, s_off, E);
+    wave0_exclusive_scan(s_tot, s_off, E, pad);
     __syncthreads();
     if (b == 0) {
         for (int e = threadIdx.x; e <= E; e += kPlaceThreads) expert_offsets[e] = s_off[e];
         if (expert_counts != nullptr)
             for (int e = threadIdx.x; e < E; e += kPlaceThreads) expert_counts[e] = s_tot[e];
     }
+    mark_padding<kPlaceThreads>(s_tot, s_off, E, pad, b, gridDim.x, src_of_dest);
 #pragma unroll
     for (int u = 0; u < kPlaceSlots; ++u) {
         const int s = threadIdx.x + u * kPlaceThreads;
@@ -212,7 +215,7 @@ constexpr int kFusedRows = 4;
 constexpr int kFusedSlots = kFusedRows * kChunk * kKMax / kFusedThreads;
 
 __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
-    const int32_t* __restrict__ counts, int nb, int tok_per_row, int T, int E, int k,
+    const int32_t* __restrict__ counts, int nb, int tok_per_row, int T, int E, int k, int pad,
     const int32_t* __restrict__ topk_ids, int32_t* __restrict__ dest_of_src, int32_t* __restrict__ src_of_dest,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ expert_counts) {
     __shared__ i32x4 part_tot[kFusedThreads];
@@ -270,13 +273,14 @@ __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
         }
     }
     __syncthreads();
-    wave0_exclusive_scan(s_tot, s_off, E);
+    wave0_exclusive_scan(s_tot, s_off, E, pad);
     __syncthreads();
     if (blockIdx.x == 0) {
         for (int e = threadIdx.x; e <= E; e += kFusedThreads) expert_offsets[e] = s_off[e];
         if (expert_counts != nullptr)
             for (int e = threadIdx.x; e < E; e += kFusedThreads) expert_counts[e] = s_tot[e];
     }
+    mark_padding<kFusedThreads>(s_tot, s_off, E, pad, blockIdx.x, gridDim.x, src_of_dest);
 #pragma unroll
     for (int u = 0; u < kFusedSlots; ++u) {
         const int s = threadIdx.x + u * kFusedThreads;
@@ -294,7 +298,7 @@ template <int G, int V>
 hipError_t launch_route_gv(const RouteArgs& a, RouteVariant v, hipStream_t stream) {
     if (v == RouteVariant::SingleWorkgroup) {
         route_single_kernel<G, V><<<1, SingleShape<G>::THREADS, 0, stream>>>(
-            a.logits, a.bias, a.T, a.E, a.k, a.topk_ids, a.topk_weights, a.expert_offsets, a.expert_counts,
+            a.logits, a.bias, a.T, a.E, a.k, a.pad_to, a.topk_ids, a.topk_weights, a.expert_offsets, a.expert_counts,
             a.dest_of_src, a.src_of_dest);
         return hipGetLastError();
     }
@@ -309,14 +313,14 @@ hipError_t launch_route_gv(const RouteArgs& a, RouteVariant v, hipStream_t strea
     if (err != hipSuccess) return err;
     if (v == RouteVariant::TwoPass) {
         route_scan_place_kernel<<<(nb + kFusedRows - 1) / kFusedRows, kFusedThreads, 0, stream>>>(
-            counts, nb, S::TOK, a.T, a.E, a.k, a.topk_ids, a.dest_of_src, a.src_of_dest, a.expert_offsets,
+            counts, nb, S::TOK, a.T, a.E, a.k, a.pad_to, a.topk_ids, a.dest_of_src, a.src_of_dest, a.expert_offsets,
             a.expert_counts);
         return hipGetLastError();
     }
     route_scan_kernel<<<Epad / 4, kScanThreads, 0, stream>>>(counts, nb, Epad, totals);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    route_place_kernel<<<nb, kPlaceThreads, 0, stream>>>(counts, totals, S::TOK, a.T, a.E, a.k, a.topk_ids,
+    route_place_kernel<<<nb, kPlaceThreads, 0, stream>>>(counts, totals, S::TOK, a.T, a.E, a.k, a.pad_to, a.topk_ids,
                                                          a.dest_of_src, a.src_of_dest, a.expert_offsets,
                                                          a.expert_counts);
     return hipGetLastError();

@@ -183,16 +183,21 @@ __device__ __forceinline__ int mask_count(const unsigned long long* masks, int E
     return n;
 }
 
-// Exclusive prefix sum of in[0..n) into out[0..n], out[n] = total; n <= 512.
-// Run by wave 0 only: each lane owns ceil(n/64) consecutive entries.
-__device__ __forceinline__ void wave0_exclusive_scan(const int32_t* in, int32_t* out, int n) {
+// Segment length of an expert with `count` rows: count rounded up to a
+// multiple of pad (pad = 1: unpadded).
+__device__ __forceinline__ int padded_len(int count, int pad) { return pad == 1 ? count : (count + pad - 1) / pad * pad; }
+
+// Exclusive prefix sum of the padded lengths of in[0..n) into out[0..n],
+// out[n] = total; n <= 512.  Run by wave 0 only: each lane owns ceil(n/64)
+// consecutive entries.
+__device__ __forceinline__ void wave0_exclusive_scan(const int32_t* in, int32_t* out, int n, int pad) {
     if (threadIdx.x >= kWave) return;
     const int lane = threadIdx.x;
     const int per = (n + kWave - 1) / kWave;
     const int base = lane * per;
     int local = 0;
     for (int i = 0; i < per; ++i)
-        if (base + i < n) local += in[base + i];
+        if (base + i < n) local += padded_len(in[base + i], pad);
     int incl = local;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -203,10 +208,28 @@ __device__ __forceinline__ void wave0_exclusive_scan(const int32_t* in, int32_t*
     for (int i = 0; i < per; ++i) {
         if (base + i < n) {
             out[base + i] = run;
-            run += in[base + i];
+            run += padded_len(in[base + i], pad);
         }
     }
     if (lane == kWave - 1) out[n] = incl;
+}
+
+// Padding rows of the padded layout get src_of_dest = -1: rows
+// [off[e] + cnt[e], off[e+1]) of every expert e.  Experts are dealt to the
+// waves of `nblocks` workgroups round-robin; the lanes of a wave stride over
+// the expert's padding rows.  No-op when pad == 1.
+template <int THREADS>
+__device__ __forceinline__ void mark_padding(const int32_t* s_cnt, const int32_t* s_off, int E, int pad, int block,
+                                             int nblocks, int32_t* __restrict__ src_of_dest) {
+    if (pad == 1) return;
+    constexpr int NW = THREADS / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int w = threadIdx.x / kWave;
+    for (int e = block * NW + w; e < E; e += nblocks * NW) {
+        const int first = s_off[e] + s_cnt[e];
+        const int last = s_off[e + 1];
+        for (int p = first + lane; p < last; p += kWave) src_of_dest[p] = -1;
+    }
 }
 
 // Launch shapes.
@@ -225,14 +248,14 @@ struct SingleShape {
 };
 
 
-// Top-k, histogram, offsets and ranks of T <= kRouteFusedMaxTokens tokens by
-// one workgroup, all in LDS: ids_lds [T][k], masks [nchunks][Epad],
-// s_cnt [E], s_off [E+1].  Waves whose tokens all lie at or past T skip the
+// Top-k, histogram, offsets (segments padded to a multiple of `pad`) and
+// ranks of T <= kRouteFusedMaxTokens tokens by one workgroup, all in LDS:
+// ids_lds [T][k], masks [nchunks][Epad], s_cnt [E], s_off [E+1].  Waves whose tokens all lie at or past T skip the
 // top-k.  When `write` is set the workgroup also writes topk_ids,
 // topk_weights, expert_offsets and expert_counts (not the maps).
 template <int G, int V>
 __device__ __forceinline__ void route_small(const float* __restrict__ logits, const float* __restrict__ bias, int T,
-                                            int E, int k, bool write, int32_t* __restrict__ topk_ids,
+                                            int E, int k, int pad, bool write, int32_t* __restrict__ topk_ids,
                                             float* __restrict__ topk_weights, int32_t* __restrict__ expert_offsets,
                                             int32_t* __restrict__ expert_counts, int32_t* ids_lds,
                                             unsigned long long* masks, int32_t* s_cnt, int32_t* s_off) {
@@ -251,7 +274,7 @@ __device__ __forceinline__ void route_small(const float* __restrict__ logits, co
     build_masks<S::THREADS>(ids_lds, T, k, Epad, nchunks, masks);
     for (int e = threadIdx.x; e < E; e += S::THREADS) s_cnt[e] = mask_count(masks, Epad, nchunks, e);
     __syncthreads();
-    wave0_exclusive_scan(s_cnt, s_off, E);
+    wave0_exclusive_scan(s_cnt, s_off, E, pad);
     __syncthreads();
     if (write) {
         for (int e = threadIdx.x; e <= E; e += S::THREADS) expert_offsets[e] = s_off[e];

@@ -45,6 +45,13 @@ class Oracle:
                                              _i32p, _f32p, _i32p, _i32p, _i32p, _i32p]
         lib.moe_ref_expand_rows.restype = None
         lib.moe_ref_expand_rows.argtypes = [_u16p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u16p]
+        lib.moe_ref_expand_rows_fp8.restype = None
+        lib.moe_ref_expand_rows_fp8.argtypes = [_u16p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, ctypes.POINTER(ctypes.c_uint8), _f32p]
+        lib.moe_ref_e4m3_from_f32.restype = ctypes.c_uint8
+        lib.moe_ref_e4m3_from_f32.argtypes = [ctypes.c_float]
+        lib.moe_ref_f64_from_e4m3.restype = ctypes.c_double
+        lib.moe_ref_f64_from_e4m3.argtypes = [ctypes.c_uint8]
         lib.moe_ref_swiglu.restype = None
         lib.moe_ref_swiglu.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, _u16p]
         lib.moe_ref_combine.restype = None
@@ -115,6 +122,24 @@ class Oracle:
         out = np.zeros((T * k if rows is None else rows, H), np.uint16)
         self.lib.moe_ref_expand_rows(_ptr(x, _u16p), _ptr(dest_of_src, _i32p), T, H, k, _ptr(out, _u16p))
         return out
+
+    def expand_rows_fp8(self, x: np.ndarray, dest_of_src: np.ndarray, k: int, group: int,
+                        rows: int | None = None):
+        """FP8 quantising expand; returns (codes uint8 [rows, H], scales fp32 [rows, H/group])."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        dest_of_src = np.ascontiguousarray(dest_of_src, dtype=np.int32).reshape(-1)
+        T, H = x.shape
+        assert dest_of_src.size == T * k and H % group == 0
+        n = T * k if rows is None else rows
+        q = np.zeros((n, H), np.uint8)
+        sc = np.zeros((n, H // group), np.float32)
+        self.lib.moe_ref_expand_rows_fp8(_ptr(x, _u16p), _ptr(dest_of_src, _i32p), T, H, k, group,
+                                         q.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), _ptr(sc, _f32p))
+        return q, sc
+
+    def e4m3_from_f32(self, v: np.ndarray) -> np.ndarray:
+        return np.array([self.lib.moe_ref_e4m3_from_f32(float(a)) for a in np.asarray(v, np.float32).reshape(-1)],
+                        np.uint8)
 
     def swiglu(self, h: np.ndarray) -> np.ndarray:
         h = np.ascontiguousarray(h, dtype=np.uint16)

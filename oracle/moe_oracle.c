@@ -198,6 +198,74 @@ void moe_ref_expand_rows(const uint16_t* x, const int32_t* dest_of_src, int T, i
     }
 }
 
+/* ------------------------------------------------------ FP8 quantising expand */
+
+/* Round an fp32 value to FP8 E4M3 (OCP "e4m3fn": 1 sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits, largest finite 448, no infinities), nearest with
+ * ties to even, saturating: magnitudes beyond 448 become 448.  Normal values
+ * keep 4 significant bits, so the quantum of a in [2^(e-1), 2^e) is 2^(e-4);
+ * below 2^-6 (subnormals) the quantum is 2^-9.  Returns the 8-bit code. */
+uint8_t moe_ref_e4m3_from_f32(float v) {
+    if (isnan(v)) return 0x7F;
+    const uint8_t sgn = signbit(v) ? 0x80 : 0x00;
+    double mag = fabs((double)v);
+    if (mag > 448.0) mag = 448.0;
+    if (mag == 0.0) return sgn;
+    int ex;
+    (void)frexp(mag, &ex);
+    const int qe = ex - 4 < -9 ? -9 : ex - 4;                        /* quantum exponent */
+    const double rounded = ldexp(nearbyint(ldexp(mag, -qe)), qe);
+    if (rounded == 0.0) return sgn;
+    if (rounded < 0x1p-6) return sgn | (uint8_t)(rounded / 0x1p-9);  /* subnormal: m * 2^-9 */
+    int re;
+    const double frac = frexp(rounded, &re);                         /* rounded = frac * 2^re, frac in [0.5, 1) */
+    const int mant = (int)((2.0 * frac - 1.0) * 8.0);                /* exact: 3 fraction bits */
+    return sgn | (uint8_t)(((re - 1 + 7) << 3) | mant);
+}
+
+double moe_ref_f64_from_e4m3(uint8_t c) {
+    int ex = (c >> 3) & 0xF, m = c & 0x7;
+    double mag = ex == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, ex - 7);
+    if (ex == 0xF && m == 0x7) mag = NAN;
+    return (c & 0x80) ? -mag : mag;
+}
+
+/* Quantising expand.  "CuTeDSL at Perplexity", Blackwell support: kernels
+ * were adapted for FP8 blockwise scaling, with absolute maxima over small
+ * groups of elements; FlashInfer PR analysis, section 1: expandInputRows
+ * applies an operation between its load and its store.  Reading: for each
+ * token t and group g of `group` consecutive columns,
+ *   amax  = max |x[t, c]| over the group
+ *   scale = fp32(amax / 448)
+ *   inv   = fp32(448 / amax)   (0 when amax = 0)
+ *   q[c]  = e4m3(fp32(x[t, c] * inv))   saturating, nearest-even
+ * and every expanded row dest_of_src[t*k + j] receives the token's codes
+ * (q_out [rows, H]) and scales (scales [rows, H/group]).  The divisions and
+ * the product are single fp32 operations, the precision the kernel decides in. */
+void moe_ref_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, int T, int H, int k, int group,
+                             uint8_t* q_out, float* scales) {
+    const int G = H / group;
+    for (int t = 0; t < T; ++t) {
+        for (int g = 0; g < G; ++g) {
+            float amax = 0.0f;
+            for (int c = g * group; c < (g + 1) * group; ++c) {
+                float v = fabsf((float)moe_ref_f64_from_bf16(x[(size_t)t * H + c]));
+                if (v > amax) amax = v;
+            }
+            const float scale = amax / 448.0f;
+            const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+            for (int j = 0; j < k; ++j) {
+                const int64_t dst_row = dest_of_src[(size_t)t * k + j];
+                scales[(size_t)dst_row * G + g] = scale;
+                for (int c = g * group; c < (g + 1) * group; ++c) {
+                    const float xv = (float)moe_ref_f64_from_bf16(x[(size_t)t * H + c]);
+                    q_out[(size_t)dst_row * H + c] = moe_ref_e4m3_from_f32(xv * inv);
+                }
+            }
+        }
+    }
+}
+
 /* ---------------------------------------------------------------- SwiGLU */
 
 /* FlashInfer PR analysis, sections 1-2 (doActivationKernel): the activation

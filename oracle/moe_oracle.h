@@ -52,6 +52,17 @@ int moe_ref_route_padded(const float* logits, const float* bias, int T, int E, i
 void moe_ref_expand_rows(const uint16_t* x, const int32_t* dest_of_src, int T, int H, int k,
                          uint16_t* x_exp);
 
+/* FP8 quantising expand: per token and group of `group` columns, scale =
+ * fp32(amax/448), codes = e4m3(fp32(x * fp32(448/amax))) saturating; codes
+ * and scales written to every expanded row of the token.
+ * q_out [rows, H] uint8 codes, scales [rows, H/group] fp32. */
+void moe_ref_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, int T, int H, int k, int group,
+                             uint8_t* q_out, float* scales);
+
+/* The oracle's FP8 E4M3 (OCP, bias 7, max 448) conversions, exported for pinning. */
+uint8_t moe_ref_e4m3_from_f32(float v);
+double moe_ref_f64_from_e4m3(uint8_t c);
+
 /* act[r,i] = bf16( silu(h[r,i]) * h[r,I+i] ), computed in fp64, rounded once. */
 void moe_ref_swiglu(const uint16_t* h, int R, int I, uint16_t* act);
 

@@ -420,12 +420,121 @@ def pin_bf16_rounding(o) -> list:
     return fails
 
 
+# ===================================================================== FP8
+def _torch_e4m3(v: np.ndarray) -> np.ndarray:
+    """torch's own fp32 -> float8_e4m3fn conversion (nearest-even) of clamped values."""
+    import torch
+
+    c = np.clip(np.asarray(v, np.float32), np.float32(-448.0), np.float32(448.0))
+    return torch.from_numpy(c.copy()).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+_E4M3_VALUES = None
+
+
+def _e4m3_table():
+    """All non-negative finite e4m3 values with their codes, ascending (independent decode)."""
+    global _E4M3_VALUES
+    if _E4M3_VALUES is None:
+        vals = []
+        for code in range(0x7F):
+            ex, m = code >> 3, code & 7
+            vals.append(m * 2.0 ** -9 if ex == 0 else (1 + m / 8) * 2.0 ** (ex - 7))
+        _E4M3_VALUES = np.array(vals)
+    return _E4M3_VALUES
+
+
+def pin_e4m3_rounding(o) -> list:
+    fails = []
+    rng = _rng(9)
+    v = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-4, 3, 4000),
+                        rng.uniform(-460, 460, 2000), np.array([0.0, -0.0, 448.0, 449.0, 463.0, 465.0, 1e9, -1e9,
+                                                                2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -11, 2.0 ** -6])
+                        ]).astype(np.float32)
+    got = o.e4m3_from_f32(v)
+    want = _torch_e4m3(v)
+    if not np.array_equal(got, want):
+        i = int(np.argmax(got != want))
+        fails.append(f"e4m3 vs torch at {v[i]!r}: {got[i]:#04x} != {want[i]:#04x}")
+    # exact table search: nearest e4m3 value, ties to the even code
+    table = _e4m3_table()
+    for x in v[:600]:
+        a = min(abs(float(x)), 448.0)
+        i = int(np.searchsorted(table, a, side="right")) - 1
+        lo, hi = table[i], table[min(i + 1, len(table) - 1)]
+        code = i if (a - lo < hi - a or (a - lo == hi - a and i % 2 == 0) or i == len(table) - 1) else i + 1
+        code |= 0x80 if np.signbit(x) else 0
+        g = int(o.e4m3_from_f32(np.array([x]))[0])
+        if g != code:
+            fails.append(f"e4m3 vs table at {x!r}: {g:#04x} != {code:#04x}")
+            break
+    # every finite code decodes and re-encodes to itself
+    for code in list(range(0x7F)) + list(range(0x80, 0xFF)):
+        back = int(o.e4m3_from_f32(np.array([o.lib.moe_ref_f64_from_e4m3(code)]))[0])
+        if back != code:
+            fails.append(f"e4m3 code {code:#04x} does not round-trip ({back:#04x})")
+            break
+    return fails
+
+
+def _bruteforce_expand_fp8(x_bits, dest, k, group, rows):
+    T, H = x_bits.shape
+    G = H // group
+    xv = bf.bf16_to_float(x_bits).astype(np.float32)
+    q = np.zeros((rows, H), np.uint8)
+    sc = np.zeros((rows, G), np.float32)
+    for t in range(T):
+        for g in range(G):
+            seg = xv[t, g * group:(g + 1) * group]
+            amax = np.float32(np.max(np.abs(seg)))
+            scale = np.float32(amax / np.float32(448.0))
+            inv = np.float32(np.float32(448.0) / amax) if amax > 0 else np.float32(0.0)
+            codes = _torch_e4m3((seg * inv).astype(np.float32))
+            for j in range(k):
+                d = dest[t * k + j]
+                q[d, g * group:(g + 1) * group] = codes
+                sc[d, g] = scale
+    return q, sc
+
+
+def pin_expand_fp8(o) -> list:
+    fails = []
+    rng = _rng(10)
+    for (T, H, E, k, group) in ((5, 32, 8, 2, 8), (4, 64, 6, 3, 16), (3, 128, 4, 4, 128), (6, 48, 5, 1, 16)):
+        x = _rand_bf16(rng, (T, H), scale=3.0)
+        x[0, :group] = 0  # an all-zero group
+        r = o.route(rng.standard_normal((T, E)).astype(np.float32), k)
+        q, sc = o.expand_rows_fp8(x, r["dest_of_src"], k, group)
+        qb, scb = _bruteforce_expand_fp8(x, r["dest_of_src"], k, group, T * k)
+        if not np.array_equal(q, qb):
+            fails.append(f"fp8 expand codes differ from brute force T={T} H={H} group={group}")
+        if not np.array_equal(sc, scb):
+            fails.append(f"fp8 expand scales differ from brute force T={T} H={H} group={group}")
+        # properties: the group maximum maps to +-448; dequantised values within half an e4m3 step
+        d0 = r["dest_of_src"][0]
+        if np.any(q[d0, :group] != 0) or sc[d0, 0] != 0:
+            fails.append("fp8 expand: an all-zero group is not all-zero codes with scale 0")
+        deq = np.array([[o.lib.moe_ref_f64_from_e4m3(int(c)) for c in row] for row in q]) * \
+            np.repeat(sc.astype(np.float64), group, axis=1)
+        for s in range(T * k):
+            t, dd = s // k, r["dest_of_src"][s]
+            ref = bf.bf16_to_float(x[t])
+            err = np.abs(deq[dd] - ref)
+            lim = np.maximum(np.abs(ref) * 2.0 ** -4, 2.0 ** -10 * np.repeat(sc[dd], group)) * (1 + 1e-6)
+            if np.any(err > lim):
+                fails.append(f"fp8 expand: dequantised error above half a step (T={T} group={group})")
+                break
+    return fails
+
+
 ALL_PINS = [
     pin_route_golden,
     pin_route_bruteforce,
     pin_route_properties,
     pin_route_padded,
     pin_expand,
+    pin_e4m3_rounding,
+    pin_expand_fp8,
     pin_swiglu_layout_and_identities,
     pin_swiglu_expit_exhaustive,
     pin_combine_identity,

@@ -174,3 +174,18 @@ def test_route_expand_argument_errors(lib):
     # above the one-launch size the route workspace is required
     assert call(T=65) == "MOE_ERR_WORKSPACE"
     assert call(T=4096, E=128, k=8, ws=FAKE, wsb=16) == "MOE_ERR_WORKSPACE"
+
+
+def test_route_padded_argument_errors(lib):
+    def call(T=4, E=8, k=2, pad=16):
+        return status(lib, lib.moe_route_padded(FAKE, None, T, E, k, pad, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                                FAKE, 1 << 20, None))
+
+    assert call(pad=0) == "MOE_ERR_SHAPE"
+    assert call(pad=-3) == "MOE_ERR_SHAPE"
+    assert call(pad=4097) == "MOE_ERR_UNSUPPORTED"
+    assert call(T=2 ** 22, E=512, k=16, pad=4096) == "MOE_ERR_UNSUPPORTED"
+    assert call(k=9) == "MOE_ERR_SHAPE"
+    assert lib.moe_route_padded_rows(4096, 128, 8, 128) == 4096 * 8 + 128 * 127
+    assert lib.moe_route_padded_rows(10, 4, 2, 1) == 20
+    assert lib.moe_route_padded_rows(10, 4, 2, 0) == 0

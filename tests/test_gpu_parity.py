@@ -264,3 +264,54 @@ def test_route_expand_equals_separate_calls(dev, monkeypatch, variant):
     sep = G.route_host(r)
     for key in fused:
         compare.assert_equal(sep[key], fused[key], f"fused vs {variant}: {key}")
+
+
+# ------------------------------------------------------------------ padded segments
+PADDED_CASES = [(1, 8, 2, 4), (33, 8, 2, 16), (100, 17, 5, 8), (300, 128, 8, 128), (64, 512, 16, 32),
+                (1023, 64, 6, 64), (257, 256, 8, 3), (4096, 128, 8, 128), (50, 4, 4, 1)]
+
+
+@pytest.mark.parametrize("variant", ["auto", "single", "two", "three"])
+@pytest.mark.parametrize("T,E,k,M", PADDED_CASES)
+def test_route_padded_matches_oracle(dev, oracle_lib, monkeypatch, variant, T, E, k, M):
+    import moe_glue_amd as mg
+
+    if variant == "single" and T > 256:
+        pytest.skip("single-workgroup route covers T <= 256")
+    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
+    _log(f"[route_padded] T={T} E={E} k={k} pad_to={M} variant={variant}")
+    rng = np.random.default_rng([T, E, k, M])
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    r = G.route_host(mg.route_padded(G.to_dev(logits, dev), k, M))
+    ref = oracle_lib.route_padded(logits, k, M)
+    P = int(ref["expert_offsets"][E])
+    r["src_of_dest"] = r["src_of_dest"][:P]
+    compare.assert_route_equal(r, ref, f"route_padded T={T} E={E} k={k} M={M}")
+
+
+@pytest.mark.parametrize("T,E,k,M,H", [(300, 128, 8, 128, 2048), (77, 17, 5, 16, 520), (1023, 64, 6, 64, 4096)])
+def test_expand_combine_on_padded_layout(dev, oracle_lib, T, E, k, M, H):
+    import torch
+    import moe_glue_amd as mg
+
+    _log(f"[padded rows] T={T} E={E} k={k} pad_to={M} H={H}")
+    cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
+    inp = inputs.make_inputs(cfg, 9, parts=("x", "logits"))
+    ref = oracle_lib.route_padded(inp["logits"], k, M)
+    P = int(ref["expert_offsets"][E])
+    r = mg.route_padded(G.to_dev(inp["logits"], dev), k, M)
+    sentinel = 0x7F7F
+    xe = torch.full((mg.padded_rows(T, E, k, M), H), sentinel, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    mg.expand_rows(G.to_dev(inp["x"], dev), r["dest_of_src"], k, out=xe)
+    torch.cuda.synchronize()
+    got = G.to_host(xe)[:P]
+    want = oracle_lib.expand_rows(inp["x"], ref["dest_of_src"], k, rows=P)
+    pad_rows = ref["src_of_dest"] < 0
+    compare.assert_equal(got[~pad_rows], want[~pad_rows], "padded x_expanded (valid rows)")
+    assert np.all(got[pad_rows] == sentinel), "expand wrote into padding rows"
+    # combine reads only valid rows of a padded y
+    y = inputs.normal_bf16(9, 77, (P, H))
+    out = mg.combine(G.to_dev(y, dev), r["topk_weights"], r["dest_of_src"])
+    torch.cuda.synchronize()
+    compare.assert_bf16_close(G.to_host(out), oracle_lib.combine(y, ref["topk_weights"], ref["dest_of_src"]),
+                              "combine on padded y")

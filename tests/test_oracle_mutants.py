@@ -70,6 +70,19 @@ MUTANTS = [
     ("expand_index_transposed",
      "int64_t d = dest_of_src[(size_t)t * k + j];",
      "int64_t d = dest_of_src[(size_t)j * T + t];"),
+    ("e4m3_bias_8", "return sgn | (uint8_t)(((re - 1 + 7) << 3) | mant);",
+     "return sgn | (uint8_t)(((re - 1 + 8) << 3) | mant);"),
+    ("e4m3_not_saturating", "if (mag > 448.0) mag = 448.0;", "(void)0;"),
+    ("e4m3_subnormal_quantum", "const int qe = ex - 4 < -9 ? -9 : ex - 4;", "const int qe = ex - 4 < -10 ? -10 : ex - 4;"),
+    ("e4m3_truncates", "const double rounded = ldexp(nearbyint(ldexp(mag, -qe)), qe);",
+     "const double rounded = ldexp(floor(ldexp(mag, -qe)), qe);"),
+    ("fp8_scale_240", "const float scale = amax / 448.0f;", "const float scale = amax / 240.0f;"),
+    ("fp8_divide_by_scale", "q_out[(size_t)dst_row * H + c] = moe_ref_e4m3_from_f32(xv * inv);",
+     "q_out[(size_t)dst_row * H + c] = moe_ref_e4m3_from_f32(xv / scale);"),
+    ("fp8_scales_by_token", "scales[(size_t)dst_row * G + g] = scale;", "scales[(size_t)t * G + g] = scale;"),
+    ("fp8_amax_first_only",
+     "for (int c = g * group; c < (g + 1) * group; ++c) {\n                float v = fabsf(",
+     "for (int c = g * group; c < g * group + 1; ++c) {\n                float v = fabsf("),
     ("swiglu_gate_up_swapped",
      "double g = moe_ref_f64_from_bf16(h[(size_t)r * 2 * I + i]);\n"
      "            double u = moe_ref_f64_from_bf16(h[(size_t)r * 2 * I + I + i]);",
