@@ -33,20 +33,22 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "moe_glue_amd", "csrc")
 # Source files each call's kernels are built from (a traffic figure is valid
 # only while these are unchanged).
-KERNEL_SOURCES = {"route": ("route.hip", "route_common.h"), "expand": ("expand.hip",),
+KERNEL_SOURCES = {"route": ("route.hip", "route_common.h"), "expand": ("expand.hip",), "expand_fp8": ("quant.hip",),
                   "swiglu": ("swiglu.hip",), "combine": ("combine.hip",),
                   "dispatch": ("dispatch.hip", "route_common.h")}
 SMALL_DISPATCH_MAX_T = 64  # the library's one-launch route + expand limit
 
 
-def algorithmic_bytes(cfg) -> dict:
+def algorithmic_bytes(cfg, fp8_group: int = 0) -> dict:
     """Bytes each call must move: every input read once, every output written once."""
     T, H, E, k, I, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.R
     route = T * E * 4 + (E * 4 if cfg.bias_std > 0 else 0) + R * 4 + R * 4 + R * 4 + R * 4 + (E + 1) * 4 + E * 4
     expand = T * H * 2 + R * 4 + R * H * 2
     swiglu = R * 2 * I * 2 + R * I * 2
     combine = R * H * 2 + R * 4 + R * 4 + T * H * 2
-    return {"route": route, "expand": expand, "swiglu": swiglu, "combine": combine, "dispatch": route + expand}
+    expand_fp8 = T * H * 2 + R * 4 + R * H + (R * (H // fp8_group) * 4 if fp8_group else 0)
+    return {"route": route, "expand": expand, "swiglu": swiglu, "combine": combine, "dispatch": route + expand,
+            "expand_fp8": expand_fp8}
 
 
 def source_digest(kernel: str) -> str:
@@ -123,7 +125,7 @@ class HipEvent:
 class Sets:
     """NSETS complete input/output sets on the device, with ctypes argument tuples."""
 
-    def __init__(self, inp, nsets, dev, pad_to=1):
+    def __init__(self, inp, nsets, dev, pad_to=1, fp8_group=0):
         import torch
         import moe_glue_amd as mg
 
@@ -154,6 +156,9 @@ class Sets:
                 y[:R].copy_(d["y"])
                 d["y"] = y
             d["x_exp"] = torch.empty((P, H), dtype=torch.bfloat16, device=dev)
+            if fp8_group:
+                d["x_exp"] = torch.empty((P, H), dtype=torch.uint8, device=dev)
+                d["x_scales"] = torch.empty((P, H // fp8_group), dtype=torch.float32, device=dev)
             d["act"] = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
             d["out"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
             p = lambda key: 0 if d[key] is None else d[key].data_ptr()  # noqa: E731
@@ -166,18 +171,24 @@ class Sets:
                              p("expert_offsets"), p("expert_counts"), p("dest_of_src"), p("src_of_dest"), p("x_exp"),
                              p("workspace"), d["workspace"].numel(), stream),
                 "expand": (p("x"), p("dest_of_src"), T, H, k, p("x_exp"), stream),
+                "expand_fp8": ((p("x"), p("dest_of_src"), T, H, k, fp8_group, p("x_exp"), p("x_scales"), stream)
+                               if fp8_group else None),
                 "swiglu": (p("h"), R, I, p("act"), stream),
                 "combine": (p("y"), p("topk_weights"), p("dest_of_src"), T, H, k, p("out"), stream),
             }
             self.sets.append(d)
         self.fns = {"route": self.lib.moe_route if pad_to == 1 else self.lib.moe_route_padded,
-                    "expand": self.lib.moe_expand_rows,
+                    "expand": self.lib.moe_expand_rows, "expand_fp8": self.lib.moe_expand_rows_fp8,
                     "dispatch": self.lib.moe_route_expand, "swiglu": self.lib.moe_swiglu,
                     "combine": self.lib.moe_combine}
         # Small (decode) batches take the one-launch dispatch (route + expand);
         # larger ones call route and expand separately.
-        self.calls = (["dispatch", "swiglu", "combine"] if cfg.T <= SMALL_DISPATCH_MAX_T and pad_to == 1
-                      else ["route", "expand", "swiglu", "combine"])
+        if fp8_group:
+            self.calls = ["route", "expand_fp8", "swiglu", "combine"]
+        elif cfg.T <= SMALL_DISPATCH_MAX_T and pad_to == 1:
+            self.calls = ["dispatch", "swiglu", "combine"]
+        else:
+            self.calls = ["route", "expand", "swiglu", "combine"]
 
     def step(self, s, events=None):
         a = self.sets[s % len(self.sets)]["args"]
@@ -241,6 +252,8 @@ def main(argv=None):
     ap.add_argument("--sets", type=int, default=4, help="input/output sets rotated across steps")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--pad", type=int, default=1, help="pad expert segments to a multiple of this many rows")
+    ap.add_argument("--fp8-group", type=int, default=0,
+                    help="expand with FP8 E4M3 quantisation, one scale per this many columns (0: bf16 expand)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--events", choices=["nofence", "torch", "none"], default="nofence",
                     help="per-call HIP events inside the timed region (default: without the system fence)")
@@ -260,7 +273,7 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     cfg = I.CONFIGS[args.config]
     inp = I.make_inputs(cfg, args.seed)
-    sets = Sets(inp, args.sets, dev, args.pad)
+    sets = Sets(inp, args.sets, dev, args.pad, args.fp8_group)
     achievable, _ = copy_probe_gbps(dev)
 
     for s in range(args.warmup):
@@ -296,7 +309,7 @@ def main(argv=None):
         torch.cuda.synchronize()
         events_elapsed = time.perf_counter() - t1
 
-    ab = algorithmic_bytes(cfg)
+    ab = algorithmic_bytes(cfg, args.fp8_group)
     kernels = {}
     if use_events:
         for i, n in enumerate(names):
@@ -329,7 +342,7 @@ def main(argv=None):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}", "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
-                   "input_sets": args.sets, "seed": args.seed, "pad_to": args.pad},
+                   "input_sets": args.sets, "seed": args.seed, "pad_to": args.pad, "fp8_group": args.fp8_group},
         "path_GBps": round(sum(ab[n] for n in names) / (elapsed / args.steps) / 1e9, 1),
         "achievable_copy_GBps": round(achievable, 1),
         "host_us_per_step": round(1e6 * host_s / args.steps, 2),

@@ -8,6 +8,7 @@
  *   moe_combine      routing-weighted sum of each token's k expert outputs
  *   moe_route_expand route + expand in one launch for small (decode) batches
  *   moe_route_padded route with expert segments padded to a row multiple
+ *   moe_expand_rows_fp8  expand with FP8 (E4M3) quantisation per column group
  *
  * The problem statement these calls follow:
  *   - "CuTeDSL at Perplexity" (Perplexity blog), section "Mixture of Experts
@@ -135,6 +136,26 @@ moe_status moe_route_padded(const float* logits, const float* bias, int32_t T, i
  * MOE_ERR_UNSUPPORTED (T*H/8 >= 2^31), MOE_ERR_HIP. */
 moe_status moe_expand_rows(const uint16_t* x, const int32_t* dest_of_src, int32_t T, int32_t H,
                            int32_t k, uint16_t* x_expanded, void* stream);
+
+/* FP8 quantising expand.  expandInputRows (FlashInfer PR analysis, section 1)
+ * with a quantisation between its load and its store; "CuTeDSL at
+ * Perplexity", Blackwell support: FP8 block-wise scaling with absolute maxima
+ * over small groups of elements.  For each token t and each group g of
+ * `group` consecutive columns:
+ *   amax  = max |x[t, c]| over the group
+ *   scale = fp32(amax / 448)
+ *   inv   = fp32(448 / amax)  (0 when amax = 0)
+ *   code  = E4M3(clamp(fp32(x[t, c] * inv), -448, 448)), nearest-even
+ * (OCP FP8 E4M3: bias 7, largest finite 448), and every expanded row
+ * dest_of_src[t*k + j] receives the token's codes and scales:
+ *   x_expanded uint8 [rows, H] codes, scales fp32 [rows, H/group],
+ * rows = T*k (or the padded total of moe_route_padded).  Dequantise with
+ * code * scale.  group: a power of two in [8, 512] dividing H.
+ * Alignment: x 16 bytes, x_expanded 8 bytes, scales 4 bytes; H % 8 == 0.
+ * T = 0 is a no-op.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN,
+ * MOE_ERR_UNSUPPORTED (group, sizes), MOE_ERR_HIP. */
+moe_status moe_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, int32_t T, int32_t H, int32_t k,
+                               int32_t group, uint8_t* x_expanded, float* scales, void* stream);
 
 /* ------------------------------------------------ route + expand (dispatch) */
 

@@ -10,6 +10,7 @@ Four calls, each a thin wrapper over the C ABI of the HIP library
     combine(y, topk_weights, dest_of_src)  weighted sum back to token order
     route_expand(logits, k, x, bias=None)  route + expand, one launch for T <= 64
     route_padded(logits, k, pad_to)    route with expert segments padded to pad_to rows
+    expand_rows_fp8(x, dest, k, group) expand with FP8 E4M3 quantisation per column group
 
 Tensors are torch CUDA (HIP) tensors; bf16 tensors use torch.bfloat16.  Work
 is enqueued on torch's current stream and nothing synchronises.  Every call
@@ -22,6 +23,7 @@ from ._binding import (E_MAX, EXPORTED, K_MAX, LIB_PATH, MoEGlueArgumentError, M
                        load)
 
 __all__ = ["route", "route_workspace_bytes", "alloc_route_outputs", "route_padded", "padded_rows", "expand_rows",
+           "expand_rows_fp8",
            "route_expand", "swiglu", "combine",
            "copy_probe", "MoEGlueError", "MoEGlueArgumentError", "E_MAX", "K_MAX"]
 
@@ -138,6 +140,24 @@ def expand_rows(x, dest_of_src, k: int, out=None):
     st = load().moe_expand_rows(_ptr(x), _ptr(dest_of_src), T, H, k, _ptr(out), _stream(x.device))
     check(st, "moe_expand_rows")
     return out
+
+
+def expand_rows_fp8(x, dest_of_src, k: int, group: int, rows: int | None = None, out=None, scales=None):
+    """FP8 (E4M3) quantising expand; returns (codes uint8 [rows, H], scales fp32
+    [rows, H/group]).  See moe_expand_rows_fp8 in include/moe_glue.h."""
+    torch = _torch()
+    _need_gpu("x", x, torch.bfloat16, 2)
+    _need_gpu("dest_of_src", dest_of_src, torch.int32)
+    T, H = x.shape
+    n = T * k if rows is None else rows
+    if out is None:
+        out = torch.empty((n, H), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((n, max(1, H // group)), dtype=torch.float32, device=x.device)
+    st = load().moe_expand_rows_fp8(_ptr(x), _ptr(dest_of_src), T, H, k, group, _ptr(out), _ptr(scales),
+                                    _stream(x.device))
+    check(st, "moe_expand_rows_fp8")
+    return out, scales
 
 
 def route_expand(logits, k: int, x, bias=None, out: dict | None = None) -> dict:

@@ -19,7 +19,8 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libmoe_glue.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "expand.hip", "swiglu.hip", "combine.hip", "probe.hip"]
+SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "expand.hip", "quant.hip", "swiglu.hip", "combine.hip",
+           "probe.hip"]
 HEADERS = ["device_common.h", "kernels.h", "route_common.h"]
 ARCH = "gfx950"
 

@@ -217,6 +217,25 @@ moe_status moe_route_expand(const float* logits, const float* bias, int32_t T, i
                     "moe_route_expand launch (expand)");
 }
 
+moe_status moe_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, int32_t T, int32_t H, int32_t k,
+                               int32_t group, uint8_t* x_expanded, float* scales, void* stream) {
+    const char* fn = "moe_expand_rows_fp8";
+    moe_status s = check_rows(fn, T, H, "H");
+    if (s != MOE_OK) return s;
+    if (k < 1 || k > MOE_K_MAX) return fail(MOE_ERR_SHAPE, "%s: k=%d must be in [1, %d]", fn, k, MOE_K_MAX);
+    if ((int64_t)T * k >= INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "%s: T*k too large", fn);
+    if (group < 8 || group > 512 || (group & (group - 1)) != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: group=%d must be a power of two in [8, 512]", fn, group);
+    if (H % group != 0) return fail(MOE_ERR_SHAPE, "%s: H=%d is not a multiple of group=%d", fn, H, group);
+    if (T == 0) return ok();
+    if (!x || !dest_of_src || !x_expanded || !scales) return fail(MOE_ERR_NULL, "%s: NULL tensor pointer", fn);
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(x_expanded) & 7u) != 0 || !aligned4(scales))
+        return fail(MOE_ERR_ALIGN, "%s: x must be 16-byte, codes 8-byte and scales 4-byte aligned", fn);
+    return from_hip(moe::launch_expand_rows_fp8(x, dest_of_src, T, H, k, group, x_expanded, scales,
+                                                static_cast<hipStream_t>(stream)),
+                    "moe_expand_rows_fp8 launch");
+}
+
 moe_status moe_swiglu(const uint16_t* h, int32_t R, int32_t I, uint16_t* act, void* stream) {
     moe_status s = check_rows("moe_swiglu", R, I, "I");
     if (s != MOE_OK) return s;

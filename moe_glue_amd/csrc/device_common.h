@@ -74,4 +74,47 @@ __host__ __device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv& 
 
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// ------------------------------------------------------ lane-group reductions
+// Reductions over each aligned group of G lanes (G a power of two <= 64),
+// result in every lane of the group, without the LDS crossbar: DPP quad
+// permutations for lane distance 1 and 2, DPP half-row / row mirrors to join
+// quads into 8 and 16 lanes, and the gfx950 permlane16/permlane32 swaps to
+// join rows into 32 and 64 lanes.  All are VALU operations.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+enum class Op { Max, Min, FAdd };  // unsigned max / min, fp32 add (on the bits)
+
+template <Op OP>
+__device__ __forceinline__ uint32_t apply(uint32_t a, uint32_t b) {
+    if constexpr (OP == Op::Max) return a > b ? a : b;
+    if constexpr (OP == Op::Min) return a < b ? a : b;
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+}
+
+template <int G, Op OP>
+__device__ __forceinline__ uint32_t group_reduce(uint32_t v) {
+    if constexpr (G > 1) v = apply<OP>(v, dpp<kQuadXor1>(v));
+    if constexpr (G > 2) v = apply<OP>(v, dpp<kQuadXor2>(v));
+    if constexpr (G > 4) v = apply<OP>(v, dpp<kRowHalfMirror>(v));
+    if constexpr (G > 8) v = apply<OP>(v, dpp<kRowMirror>(v));
+    if constexpr (G > 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = apply<OP>(p[0], p[1]);
+    }
+    if constexpr (G > 32) {
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        v = apply<OP>(p[0], p[1]);
+    }
+    return v;
+}
+
+
 }  // namespace moe

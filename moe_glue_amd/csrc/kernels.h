@@ -62,6 +62,8 @@ hipError_t launch_route_expand_small(const RouteArgs& a, const void* x, int H, v
 // ---------------------------------------------------- streaming row kernels
 hipError_t launch_expand_rows(const void* x, const int32_t* dest_of_src, int T, int H, int k, void* x_expanded,
                               hipStream_t stream);
+hipError_t launch_expand_rows_fp8(const void* x, const int32_t* dest_of_src, int T, int H, int k, int group,
+                                  void* q_out, float* scales, hipStream_t stream);
 hipError_t launch_swiglu(const void* h, int R, int I, void* act, hipStream_t stream);
 hipError_t launch_combine(const void* y, const float* topk_weights, const int32_t* dest_of_src, int T, int H,
                           int k, void* out, hipStream_t stream);

@@ -189,3 +189,20 @@ def test_route_padded_argument_errors(lib):
     assert lib.moe_route_padded_rows(4096, 128, 8, 128) == 4096 * 8 + 128 * 127
     assert lib.moe_route_padded_rows(10, 4, 2, 1) == 20
     assert lib.moe_route_padded_rows(10, 4, 2, 0) == 0
+
+
+def test_expand_fp8_argument_errors(lib):
+    def call(x=FAKE, d=FAKE, T=4, H=256, k=2, group=128, q=FAKE, sc=FAKE):
+        return status(lib, lib.moe_expand_rows_fp8(x, d, T, H, k, group, q, sc, None))
+
+    assert call(group=12) == "MOE_ERR_UNSUPPORTED"
+    assert call(group=4) == "MOE_ERR_UNSUPPORTED"
+    assert call(group=1024) == "MOE_ERR_UNSUPPORTED"
+    assert call(H=192, group=128) == "MOE_ERR_SHAPE"
+    assert call(H=100) == "MOE_ERR_ALIGN"
+    assert call(sc=None) == "MOE_ERR_NULL"
+    assert call(q=None) == "MOE_ERR_NULL"
+    assert call(q=FAKE + 4) == "MOE_ERR_ALIGN"
+    assert call(x=FAKE + 8) == "MOE_ERR_ALIGN"
+    assert call(sc=FAKE + 2) == "MOE_ERR_ALIGN"
+    assert call(T=0, x=None, d=None, q=None, sc=None) == "MOE_OK"

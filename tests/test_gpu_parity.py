@@ -315,3 +315,46 @@ def test_expand_combine_on_padded_layout(dev, oracle_lib, T, E, k, M, H):
     torch.cuda.synchronize()
     compare.assert_bf16_close(G.to_host(out), oracle_lib.combine(y, ref["topk_weights"], ref["dest_of_src"]),
                               "combine on padded y")
+
+
+# ------------------------------------------------------------------ FP8 quantising expand
+@pytest.mark.parametrize("T,H,E,k,group", [(1, 8, 4, 1, 8), (17, 256, 8, 2, 32), (300, 2048, 128, 8, 128),
+                                           (77, 520, 17, 5, 8), (65, 4096, 64, 16, 512), (33, 7168, 256, 8, 128),
+                                           (129, 1024, 32, 4, 64), (40, 96, 6, 3, 16)])
+def test_expand_fp8_matches_oracle(dev, oracle_lib, T, H, E, k, group):
+    import torch
+    import moe_glue_amd as mg
+
+    _log(f"[expand_fp8] T={T} H={H} E={E} k={k} group={group}")
+    cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
+    inp = inputs.make_inputs(cfg, 12, parts=("x", "logits"))
+    x = inp["x"].copy()
+    x[0, :group] = 0                      # an all-zero group
+    x[-1, -group:] = np.uint16(0x3F80)    # a constant group: every code is +448
+    r = oracle_lib.route(inp["logits"], k)
+    q, sc = mg.expand_rows_fp8(G.to_dev(x, dev), G.to_dev(r["dest_of_src"], dev), k, group)
+    torch.cuda.synchronize()
+    qr, scr = oracle_lib.expand_rows_fp8(x, r["dest_of_src"], k, group)
+    compare.assert_equal(G.to_host(sc), scr, "fp8 scales")
+    compare.assert_equal(G.to_host(q), qr, "fp8 codes")
+
+
+def test_expand_fp8_qwen_workload_and_padded_layout(dev, oracle_lib):
+    import torch
+    import moe_glue_amd as mg
+
+    cfg = inputs.CONFIGS["qwen3_30b_a3b"]
+    _log(f"[expand_fp8] {inputs.describe(cfg)} group=128, padded to 128 rows")
+    inp = inputs.make_inputs(cfg, 0, parts=("x", "logits"))
+    ref = oracle_lib.route_padded(inp["logits"], cfg.k, 128)
+    P = int(ref["expert_offsets"][cfg.E])
+    r = mg.route_padded(G.to_dev(inp["logits"], dev), cfg.k, 128)
+    q = torch.full((mg.padded_rows(cfg.T, cfg.E, cfg.k, 128), cfg.H), 0xAB, dtype=torch.uint8, device=dev)
+    q, sc = mg.expand_rows_fp8(G.to_dev(inp["x"], dev), r["dest_of_src"], cfg.k, 128, rows=q.shape[0], out=q)
+    torch.cuda.synchronize()
+    qr, scr = oracle_lib.expand_rows_fp8(inp["x"], ref["dest_of_src"], cfg.k, 128, rows=P)
+    valid = ref["src_of_dest"] >= 0
+    qh, sch = G.to_host(q)[:P], G.to_host(sc)[:P]
+    compare.assert_equal(qh[valid], qr[valid], "fp8 codes (valid rows)")
+    compare.assert_equal(sch[valid], scr[valid], "fp8 scales (valid rows)")
+    assert np.all(qh[~valid] == 0xAB), "fp8 expand wrote into padding rows"
