@@ -1,8 +1,9 @@
 """Benchmark of the MoE glue path on one MI355X.
 
-One step = the whole path on one batch: moe_route -> moe_expand_rows ->
-moe_swiglu -> moe_combine (the GEMM outputs are seeded stand-ins already in
-HBM).  The default workload is the Qwen3-30B-A3B-shaped prefill batch
+One step = the whole path on one batch: moe_route_expand (route, then the
+expansion of the token rows) -> moe_swiglu -> moe_combine (the GEMM outputs
+are seeded stand-ins already in HBM).  With --pad or --fp8-group the route and
+the (padded / quantising) expand are separate calls.  The default workload is the Qwen3-30B-A3B-shaped prefill batch
 (T=4096, H=2048, E=128, k=8, I=768).
 
 Inputs are resident in HBM before the timed region.  Steps rotate over
@@ -35,8 +36,7 @@ CSRC = os.path.join(ROOT, "moe_glue_amd", "csrc")
 # only while these are unchanged).
 KERNEL_SOURCES = {"route": ("route.hip", "route_common.h"), "expand": ("expand.hip",), "expand_fp8": ("quant.hip",),
                   "swiglu": ("swiglu.hip",), "combine": ("combine.hip",),
-                  "dispatch": ("dispatch.hip", "route_common.h")}
-SMALL_DISPATCH_MAX_T = 64  # the library's one-launch route + expand limit
+                  "route_expand": ("route.hip", "route_common.h", "dispatch.hip", "expand.hip")}
 
 
 def algorithmic_bytes(cfg, fp8_group: int = 0) -> dict:
@@ -47,7 +47,7 @@ def algorithmic_bytes(cfg, fp8_group: int = 0) -> dict:
     swiglu = R * 2 * I * 2 + R * I * 2
     combine = R * H * 2 + R * 4 + R * 4 + T * H * 2
     expand_fp8 = T * H * 2 + R * 4 + R * H + (R * (H // fp8_group) * 4 if fp8_group else 0)
-    return {"route": route, "expand": expand, "swiglu": swiglu, "combine": combine, "dispatch": route + expand,
+    return {"route": route, "expand": expand, "swiglu": swiglu, "combine": combine, "route_expand": route + expand,
             "expand_fp8": expand_fp8}
 
 
@@ -167,7 +167,7 @@ class Sets:
             d["args"] = {
                 "route": ((p("logits"), p("bias"), T, E, k) + route_args if pad_to == 1
                           else (p("logits"), p("bias"), T, E, k, pad_to) + route_args),
-                "dispatch": (p("logits"), p("bias"), T, E, k, p("x"), H, p("topk_ids"), p("topk_weights"),
+                "route_expand": (p("logits"), p("bias"), T, E, k, p("x"), H, p("topk_ids"), p("topk_weights"),
                              p("expert_offsets"), p("expert_counts"), p("dest_of_src"), p("src_of_dest"), p("x_exp"),
                              p("workspace"), d["workspace"].numel(), stream),
                 "expand": (p("x"), p("dest_of_src"), T, H, k, p("x_exp"), stream),
@@ -179,14 +179,15 @@ class Sets:
             self.sets.append(d)
         self.fns = {"route": self.lib.moe_route if pad_to == 1 else self.lib.moe_route_padded,
                     "expand": self.lib.moe_expand_rows, "expand_fp8": self.lib.moe_expand_rows_fp8,
-                    "dispatch": self.lib.moe_route_expand, "swiglu": self.lib.moe_swiglu,
+                    "route_expand": self.lib.moe_route_expand, "swiglu": self.lib.moe_swiglu,
                     "combine": self.lib.moe_combine}
-        # Small (decode) batches take the one-launch dispatch (route + expand);
-        # larger ones call route and expand separately.
+        # Route and expand run as one moe_route_expand call (one launch for
+        # decode batches, destination-order expand above); the padded and the
+        # quantising expand have no fused form.
         if fp8_group:
             self.calls = ["route", "expand_fp8", "swiglu", "combine"]
-        elif cfg.T <= SMALL_DISPATCH_MAX_T and pad_to == 1:
-            self.calls = ["dispatch", "swiglu", "combine"]
+        elif pad_to == 1:
+            self.calls = ["route_expand", "swiglu", "combine"]
         else:
             self.calls = ["route", "expand", "swiglu", "combine"]
 
@@ -320,7 +321,10 @@ def main(argv=None):
                           "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
                           "frac_of_achievable": round(gbps / achievable, 4),
                           "traffic": measured_traffic(n, cfg.name)}
-    dominant = max((n for n in names if n != "route"), key=lambda n: kernels[n]["us"]) if kernels else None
+    # the roofline kernel: the longest call that is a single kernel (route and
+    # route_expand launch several)
+    single = [n for n in names if n not in ("route", "route_expand")]
+    dominant = max(single, key=lambda n: kernels[n]["us"]) if kernels else None
     roofline = None
     if kernels:
         d = kernels[dominant]

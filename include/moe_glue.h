@@ -6,7 +6,8 @@
  *   moe_expand_rows  copy each token row to its k expert-contiguous rows
  *   moe_swiglu       gated SiLU on the first grouped GEMM's output
  *   moe_combine      routing-weighted sum of each token's k expert outputs
- *   moe_route_expand route + expand in one launch for small (decode) batches
+ *   moe_route_expand route + expand (one launch for small decode batches,
+ *                    destination-order copy above)
  *   moe_route_padded route with expert segments padded to a row multiple
  *   moe_expand_rows_fp8  expand with FP8 (E4M3) quantisation per column group
  *
@@ -65,10 +66,13 @@ typedef enum moe_status {
 
 /* ------------------------------------------------------------------ route */
 
-/* Bytes of device workspace moe_route needs for (T, E, k); 0 is never
- * returned for valid arguments, and a negative/invalid argument gives 0.
- * The workspace needs no initialisation and may be reused by later calls on
- * the same stream. */
+/* Bytes of device workspace that moe_route, moe_route_padded and
+ * moe_route_expand need for (T, E, k); 0 is never returned for valid
+ * arguments, and a negative/invalid argument gives 0.  (moe_route and
+ * moe_route_padded use only the front part: the per-workgroup expert
+ * histograms; moe_route_expand also keeps T*k row-list entries of 8 bytes
+ * there.)  The workspace needs no initialisation and may be reused by later
+ * calls on the same stream. */
 size_t moe_route_workspace_bytes(int32_t T, int32_t E, int32_t k);
 
 /* Softmax top-k routing plus dispatch bookkeeping ("CuTeDSL at Perplexity",
@@ -159,15 +163,18 @@ moe_status moe_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, in
 
 /* ------------------------------------------------ route + expand (dispatch) */
 
-/* The whole dispatch of a small batch in one launch: exactly the results of
- * moe_route followed by moe_expand_rows on the same arguments (all outputs of
- * both calls are written).  "CuTeDSL at Perplexity", sections "Grid
- * synchronization" and MoE dispatch/combine > Local, describes decode
- * dispatch as routing and copying in a single launch.  For T <= 64 this call
- * uses one launch in which every workgroup recomputes the routing in LDS and
- * copies its share of the rows (the workspace is not touched and may be NULL);
- * for larger T it runs moe_route and then moe_expand_rows, and the workspace
- * must be as moe_route requires (moe_route_workspace_bytes).
+/* The whole dispatch: exactly the results of moe_route followed by
+ * moe_expand_rows on the same arguments (all outputs of both calls are
+ * written).  "CuTeDSL at Perplexity", sections "Grid synchronization" and
+ * MoE dispatch/combine > Local, describes dispatch as routing then copying
+ * the tokens into the experts' buffer.  For T <= 64 this call uses one launch
+ * in which every workgroup recomputes the routing in LDS and copies its share
+ * of the rows (the workspace is not touched and may be NULL).  For larger T
+ * the route runs as in moe_route; when the expanded rows are large (about
+ * 100 MB and up) it also lists them per token group in the workspace and the
+ * copy runs in destination-row order from that list, else in token order.
+ * The workspace must hold moe_route_workspace_bytes(T, E, k) bytes (16-byte
+ * aligned) whenever T > 64.
  * Layouts, limits, alignment and errors: the union of moe_route's and
  * moe_expand_rows'. */
 moe_status moe_route_expand(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,

@@ -15,6 +15,8 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace moe {
 namespace {
 
@@ -68,7 +70,75 @@ hipError_t launch_u(const void* x, const int32_t* dest_of_src, int T, int H, int
     return hipGetLastError();
 }
 
+// ----------------------------------------------------------- grouped form
+// Destination-row order, from the route's row list.  Writing in token order
+// sends every token's k rows to k experts' segments at once, i.e. E open write
+// streams across the whole output; in destination order the writes of the
+// whole chip stay inside one moving window, which HBM absorbs faster.  The
+// price is that each source row is read k times -- so the tokens are split
+// into groups (RowGroups) and the rows of one group are copied by one XCD:
+// workgroup b runs on XCD b % 8 and copies rows of group (m / chunks) * 8 +
+// b % 8, m = b / 8, in destination order.  While an XCD works on a group, the
+// group's source rows stay in its L2 and HBM sees each read about once; the
+// eight XCDs work on neighbouring groups, whose rows in each expert segment
+// are neighbours too.  Each workgroup copies kGroupedItems / (H/8) rows (at
+// least one).
+constexpr int kGroupedThreads = 256;
+constexpr int kGroupedItems = 512;  // 16-byte vectors per workgroup: small windows
+
+template <int U>
+__global__ __launch_bounds__(kGroupedThreads) void expand_grouped_kernel(const u32x4* __restrict__ x,
+                                                                         const int2* __restrict__ row_list,
+                                                                         RowGroups groups, int k, uint32_t H16,
+                                                                         FastDiv div_h16, uint32_t rows_per_wg,
+                                                                         uint32_t chunks,
+                                                                         u32x4* __restrict__ x_exp) {
+    const uint32_t m = blockIdx.x / kXcds;
+    const int g = (int)(m / chunks) * kXcds + (int)(blockIdx.x % kXcds);
+    if (g >= groups.n) return;
+    const uint32_t first = (m % chunks) * rows_per_wg;
+    const int32_t t0 = group_tok(groups, g);
+    const uint32_t n = (uint32_t)(group_tok(groups, g + 1) - t0) * (uint32_t)k;
+    if (first >= n) return;
+    const int2* lst = row_list + (size_t)t0 * k + first;
+    const uint32_t items = min(rows_per_wg, n - first) * H16;
+    for (uint32_t i0 = threadIdx.x; i0 < items; i0 += kGroupedThreads * U) {
+        int2 ent[U];
+        uint32_t col[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t i = min(i0 + u * kGroupedThreads, items - 1);  // clamped: loads stay in bounds
+            const uint32_t r = fastdiv(i, div_h16);
+            col[u] = i - r * H16;
+            ent[u] = lst[r];
+        }
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = x[(size_t)ent[u].y * H16 + col[u]];  // cached: reused from L2
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (i0 + u * kGroupedThreads < items) store_stream(x_exp + (size_t)ent[u].x * H16 + col[u], v[u]);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_expand_grouped(const void* x, const int32_t* row_list, const RowGroups& groups, int H, int k,
+                                 void* x_expanded, hipStream_t stream) {
+    const uint32_t H16 = (uint32_t)H / 8;
+    const uint32_t rows_per_wg = H16 >= (uint32_t)kGroupedItems ? 1u : (uint32_t)kGroupedItems / H16;
+    uint32_t chunks = 0;  // workgroups per group
+    for (int g = 0; g < groups.n; ++g) {
+        const uint32_t n = (uint32_t)(group_tok(groups, g + 1) - group_tok(groups, g)) * (uint32_t)k;
+        chunks = std::max(chunks, (n + rows_per_wg - 1) / rows_per_wg);
+    }
+    if (chunks == 0) return hipSuccess;
+    const uint32_t rounds = ((uint32_t)groups.n + kXcds - 1) / kXcds;  // groups per XCD
+    expand_grouped_kernel<2><<<rounds * kXcds * chunks, kGroupedThreads, 0, stream>>>(
+        static_cast<const u32x4*>(x), reinterpret_cast<const int2*>(row_list), groups, k, H16, make_fastdiv(H16),
+        rows_per_wg, chunks, static_cast<u32x4*>(x_expanded));
+    return hipGetLastError();
+}
 
 hipError_t launch_expand_rows(const void* x, const int32_t* dest_of_src, int T, int H, int k, void* x_expanded,
                               hipStream_t stream) {

@@ -4,7 +4,7 @@
 // status.
 #pragma once
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -22,6 +22,41 @@ constexpr size_t kRouteTwoPassMaxBytes = 128 * 1024;
 // (TwoPass) or in two (ThreePass); Auto picks by T and the matrix size.
 enum class RouteVariant { Auto = 0, SingleWorkgroup = 1, TwoPass = 2, ThreePass = 3 };
 
+// Token groups of the grouped expand.  Workgroups are dealt to the 8 XCDs
+// round-robin, so workgroup b runs on XCD b % 8; XCD x copies the rows of
+// groups x, x + 8, x + 16, ... one group after the other, and a group's
+// source rows (about kGroupSourceBytes at most) stay in that XCD's L2.
+// Group boundaries fall on whole scan+place workgroups ("units" of
+// kPlaceRows top-k rows): group i starts at top-k row
+// row(i) = min(nb, kPlaceRows * floor(i * units / n)).
+constexpr int kXcds = 8;
+constexpr int kPlaceRows = 4;
+constexpr int64_t kGroupSourceBytes = 2 << 20;
+constexpr int kMaxGroupsPerXcd = 16;
+struct RowGroups {
+    int32_t n;      // number of groups: kXcds * groups per XCD
+    int32_t units;  // scan+place units
+    int32_t nb;     // top-k rows
+    int32_t tb;     // tokens per top-k row
+    int32_t T;
+};
+// (32-bit unsigned arithmetic: units < 2^25 and n <= 128 keep every product
+// below 2^32.)
+__host__ __device__ inline int32_t group_row(const RowGroups& g, int i) {
+    const uint32_t r = (uint32_t)kPlaceRows * ((uint32_t)i * (uint32_t)g.units / (uint32_t)g.n);
+    return r < (uint32_t)g.nb ? (int32_t)r : g.nb;
+}
+__host__ __device__ inline int32_t group_tok(const RowGroups& g, int i) {
+    const int64_t t = (int64_t)group_row(g, i) * g.tb;
+    return t < g.T ? (int32_t)t : g.T;
+}
+// The group holding unit u: the last i with floor(i * units / n) <= u.
+__host__ __device__ inline int32_t group_of_unit(const RowGroups& g, int u) {
+    const uint32_t units = (uint32_t)g.units;
+    const int32_t i = (int32_t)((((uint32_t)u + 1) * (uint32_t)g.n + units - 1) / units) - 1;
+    return i < g.n - 1 ? i : g.n - 1;
+}
+
 struct RouteArgs {
     const float* logits;
     const float* bias;
@@ -34,6 +69,11 @@ struct RouteArgs {
     int32_t* src_of_dest;
     void* workspace;
     int pad_to;  // expert segments padded to a multiple of pad_to rows (1: unpadded)
+    // When set (multi-workgroup variants only): the expanded rows listed per
+    // token group of `groups` for the grouped expand; entry = (dest row,
+    // token), group i at [tok(i)*k, tok(i+1)*k), each group in dest-row order.
+    int32_t* row_list;
+    RowGroups groups;
 };
 
 // Keys per lane (8 above 32 experts, else 4) and lanes that cooperate on one token.
@@ -44,12 +84,18 @@ int route_tokens_per_block(int E);
 // Experts padded to a multiple of 4 (one int4 per 4 experts in the workspace).
 inline int route_padded_experts(int E) { return (E + 3) & ~3; }
 // Workspace of the multi-workgroup route: one histogram row per top-k
-// workgroup plus one row of totals.
-inline size_t route_workspace_bytes(int T, int E) {
+// workgroup plus one row of totals, then (16-byte aligned) the row list of
+// the grouped expand, T*k entries of two int32.
+inline size_t route_histogram_bytes(int T, int E) {
     const int tb = route_tokens_per_block(E);
     const size_t nb = (size_t)(T > 0 ? (T + tb - 1) / tb : 0);
-    return (nb + 1) * (size_t)route_padded_experts(E) * sizeof(int32_t);
+    return ((nb + 1) * (size_t)route_padded_experts(E) * sizeof(int32_t) + 15) & ~(size_t)15;
 }
+inline size_t route_workspace_bytes(int T, int E, int k) {
+    return route_histogram_bytes(T, E) + (size_t)T * k * 2 * sizeof(int32_t);
+}
+// Groups for a batch of T tokens whose rows are H bf16 wide.
+RowGroups route_row_groups(int T, int E, int H);
 RouteVariant route_pick_variant(int T, int E, RouteVariant requested);
 
 hipError_t launch_route(const RouteArgs& a, RouteVariant variant, hipStream_t stream);
@@ -62,6 +108,9 @@ hipError_t launch_route_expand_small(const RouteArgs& a, const void* x, int H, v
 // ---------------------------------------------------- streaming row kernels
 hipError_t launch_expand_rows(const void* x, const int32_t* dest_of_src, int T, int H, int k, void* x_expanded,
                               hipStream_t stream);
+// Expand in destination-row order from the route's row list (RouteArgs::row_list).
+hipError_t launch_expand_grouped(const void* x, const int32_t* row_list, const RowGroups& groups, int H, int k,
+                                 void* x_expanded, hipStream_t stream);
 hipError_t launch_expand_rows_fp8(const void* x, const int32_t* dest_of_src, int T, int H, int k, int group,
                                   void* q_out, float* scales, hipStream_t stream);
 hipError_t launch_swiglu(const void* h, int R, int I, void* act, hipStream_t stream);

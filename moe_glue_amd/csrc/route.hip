@@ -35,6 +35,8 @@
 // exponentials of the slots it writes, and one more reduction sums them.
 #include "route_common.h"
 
+#include <algorithm>
+
 namespace moe {
 namespace {
 
@@ -151,23 +153,31 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int32_t* __res
 }
 
 // 3. Per workgroup of step 1: offsets from the totals (LDS scan), then
-// dest = offset[e] + prefix[b][e] + rank for each of its slots.
+// dest = offset[e] + prefix[b][e] + rank for each of its slots.  With LIST
+// each slot also gets its entry in the row list of its token group g:
+// position gcum_g[e] + (tokens of group g before it that picked e), where
+// gcum_g is the exclusive scan over experts of the group's own counts.
 constexpr int kPlaceThreads = 256;
 constexpr int kPlaceSlots = kChunk * kKMax / kPlaceThreads;  // slots per lane, at most
 
+template <bool LIST>
 __global__ __launch_bounds__(kPlaceThreads) void route_place_kernel(
     const int32_t* __restrict__ prefix, const int32_t* __restrict__ totals, int tok_per_block, int T, int E, int k,
-    int pad,
-    const int32_t* __restrict__ topk_ids, int32_t* __restrict__ dest_of_src, int32_t* __restrict__ src_of_dest,
-    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ expert_counts) {
+    int pad, const int32_t* __restrict__ topk_ids, int32_t* __restrict__ dest_of_src,
+    int32_t* __restrict__ src_of_dest, int32_t* __restrict__ expert_offsets, int32_t* __restrict__ expert_counts,
+    RowGroups groups, int2* __restrict__ row_list) {
     __shared__ int32_t s_tot[kEMax];
     __shared__ int32_t s_pre[kEMax];
     __shared__ int32_t s_off[kEMax + 1];
+    __shared__ int32_t s_gpre[LIST ? kEMax : 1];
+    __shared__ int32_t s_glen[LIST ? kEMax : 1];
+    __shared__ int32_t s_gcum[LIST ? kEMax + 1 : 1];
 
     const int Epad = (E + 3) & ~3;
     const int b = blockIdx.x;
     const int tok0 = b * tok_per_block;
     const int nslot = min(tok_per_block, T - tok0) * k;
+    const int gj = LIST ? group_of_unit(groups, b / kPlaceRows) : 0;  // the token group holding this row
     // every load first: the slots (expert, rank), the totals, this row's prefix
     int my_e[kPlaceSlots], my_r[kPlaceSlots];
 #pragma unroll
@@ -181,9 +191,17 @@ __global__ __launch_bounds__(kPlaceThreads) void route_place_kernel(
     for (int e = threadIdx.x; e < E; e += kPlaceThreads) {
         s_tot[e] = totals[e];
         s_pre[e] = prefix[(size_t)b * Epad + e];
+        if constexpr (LIST) {
+            const int r0 = group_row(groups, gj), r1 = group_row(groups, gj + 1);
+            const int gpre = prefix[(size_t)r0 * Epad + e];
+            const int gend = r1 < groups.nb ? prefix[(size_t)r1 * Epad + e] : totals[e];
+            s_gpre[e] = gpre;
+            s_glen[e] = gend - gpre;
+        }
     }
     __syncthreads();
-    wave0_exclusive_scan(s_tot, s_off, E, pad);
+    wave_exclusive_scan(s_tot, s_off, E, pad, 0);
+    if constexpr (LIST) wave_exclusive_scan(s_glen, s_gcum, E, 1, 1);
     __syncthreads();
     if (b == 0) {
         for (int e = threadIdx.x; e <= E; e += kPlaceThreads) expert_offsets[e] = s_off[e];
@@ -196,43 +214,71 @@ __global__ __launch_bounds__(kPlaceThreads) void route_place_kernel(
         const int s = threadIdx.x + u * kPlaceThreads;
         if (s < nslot) {
             const size_t gs = (size_t)tok0 * k + s;
-            const int d = s_off[my_e[u]] + s_pre[my_e[u]] + my_r[u];
+            const int e = my_e[u];
+            const int before = s_pre[e] + my_r[u];  // earlier tokens that picked e
+            const int d = s_off[e] + before;
             dest_of_src[gs] = d;
             src_of_dest[d] = (int32_t)gs;
+            if constexpr (LIST)
+                row_list[(size_t)group_tok(groups, gj) * k + s_gcum[e] + (before - s_gpre[e])] =
+                    make_int2(d, tok0 + s / k);
         }
     }
 }
 
 // 2+3 fused, for a small histogram matrix: workgroup g owns kFusedRows
-// consecutive top-k rows.  It sums every histogram row (one int4 of experts
-// per lane, RP rows in parallel) into the totals and the prefix before its
-// first row, extends that prefix over its own rows, scans the totals into
-// offsets, and writes its slots.  Reading the whole matrix per workgroup costs
-// L2 bandwidth instead of a third launch; the host picks this form only while
-// the matrix is small.
+// consecutive top-k rows.  It sums every histogram row into column sums --
+// the totals and the prefix before its first row (and with LIST the prefixes
+// at its token group's first and last row) -- keeps its own rows, scans the
+// totals into offsets, and writes its slots.  Reading the whole matrix per
+// workgroup costs L2 bandwidth instead of a third launch; the host picks this
+// form only while the matrix is small.  With LIST each slot also gets its
+// row-list entry (as in route_place_kernel).
+//
+// Lane layout: lane = rg * Qp + q, q = int4 column (Qp = Q rounded up to a
+// power of two), rg = row group; each lane sums rows rg, rg + RP, ...  The
+// row groups are reduced inside each wave by lane exchanges (lanes with the
+// same q sit Qp apart), leaving at most 16 partials per column in LDS; then
+// F lanes share each (sum, expert) item, read its partials as plain ints and
+// join by lane exchanges.
 constexpr int kFusedThreads = 1024;
-constexpr int kFusedRows = 4;
+constexpr int kFusedRows = kPlaceRows;
 constexpr int kFusedSlots = kFusedRows * kChunk * kKMax / kFusedThreads;
+constexpr int kFusedWaves = kFusedThreads / kWave;
 
+template <bool LIST>
 __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
     const int32_t* __restrict__ counts, int nb, int tok_per_row, int T, int E, int k, int pad,
     const int32_t* __restrict__ topk_ids, int32_t* __restrict__ dest_of_src, int32_t* __restrict__ src_of_dest,
-    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ expert_counts) {
-    __shared__ i32x4 part_tot[kFusedThreads];
-    __shared__ i32x4 part_pre[kFusedThreads];
-    __shared__ int32_t s_tot[kEMax];
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ expert_counts, RowGroups groups,
+    int2* __restrict__ row_list) {
+    // column sums over rows below: nb (all), row0, and with LIST the group's first and last row
+    constexpr int NACC = LIST ? 4 : 2;
+    // partials (partial group pg, column q) at pg * Qp + q: at most kFusedThreads entries
+    __shared__ i32x4 part[NACC][kFusedThreads];
+    __shared__ i32x4 s_rows[kFusedRows][kEMax / 4];
+    __shared__ int32_t s_acc[NACC][kEMax];
     __shared__ int32_t s_off[kEMax + 1];
-    __shared__ int32_t s_pre[kFusedRows][kEMax];
+    __shared__ int32_t s_gcum[LIST ? kEMax + 1 : 1];
 
     const int Epad = (E + 3) & ~3;
-    const int Q = Epad / 4;           // int4 per histogram row (<= 128)
-    const int RP = kFusedThreads / Q;  // rows summed in parallel (>= 8)
-    const int q = threadIdx.x % Q;
-    const int rg = threadIdx.x / Q;
+    const int Q = Epad / 4;  // int4 per histogram row (<= 128)
+    int Qp = 1;
+    while (Qp < Q) Qp <<= 1;
+    const int RP = kFusedThreads / Qp;  // row groups (>= 8)
+    const int q = threadIdx.x % Qp;
+    const int rg = threadIdx.x / Qp;
     const int row0 = blockIdx.x * kFusedRows;
-    const int nrows = min(kFusedRows, nb - row0);
     const int tok0 = row0 * tok_per_row;
     const int nslot = min(kFusedRows * tok_per_row, T - tok0) * k;
+    const int gj = LIST ? group_of_unit(groups, blockIdx.x) : 0;  // the token group of this workgroup
+    int bound[NACC];
+    bound[0] = nb;
+    bound[1] = row0;
+    if constexpr (LIST) {
+        bound[2] = group_row(groups, gj);
+        bound[3] = group_row(groups, gj + 1);
+    }
 
     // every independent load first: the slots, then the histogram columns
     int my_e[kFusedSlots], my_r[kFusedSlots];
@@ -244,52 +290,78 @@ __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
             my_r[u] = dest_of_src[(size_t)tok0 * k + s];
         }
     }
-    i32x4 tot = {0, 0, 0, 0};
-    i32x4 pre = {0, 0, 0, 0};
-    if (rg < RP) {
+    i32x4 acc[NACC];
+#pragma unroll
+    for (int a = 0; a < NACC; ++a) acc[a] = (i32x4){0, 0, 0, 0};
+    if (q < Q) {
         const i32x4* rows = reinterpret_cast<const i32x4*>(counts);
 #pragma unroll 8
         for (int row = rg; row < nb; row += RP) {
             const i32x4 c = rows[(size_t)row * Q + q];
-            tot += c;
-            if (row < row0) pre += c;
+#pragma unroll
+            for (int a = 0; a < NACC; ++a)
+                if (row < bound[a]) acc[a] += c;
+            if (row >= row0 && row < row0 + kFusedRows) s_rows[row - row0][q] = c;
         }
     }
-    part_tot[threadIdx.x] = tot;
-    part_pre[threadIdx.x] = pre;
+    // inside the wave: the 64 / Qp row groups of a wave (none to join when Qp >= 64)
+    for (int m = Qp; m < kWave; m <<= 1) {
+#pragma unroll
+        for (int a = 0; a < NACC; ++a)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[a][c] += __shfl_xor(acc[a][c], m);
+    }
+    // one partial per wave (Qp < 64) or per row group (Qp >= 64)
+    const int npg = Qp < kWave ? kFusedWaves : RP;
+    if (Qp >= kWave || (int)(threadIdx.x % kWave) < Qp) {
+        const int pg = Qp < kWave ? (int)(threadIdx.x / kWave) : rg;
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) part[a][pg * Qp + q] = acc[a];
+    }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += kFusedThreads) {
-        const int qe = e >> 2, ce = e & 3;
-        int st = 0, sp = 0;
-        for (int g = 0; g < RP; ++g) {
-            st += part_tot[g * Q + qe][ce];
-            sp += part_pre[g * Q + qe][ce];
-        }
-        s_tot[e] = st;
-        // the prefix at the start of each of this workgroup's rows
-        for (int r = 0; r < nrows; ++r) {
-            s_pre[r][e] = sp;
-            if (r + 1 < nrows) sp += counts[(size_t)(row0 + r) * Epad + e];
+    // items (a, e), e < 4 * Qp; F adjacent lanes per item, cnt partials each
+    {
+        const int EQ = 4 * Qp;
+        int F = kFusedThreads / (NACC * EQ);
+        F = F < 1 ? 1 : (F > npg ? npg : F);
+        const int cnt = npg / F;
+        const int h = threadIdx.x % F;
+        for (int item = threadIdx.x / F; item < NACC * EQ; item += kFusedThreads / F) {
+            const int a = item / EQ;
+            const int e = item % EQ;
+            const int32_t* pa = reinterpret_cast<const int32_t*>(part[a]) + (e >> 2) * 4 + (e & 3);
+            int sum = 0;
+#pragma unroll 4
+            for (int j = 0; j < cnt; ++j) sum += pa[(h * cnt + j) * Qp * 4];
+            for (int m = 1; m < F; m <<= 1) sum += __shfl_xor(sum, m);
+            if (h == 0 && e < E) s_acc[a][e] = sum;
         }
     }
     __syncthreads();
-    wave0_exclusive_scan(s_tot, s_off, E, pad);
+    wave_exclusive_scan(s_acc[0], s_off, E, pad, 0);
+    if constexpr (LIST) wave_exclusive_scan(s_acc[3], s_gcum, E, 1, 1, s_acc[2]);  // the group's own counts
     __syncthreads();
     if (blockIdx.x == 0) {
         for (int e = threadIdx.x; e <= E; e += kFusedThreads) expert_offsets[e] = s_off[e];
         if (expert_counts != nullptr)
-            for (int e = threadIdx.x; e < E; e += kFusedThreads) expert_counts[e] = s_tot[e];
+            for (int e = threadIdx.x; e < E; e += kFusedThreads) expert_counts[e] = s_acc[0][e];
     }
-    mark_padding<kFusedThreads>(s_tot, s_off, E, pad, blockIdx.x, gridDim.x, src_of_dest);
+    mark_padding<kFusedThreads>(s_acc[0], s_off, E, pad, blockIdx.x, gridDim.x, src_of_dest);
 #pragma unroll
     for (int u = 0; u < kFusedSlots; ++u) {
         const int s = threadIdx.x + u * kFusedThreads;
         if (s < nslot) {
             const size_t gs = (size_t)tok0 * k + s;
             const int r = (s / k) / tok_per_row;
-            const int d = s_off[my_e[u]] + s_pre[r][my_e[u]] + my_r[u];
+            const int e = my_e[u];
+            int before = s_acc[1][e] + my_r[u];  // earlier tokens that picked e
+            for (int r2 = 0; r2 < r; ++r2) before += s_rows[r2][e >> 2][e & 3];
+            const int d = s_off[e] + before;
             dest_of_src[gs] = d;
             src_of_dest[d] = (int32_t)gs;
+            if constexpr (LIST)
+                row_list[(size_t)group_tok(groups, gj) * k + s_gcum[e] + (before - s_acc[2][e])] =
+                    make_int2(d, tok0 + s / k);
         }
     }
 }
@@ -311,18 +383,31 @@ hipError_t launch_route_gv(const RouteArgs& a, RouteVariant v, hipStream_t strea
                                                            a.topk_weights, a.dest_of_src, counts);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    const bool list = a.row_list != nullptr;
+    int2* row_list = reinterpret_cast<int2*>(a.row_list);
     if (v == RouteVariant::TwoPass) {
-        route_scan_place_kernel<<<(nb + kFusedRows - 1) / kFusedRows, kFusedThreads, 0, stream>>>(
-            counts, nb, S::TOK, a.T, a.E, a.k, a.pad_to, a.topk_ids, a.dest_of_src, a.src_of_dest, a.expert_offsets,
-            a.expert_counts);
+        const int nwg = (nb + kFusedRows - 1) / kFusedRows;
+        if (list)
+            route_scan_place_kernel<true><<<nwg, kFusedThreads, 0, stream>>>(
+                counts, nb, S::TOK, a.T, a.E, a.k, a.pad_to, a.topk_ids, a.dest_of_src, a.src_of_dest,
+                a.expert_offsets, a.expert_counts, a.groups, row_list);
+        else
+            route_scan_place_kernel<false><<<nwg, kFusedThreads, 0, stream>>>(
+                counts, nb, S::TOK, a.T, a.E, a.k, a.pad_to, a.topk_ids, a.dest_of_src, a.src_of_dest,
+                a.expert_offsets, a.expert_counts, a.groups, row_list);
         return hipGetLastError();
     }
     route_scan_kernel<<<Epad / 4, kScanThreads, 0, stream>>>(counts, nb, Epad, totals);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    route_place_kernel<<<nb, kPlaceThreads, 0, stream>>>(counts, totals, S::TOK, a.T, a.E, a.k, a.pad_to, a.topk_ids,
-                                                         a.dest_of_src, a.src_of_dest, a.expert_offsets,
-                                                         a.expert_counts);
+    if (list)
+        route_place_kernel<true><<<nb, kPlaceThreads, 0, stream>>>(
+            counts, totals, S::TOK, a.T, a.E, a.k, a.pad_to, a.topk_ids, a.dest_of_src, a.src_of_dest,
+            a.expert_offsets, a.expert_counts, a.groups, row_list);
+    else
+        route_place_kernel<false><<<nb, kPlaceThreads, 0, stream>>>(
+            counts, totals, S::TOK, a.T, a.E, a.k, a.pad_to, a.topk_ids, a.dest_of_src, a.src_of_dest,
+            a.expert_offsets, a.expert_counts, a.groups, row_list);
     return hipGetLastError();
 }
 
@@ -341,6 +426,19 @@ int route_lanes_per_token(int E) {
 int route_tokens_per_block(int E) {
     const int G = route_lanes_per_token(E);
     return G >= 4 ? 16 : kWave / G;
+}
+
+RowGroups route_row_groups(int T, int E, int H) {
+    RowGroups g;
+    g.tb = route_tokens_per_block(E);
+    g.nb = T > 0 ? (T + g.tb - 1) / g.tb : 0;
+    g.units = std::max(1, (g.nb + kPlaceRows - 1) / kPlaceRows);
+    g.T = T;
+    // groups per XCD: enough that one group's source rows fit the L2 budget
+    const int64_t per_xcd = ((int64_t)T * H * 2 + kXcds - 1) / kXcds;
+    const int64_t sub = (per_xcd + kGroupSourceBytes - 1) / kGroupSourceBytes;
+    g.n = kXcds * (int32_t)std::max<int64_t>(1, std::min<int64_t>(sub, kMaxGroupsPerXcd));
+    return g;
 }
 
 RouteVariant route_pick_variant(int T, int E, RouteVariant requested) {

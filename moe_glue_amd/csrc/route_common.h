@@ -146,17 +146,18 @@ __device__ __forceinline__ int mask_count(const unsigned long long* masks, int E
 // multiple of pad (pad = 1: unpadded).
 __device__ __forceinline__ int padded_len(int count, int pad) { return pad == 1 ? count : (count + pad - 1) / pad * pad; }
 
-// Exclusive prefix sum of the padded lengths of in[0..n) into out[0..n],
-// out[n] = total; n <= 512.  Run by wave 0 only: each lane owns ceil(n/64)
-// consecutive entries.
-__device__ __forceinline__ void wave0_exclusive_scan(const int32_t* in, int32_t* out, int n, int pad) {
-    if (threadIdx.x >= kWave) return;
-    const int lane = threadIdx.x;
+// Exclusive prefix sum of the padded lengths of in[0..n) (minus minus[i] when
+// given) into out[0..n], out[n] = total; n <= 512.  Run by wave `w` of the
+// workgroup only: each lane owns ceil(n/64) consecutive entries.
+__device__ __forceinline__ void wave_exclusive_scan(const int32_t* in, int32_t* out, int n, int pad, int w,
+                                                    const int32_t* minus = nullptr) {
+    if ((int)(threadIdx.x / kWave) != w) return;
+    const int lane = threadIdx.x % kWave;
     const int per = (n + kWave - 1) / kWave;
     const int base = lane * per;
     int local = 0;
     for (int i = 0; i < per; ++i)
-        if (base + i < n) local += padded_len(in[base + i], pad);
+        if (base + i < n) local += padded_len(in[base + i] - (minus ? minus[base + i] : 0), pad);
     int incl = local;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -167,10 +168,14 @@ __device__ __forceinline__ void wave0_exclusive_scan(const int32_t* in, int32_t*
     for (int i = 0; i < per; ++i) {
         if (base + i < n) {
             out[base + i] = run;
-            run += padded_len(in[base + i], pad);
+            run += padded_len(in[base + i] - (minus ? minus[base + i] : 0), pad);
         }
     }
     if (lane == kWave - 1) out[n] = incl;
+}
+
+__device__ __forceinline__ void wave0_exclusive_scan(const int32_t* in, int32_t* out, int n, int pad) {
+    wave_exclusive_scan(in, out, n, pad, 0);
 }
 
 // Padding rows of the padded layout get src_of_dest = -1: rows

@@ -33,8 +33,10 @@ def route_host(r: dict) -> dict:
     return {k: to_host(v) for k, v in r.items() if k != "workspace"}
 
 
-def run_path(inp: dict, dev, parts=("route", "expand", "swiglu", "combine")) -> dict:
-    """The whole HIP path on one input dict from moe_glue_amd.inputs."""
+def run_path(inp: dict, dev, parts=("route", "expand", "swiglu", "combine"), fused: bool = False) -> dict:
+    """The whole HIP path on one input dict from moe_glue_amd.inputs.  With
+    `fused`, route and expand run as one moe_route_expand call (as the
+    benchmark does)."""
     import torch
     import moe_glue_amd as mg
 
@@ -42,6 +44,11 @@ def run_path(inp: dict, dev, parts=("route", "expand", "swiglu", "combine")) -> 
     out = {}
     logits = to_dev(inp["logits"], dev)
     bias = to_dev(inp["bias"], dev) if inp.get("bias") is not None else None
+    if fused:
+        r = mg.route_expand(logits, cfg.k, to_dev(inp["x"], dev), bias)
+        out.update(route_host(r))
+        torch.cuda.synchronize(dev)
+        return out
     r = mg.route(logits, cfg.k, bias)
     out.update(route_host(r))
     # the row kernels trust dest_of_src; make sure it is a permutation before they run

@@ -73,19 +73,25 @@ def test_route_workspace_errors(lib, monkeypatch):
     monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", "three")
     T, E, k = 4096, 128, 8
     need = lib.moe_route_workspace_bytes(T, E, k)
-    assert need == (4096 // 16 + 1) * 128 * 4  # 16-token histogram rows + one row of totals
+    hist = (4096 // 16 + 1) * 128 * 4  # 16-token histogram rows + one row of totals
+    assert need == hist + T * k * 8  # + the row list of moe_route_expand (two int32 per row)
     base = (FAKE, None, T, E, k, FAKE, FAKE, FAKE, None, FAKE, FAKE)
     assert status(lib, lib.moe_route(*base, None, need, None)) == "MOE_ERR_WORKSPACE"
-    assert status(lib, lib.moe_route(*base, FAKE, need - 1, None)) == "MOE_ERR_WORKSPACE"
+    assert status(lib, lib.moe_route(*base, FAKE, hist - 1, None)) == "MOE_ERR_WORKSPACE"
     assert status(lib, lib.moe_route(*base, FAKE + 4, need, None)) == "MOE_ERR_WORKSPACE"
     assert b"workspace" in lib.moe_last_error()
+    # moe_route_expand also needs the row list
+    xargs = (FAKE, None, T, E, k, FAKE, 2048, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE)
+    assert status(lib, lib.moe_route_expand(*xargs, FAKE, need - 1, None)) == "MOE_ERR_WORKSPACE"
 
 
 def test_route_workspace_size_rules(lib):
+    # histogram rows (+ totals), rounded up to 16 bytes, then T*k row-list entries of 8 bytes
     assert lib.moe_route_workspace_bytes(0, 8, 2) > 0
-    assert lib.moe_route_workspace_bytes(1, 5, 2) == 2 * 8 * 4  # one row + totals, experts padded to 8
-    assert lib.moe_route_workspace_bytes(65, 8, 2) == (3 + 1) * 8 * 4  # 32 tokens per row at E=8
-    assert lib.moe_route_workspace_bytes(33, 512, 16) == (3 + 1) * 512 * 4
+    assert lib.moe_route_workspace_bytes(1, 5, 2) == 2 * 8 * 4 + 2 * 8  # one row + totals, experts padded to 8
+    assert lib.moe_route_workspace_bytes(65, 8, 2) == (3 + 1) * 8 * 4 + 65 * 2 * 8  # 32 tokens per row at E=8
+    assert lib.moe_route_workspace_bytes(33, 512, 16) == (3 + 1) * 512 * 4 + 33 * 16 * 8
+    assert lib.moe_route_workspace_bytes(20, 5, 3) == 16 * (-(-2 * 8 * 4 // 16)) + 20 * 3 * 8
     assert lib.moe_route_workspace_bytes(4, 8, 9) == 0  # invalid
 
 

@@ -52,6 +52,23 @@ def test_workload_full_size(dev, oracle_lib, name):
     check_path(got, ref, cfg, name)
 
 
+@pytest.mark.parametrize("order", ["auto", "grouped"])
+@pytest.mark.parametrize("name", inputs.CONFIG_ORDER)
+def test_workload_full_size_route_expand(dev, oracle_lib, monkeypatch, name, order):
+    """Route + expand as one moe_route_expand call at full size (the form the
+    benchmark times): the one-launch dispatch for decode, the grouped
+    destination-order expand or the token-major one above it."""
+    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", order)
+    cfg = inputs.CONFIGS[name]
+    _log(f"[parity] route_expand {inputs.describe(cfg)} seed=0 order={order}")
+    inp = inputs.make_inputs(cfg, 0, parts=("x", "logits"))
+    got = G.run_path(inp, dev, fused=True)
+    ref = oracle_lib.route(inp["logits"], cfg.k, inp["bias"])
+    compare.assert_route_equal(got, ref, f"{name} route_expand")
+    compare.assert_equal(got["x_expanded"], oracle_lib.expand_rows(inp["x"], ref["dest_of_src"], cfg.k),
+                         f"{name} route_expand x_expanded")
+
+
 @pytest.mark.parametrize("seed", [1, 2])
 @pytest.mark.parametrize("name", ["tiny", "decode", "skewed"])
 def test_workload_more_seeds(dev, oracle_lib, name, seed):
@@ -230,12 +247,16 @@ def test_swiglu_shapes(dev, oracle_lib, R, I):
 # ------------------------------------------------------------------ route + expand
 @pytest.mark.parametrize("T,E,k,H", [(0, 16, 4, 256), (1, 8, 2, 8), (7, 128, 8, 2048), (32, 128, 8, 2048),
                                      (64, 256, 8, 7168), (64, 512, 16, 264), (33, 64, 6, 4096), (20, 3, 3, 520),
-                                     (65, 128, 8, 2048), (300, 64, 6, 256)])
-def test_route_expand_matches_oracle(dev, oracle_lib, T, E, k, H):
+                                     (65, 128, 8, 2048), (300, 64, 6, 256), (100, 17, 5, 8), (777, 8, 2, 264),
+                                     (1023, 64, 6, 4096), (2000, 256, 8, 7168), (130, 512, 16, 264),
+                                     (5000, 3, 3, 8), (4096, 128, 8, 2048), (9000, 300, 4, 64)])
+@pytest.mark.parametrize("order", ["auto", "grouped", "token"])
+def test_route_expand_matches_oracle(dev, oracle_lib, monkeypatch, order, T, E, k, H):
     import torch
     import moe_glue_amd as mg
 
-    _log(f"[route_expand] T={T} E={E} k={k} H={H}")
+    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", order)
+    _log(f"[route_expand] T={T} E={E} k={k} H={H} order={order}")
     cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8, bias_std=0.5 if E % 2 == 0 else 0.0)
     inp = inputs.make_inputs(cfg, 6, parts=("x", "logits"))
     bias = None if inp["bias"] is None else G.to_dev(inp["bias"], dev)
@@ -248,12 +269,16 @@ def test_route_expand_matches_oracle(dev, oracle_lib, T, E, k, H):
 
 
 @pytest.mark.parametrize("variant", ["single", "two", "three"])
-def test_route_expand_equals_separate_calls(dev, monkeypatch, variant):
+@pytest.mark.parametrize("T", [48, 700])
+def test_route_expand_equals_separate_calls(dev, monkeypatch, variant, T):
     import torch
     import moe_glue_amd as mg
 
-    T, E, k, H = 48, 128, 8, 2048
-    _log(f"[route_expand] fused vs separate, forced variant {variant}")
+    if variant == "single" and T > 256:
+        pytest.skip("single-workgroup route covers T <= 256")
+    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", "grouped")
+    E, k, H = 128, 8, 2048
+    _log(f"[route_expand] T={T} auto vs forced variant {variant}")
     cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
     inp = inputs.make_inputs(cfg, 8, parts=("x", "logits"))
     logits, x = G.to_dev(inp["logits"], dev), G.to_dev(inp["x"], dev)
