@@ -227,6 +227,51 @@ def copy_probe_gbps(dev, nbytes=1 << 30, reps=5):
     return 2 * nbytes / t / 1e9, t
 
 
+def launch_floor_us(dev, n=100):
+    """Device time of one tiny kernel (a 16-byte moe_copy_probe) when kernels
+    run back to back: n launches captured in a HIP graph and replayed, so the
+    host's per-call cost is out of the measurement.  None if capture fails."""
+    import torch
+    import moe_glue_amd as mg
+
+    try:
+        lib = mg.load()
+        src = torch.ones(16, dtype=torch.uint8, device=dev)
+        dst = torch.empty(16, dtype=torch.uint8, device=dev)
+        side = torch.cuda.Stream(device=dev)
+        with torch.cuda.stream(side):
+            lib.moe_copy_probe(src.data_ptr(), dst.data_ptr(), 16, side.cuda_stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(n):
+                lib.moe_copy_probe(src.data_ptr(), dst.data_ptr(), 16, side.cuda_stream)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(1e3 * e0.elapsed_time(e1) / (5 * n), 3)
+    except Exception as ex:  # capture unsupported: report nothing rather than a wrong floor
+        print(f"bench.py: launch floor not measured ({type(ex).__name__}: {ex})", file=sys.stderr)
+        return None
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(inp, passes=3):
     """The CPU oracle as it stands, single-threaded, on the same workload."""
     import oracle
@@ -241,7 +286,8 @@ def cpu_baseline(inp, passes=3):
     t = sum(times) / len(times)
     return {"value": inp["cfg"].T / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"the full {inp['cfg'].name} batch (T={inp['cfg'].T}), route+expand+swiglu+combine, "
-                      f"mean of {passes} passes after one warm pass, single thread, {t:.3f} s per pass"}
+                      f"mean of {passes} passes after one warm pass, single thread, {t:.3f} s per pass, "
+                      f"{cpu_model()}, {os.cpu_count()} logical CPUs visible"}
 
 
 def main(argv=None):
@@ -276,6 +322,7 @@ def main(argv=None):
     inp = I.make_inputs(cfg, args.seed)
     sets = Sets(inp, args.sets, dev, args.pad, args.fp8_group)
     achievable, _ = copy_probe_gbps(dev)
+    floor_us = launch_floor_us(dev)
 
     for s in range(args.warmup):
         sets.step(s)
@@ -349,6 +396,7 @@ def main(argv=None):
                    "input_sets": args.sets, "seed": args.seed, "pad_to": args.pad, "fp8_group": args.fp8_group},
         "path_GBps": round(sum(ab[n] for n in names) / (elapsed / args.steps) / 1e9, 1),
         "achievable_copy_GBps": round(achievable, 1),
+        "launch_floor_us": floor_us,
         "host_us_per_step": round(1e6 * host_s / args.steps, 2),
         "events": args.events,
         "ms_per_step_with_events": None if events_elapsed is None else round(1e3 * events_elapsed / args.steps, 4),
