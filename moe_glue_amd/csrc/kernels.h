@@ -15,8 +15,11 @@ namespace moe {
 // and the largest T it is chosen for automatically.
 constexpr int kRouteFusedMaxTokens = 256;
 constexpr int kRouteSingleAutoMaxTokens = 64;
-// Largest histogram matrix (bytes) for which scan and place share one launch.
+// Largest histogram matrix (bytes, one count byte per expert and top-k row)
+// for which scan and place share one launch, and the largest T (the column
+// sums are formed in 16-bit halves).
 constexpr size_t kRouteTwoPassMaxBytes = 128 * 1024;
+constexpr int kRouteTwoPassMaxTokens = 65535;
 
 // Single workgroup; multi workgroup with the scan and place in one launch
 // (TwoPass) or in two (ThreePass); Auto picks by T and the matrix size.
@@ -83,6 +86,13 @@ int route_lanes_per_token(int E);
 int route_tokens_per_block(int E);
 // Experts padded to a multiple of 4 (one int4 per 4 experts in the workspace).
 inline int route_padded_experts(int E) { return (E + 3) & ~3; }
+// 16-byte vectors per byte histogram row (one count byte per expert): E/16
+// rounded up to a power of two.
+__host__ __device__ inline int route_byte_row_vectors(int E) {
+    int p = 1;
+    while (p * 16 < E) p <<= 1;
+    return p;
+}
 // Workspace of the multi-workgroup route: one histogram row per top-k
 // workgroup plus one row of totals, then (16-byte aligned) the row list of
 // the grouped expand, T*k entries of two int32.

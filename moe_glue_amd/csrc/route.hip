@@ -68,9 +68,11 @@ __global__ __launch_bounds__((SingleShape<G>::THREADS)) void route_single_kernel
 
 // ------------------------------------------------------------- multi workgroup
 // 1. Workgroup b owns tokens [b*TOK, b*TOK + TOK).  Writes the top-k, each
-// slot's rank inside the workgroup (into dest_of_src, finished by step 3) and
-// the workgroup's histogram (workspace row b, Epad ints, zero padded).
-template <int G, int V>
+// slot's rank inside the workgroup (into dest_of_src, finished later) and the
+// workgroup's histogram as workspace row b: Epad int32 (three-launch form) or
+// one count byte per expert in route_byte_row_vectors(E) 16-byte vectors
+// (two-launch form; a count is at most TOK <= 64), zero padded.
+template <int G, int V, bool BYTES>
 __global__ __launch_bounds__((TopkShape<G>::THREADS)) void route_topk_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights, int32_t* __restrict__ dest_of_src,
@@ -84,13 +86,25 @@ __global__ __launch_bounds__((TopkShape<G>::THREADS)) void route_topk_kernel(
     const int tok0 = blockIdx.x * S::TOK;
     const int ntok = min(S::TOK, T - tok0);
     const int grp = threadIdx.x / G;
+    clear_masks<S::THREADS>(masks, Epad, nullptr, 0);
     topk_token<G, V>(logits, bias, T, E, k, tok0 + grp, grp, threadIdx.x % G, topk_ids, topk_weights, ids_lds);
     __syncthreads();
-    build_masks<S::THREADS>(ids_lds, ntok, k, Epad, 1, masks);
+    mark_masks<S::THREADS>(ids_lds, ntok, k, Epad, masks, nullptr);
     for (int s = threadIdx.x; s < ntok * k; s += S::THREADS)
         dest_of_src[(size_t)tok0 * k + s] = slot_rank(masks, Epad, s / k, ids_lds[s]);
-    for (int e = threadIdx.x; e < Epad; e += S::THREADS)
-        block_counts[(size_t)blockIdx.x * Epad + e] = (e < E) ? __popcll(masks[e]) : 0;
+    if constexpr (BYTES) {
+        const int words = route_byte_row_vectors(E) * 4;  // 4 experts per word
+        for (int i = threadIdx.x; i < words; i += S::THREADS) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                if (4 * i + b < E) w |= (uint32_t)__popcll(masks[4 * i + b]) << (8 * b);
+            block_counts[(size_t)blockIdx.x * words + i] = (int32_t)w;
+        }
+    } else {
+        for (int e = threadIdx.x; e < Epad; e += S::THREADS)
+            block_counts[(size_t)blockIdx.x * Epad + e] = (e < E) ? __popcll(masks[e]) : 0;
+    }
 }
 
 // Exclusive scan of one int4 per lane over a workgroup of THREADS lanes.
@@ -226,46 +240,60 @@ __global__ __launch_bounds__(kPlaceThreads) void route_place_kernel(
     }
 }
 
-// 2+3 fused, for a small histogram matrix: workgroup g owns kFusedRows
-// consecutive top-k rows.  It sums every histogram row into column sums --
-// the totals and the prefix before its first row (and with LIST the prefixes
-// at its token group's first and last row) -- keeps its own rows, scans the
-// totals into offsets, and writes its slots.  Reading the whole matrix per
-// workgroup costs L2 bandwidth instead of a third launch; the host picks this
-// form only while the matrix is small.  With LIST each slot also gets its
-// row-list entry (as in route_place_kernel).
+// 2+3 fused, for a small histogram matrix of count bytes: workgroup g owns
+// kFusedRows consecutive top-k rows.  It sums every histogram row into column
+// sums -- the totals and the prefix before its first row (and with LIST the
+// prefixes at its token group's first and last row) -- keeps its own rows,
+// scans the totals into offsets, and writes its slots.  Reading the whole
+// matrix per workgroup costs L2 bandwidth instead of a third launch; the host
+// picks this form only while the matrix is small (and T < 2^16, see below).
+// With LIST each slot also gets its row-list entry (as in route_place_kernel).
 //
-// Lane layout: lane = rg * Qp + q, q = int4 column (Qp = Q rounded up to a
-// power of two), rg = row group; each lane sums rows rg, rg + RP, ...  The
-// row groups are reduced inside each wave by lane exchanges (lanes with the
-// same q sit Qp apart), leaving at most 16 partials per column in LDS; then
-// F lanes share each (sum, expert) item, read its partials as plain ints and
-// join by lane exchanges.
+// Lane layout: lane = rg * Qp + q, q = 16-byte column (16 experts), rg = row
+// group; each lane sums rows rg, rg + RP, ...  A column's 16 count bytes are
+// summed as 16-bit halves (bytes 0,2 and 1,3 of each word), which is exact
+// while every total stays below 2^16, i.e. T < 2^16.  The row groups are
+// reduced inside each wave by DPP row rotations and permlane swaps (lanes of
+// one column sit Qp apart), then across the 16 waves through LDS.
 constexpr int kFusedThreads = 1024;
 constexpr int kFusedRows = kPlaceRows;
 constexpr int kFusedSlots = kFusedRows * kChunk * kKMax / kFusedThreads;
 constexpr int kFusedWaves = kFusedThreads / kWave;
+constexpr int kMaxRowVectors = kEMax / 16;
 
-template <bool LIST>
+// Sum of v over the lanes of the wave that sit a multiple of QP apart (QP a
+// power of two <= 32): DPP rotations inside each 16-lane row, then the
+// permlane swaps across rows.
+template <int QP>
+__device__ __forceinline__ uint32_t add_lanes(uint32_t v) {
+    if constexpr (QP <= 1) v += dpp<0x121>(v);  // row_ror:1
+    if constexpr (QP <= 2) v += dpp<0x122>(v);  // row_ror:2
+    if constexpr (QP <= 4) v += dpp<0x124>(v);  // row_ror:4
+    if constexpr (QP <= 8) v += dpp<0x128>(v);  // row_ror:8
+    if constexpr (QP <= 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = p[0] + p[1];
+    }
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return p[0] + p[1];
+}
+
+template <bool LIST, int QP>
 __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
-    const int32_t* __restrict__ counts, int nb, int tok_per_row, int T, int E, int k, int pad,
+    const u32x4* __restrict__ rows8, int nb, int tok_per_row, int T, int E, int k, int pad,
     const int32_t* __restrict__ topk_ids, int32_t* __restrict__ dest_of_src, int32_t* __restrict__ src_of_dest,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ expert_counts, RowGroups groups,
     int2* __restrict__ row_list) {
     // column sums over rows below: nb (all), row0, and with LIST the group's first and last row
     constexpr int NACC = LIST ? 4 : 2;
-    // partials (partial group pg, column q) at pg * Qp + q: at most kFusedThreads entries
-    __shared__ i32x4 part[NACC][kFusedThreads];
-    __shared__ i32x4 s_rows[kFusedRows][kEMax / 4];
+    __shared__ uint32_t part[NACC][kFusedWaves][kMaxRowVectors][8];
+    __shared__ __attribute__((aligned(16))) uint8_t s_rows[kFusedRows][kEMax];
     __shared__ int32_t s_acc[NACC][kEMax];
     __shared__ int32_t s_off[kEMax + 1];
     __shared__ int32_t s_gcum[LIST ? kEMax + 1 : 1];
 
-    const int Epad = (E + 3) & ~3;
-    const int Q = Epad / 4;  // int4 per histogram row (<= 128)
-    int Qp = 1;
-    while (Qp < Q) Qp <<= 1;
-    const int RP = kFusedThreads / Qp;  // row groups (>= 8)
+    constexpr int Qp = QP;                     // route_byte_row_vectors(E) <= 32
+    constexpr int RP = kFusedThreads / Qp;     // row groups (>= 32)
     const int q = threadIdx.x % Qp;
     const int rg = threadIdx.x / Qp;
     const int row0 = blockIdx.x * kFusedRows;
@@ -290,52 +318,53 @@ __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
             my_r[u] = dest_of_src[(size_t)tok0 * k + s];
         }
     }
-    i32x4 acc[NACC];
+    // acc[a][2j] / acc[a][2j+1]: 16-bit sums of bytes (0,2) / (1,3) of word j
+    uint32_t acc[NACC][8];
 #pragma unroll
-    for (int a = 0; a < NACC; ++a) acc[a] = (i32x4){0, 0, 0, 0};
-    if (q < Q) {
-        const i32x4* rows = reinterpret_cast<const i32x4*>(counts);
-#pragma unroll 8
-        for (int row = rg; row < nb; row += RP) {
-            const i32x4 c = rows[(size_t)row * Q + q];
+    for (int a = 0; a < NACC; ++a)
 #pragma unroll
-            for (int a = 0; a < NACC; ++a)
-                if (row < bound[a]) acc[a] += c;
-            if (row >= row0 && row < row0 + kFusedRows) s_rows[row - row0][q] = c;
+        for (int j = 0; j < 8; ++j) acc[a][j] = 0;
+#pragma unroll 4
+    for (int row = rg; row < nb; row += RP) {
+        const u32x4 w = rows8[(size_t)row * Qp + q];
+        if (row >= row0 && row < row0 + kFusedRows) *reinterpret_cast<u32x4*>(&s_rows[row - row0][q * 16]) = w;
+        uint32_t half[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            half[2 * j] = w[j] & 0x00FF00FFu;
+            half[2 * j + 1] = (w[j] >> 8) & 0x00FF00FFu;
+        }
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) {
+            const uint32_t keep = row < bound[a] ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[a][j] += half[j] & keep;
         }
     }
-    // inside the wave: the 64 / Qp row groups of a wave (none to join when Qp >= 64)
-    for (int m = Qp; m < kWave; m <<= 1) {
+    // inside the wave: lanes of one column sit Qp apart
+#pragma unroll
+    for (int a = 0; a < NACC; ++a)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[a][j] = add_lanes<QP>(acc[a][j]);
+    const int w = threadIdx.x / kWave;
+    if ((int)(threadIdx.x % kWave) < Qp) {
 #pragma unroll
         for (int a = 0; a < NACC; ++a)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[a][c] += __shfl_xor(acc[a][c], m);
-    }
-    // one partial per wave (Qp < 64) or per row group (Qp >= 64)
-    const int npg = Qp < kWave ? kFusedWaves : RP;
-    if (Qp >= kWave || (int)(threadIdx.x % kWave) < Qp) {
-        const int pg = Qp < kWave ? (int)(threadIdx.x / kWave) : rg;
-#pragma unroll
-        for (int a = 0; a < NACC; ++a) part[a][pg * Qp + q] = acc[a];
+            for (int j = 0; j < 8; ++j) part[a][w][q][j] = acc[a][j];
     }
     __syncthreads();
-    // items (a, e), e < 4 * Qp; F adjacent lanes per item, cnt partials each
-    {
-        const int EQ = 4 * Qp;
-        int F = kFusedThreads / (NACC * EQ);
-        F = F < 1 ? 1 : (F > npg ? npg : F);
-        const int cnt = npg / F;
-        const int h = threadIdx.x % F;
-        for (int item = threadIdx.x / F; item < NACC * EQ; item += kFusedThreads / F) {
-            const int a = item / EQ;
-            const int e = item % EQ;
-            const int32_t* pa = reinterpret_cast<const int32_t*>(part[a]) + (e >> 2) * 4 + (e & 3);
-            int sum = 0;
-#pragma unroll 4
-            for (int j = 0; j < cnt; ++j) sum += pa[(h * cnt + j) * Qp * 4];
-            for (int m = 1; m < F; m <<= 1) sum += __shfl_xor(sum, m);
-            if (h == 0 && e < E) s_acc[a][e] = sum;
-        }
+    // lane (a, column, word): sum the 16 waves, split the halves into experts
+    for (int i = threadIdx.x; i < NACC * Qp * 8; i += kFusedThreads) {
+        const int a = i / (Qp * 8);
+        const int qq = (i / 8) % Qp;
+        const int j = i % 8;
+        uint32_t sum = 0;
+#pragma unroll
+        for (int v = 0; v < kFusedWaves; ++v) sum += part[a][v][qq][j];
+        const int e = qq * 16 + (j / 2) * 4 + (j % 2);  // bytes 0/1 of word j/2; +2 for bytes 2/3
+        if (e < E) s_acc[a][e] = (int32_t)(sum & 0xFFFFu);
+        if (e + 2 < E) s_acc[a][e + 2] = (int32_t)(sum >> 16);
     }
     __syncthreads();
     wave_exclusive_scan(s_acc[0], s_off, E, pad, 0);
@@ -355,7 +384,7 @@ __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
             const int r = (s / k) / tok_per_row;
             const int e = my_e[u];
             int before = s_acc[1][e] + my_r[u];  // earlier tokens that picked e
-            for (int r2 = 0; r2 < r; ++r2) before += s_rows[r2][e >> 2][e & 3];
+            for (int r2 = 0; r2 < r; ++r2) before += s_rows[r2][e];
             const int d = s_off[e] + before;
             dest_of_src[gs] = d;
             src_of_dest[d] = (int32_t)gs;
@@ -364,6 +393,19 @@ __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
                     make_int2(d, tok0 + s / k);
         }
     }
+}
+
+template <int QP>
+void launch_scan_place(bool list, int nwg, const u32x4* rows8, int nb, int tok_per_row, const RouteArgs& a,
+                       int2* row_list, hipStream_t stream) {
+    if (list)
+        route_scan_place_kernel<true, QP><<<nwg, kFusedThreads, 0, stream>>>(
+            rows8, nb, tok_per_row, a.T, a.E, a.k, a.pad_to, a.topk_ids, a.dest_of_src, a.src_of_dest,
+            a.expert_offsets, a.expert_counts, a.groups, row_list);
+    else
+        route_scan_place_kernel<false, QP><<<nwg, kFusedThreads, 0, stream>>>(
+            rows8, nb, tok_per_row, a.T, a.E, a.k, a.pad_to, a.topk_ids, a.dest_of_src, a.src_of_dest,
+            a.expert_offsets, a.expert_counts, a.groups, row_list);
 }
 
 template <int G, int V>
@@ -379,22 +421,27 @@ hipError_t launch_route_gv(const RouteArgs& a, RouteVariant v, hipStream_t strea
     const int Epad = route_padded_experts(a.E);
     int32_t* counts = static_cast<int32_t*>(a.workspace);
     int32_t* totals = counts + (size_t)nb * Epad;
-    route_topk_kernel<G, V><<<nb, S::THREADS, 0, stream>>>(a.logits, a.bias, a.T, a.E, a.k, a.topk_ids,
-                                                           a.topk_weights, a.dest_of_src, counts);
+    if (v == RouteVariant::TwoPass)
+        route_topk_kernel<G, V, true><<<nb, S::THREADS, 0, stream>>>(a.logits, a.bias, a.T, a.E, a.k, a.topk_ids,
+                                                                     a.topk_weights, a.dest_of_src, counts);
+    else
+        route_topk_kernel<G, V, false><<<nb, S::THREADS, 0, stream>>>(a.logits, a.bias, a.T, a.E, a.k, a.topk_ids,
+                                                                      a.topk_weights, a.dest_of_src, counts);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const bool list = a.row_list != nullptr;
     int2* row_list = reinterpret_cast<int2*>(a.row_list);
     if (v == RouteVariant::TwoPass) {
         const int nwg = (nb + kFusedRows - 1) / kFusedRows;
-        if (list)
-            route_scan_place_kernel<true><<<nwg, kFusedThreads, 0, stream>>>(
-                counts, nb, S::TOK, a.T, a.E, a.k, a.pad_to, a.topk_ids, a.dest_of_src, a.src_of_dest,
-                a.expert_offsets, a.expert_counts, a.groups, row_list);
-        else
-            route_scan_place_kernel<false><<<nwg, kFusedThreads, 0, stream>>>(
-                counts, nb, S::TOK, a.T, a.E, a.k, a.pad_to, a.topk_ids, a.dest_of_src, a.src_of_dest,
-                a.expert_offsets, a.expert_counts, a.groups, row_list);
+        const u32x4* rows8 = reinterpret_cast<const u32x4*>(counts);
+        switch (route_byte_row_vectors(a.E)) {
+            case 1: launch_scan_place<1>(list, nwg, rows8, nb, S::TOK, a, row_list, stream); break;
+            case 2: launch_scan_place<2>(list, nwg, rows8, nb, S::TOK, a, row_list, stream); break;
+            case 4: launch_scan_place<4>(list, nwg, rows8, nb, S::TOK, a, row_list, stream); break;
+            case 8: launch_scan_place<8>(list, nwg, rows8, nb, S::TOK, a, row_list, stream); break;
+            case 16: launch_scan_place<16>(list, nwg, rows8, nb, S::TOK, a, row_list, stream); break;
+            default: launch_scan_place<32>(list, nwg, rows8, nb, S::TOK, a, row_list, stream); break;
+        }
         return hipGetLastError();
     }
     route_scan_kernel<<<Epad / 4, kScanThreads, 0, stream>>>(counts, nb, Epad, totals);
@@ -447,7 +494,8 @@ RouteVariant route_pick_variant(int T, int E, RouteVariant requested) {
         case RouteVariant::SingleWorkgroup:
             if (T <= kRouteFusedMaxTokens) return requested;
             break;
-        case RouteVariant::TwoPass:
+        case RouteVariant::TwoPass:  // its 16-bit column sums need T < 2^16
+            return T <= kRouteTwoPassMaxTokens ? requested : RouteVariant::ThreePass;
         case RouteVariant::ThreePass:
             return requested;
         default:
@@ -455,8 +503,9 @@ RouteVariant route_pick_variant(int T, int E, RouteVariant requested) {
             break;
     }
     const int tb = route_tokens_per_block(E);
-    const size_t matrix = (size_t)((T + tb - 1) / tb) * route_padded_experts(E) * sizeof(int32_t);
-    return matrix <= kRouteTwoPassMaxBytes ? RouteVariant::TwoPass : RouteVariant::ThreePass;
+    const size_t matrix = (size_t)((T + tb - 1) / tb) * route_byte_row_vectors(E) * 16;
+    return matrix <= kRouteTwoPassMaxBytes && T <= kRouteTwoPassMaxTokens ? RouteVariant::TwoPass
+                                                                          : RouteVariant::ThreePass;
 }
 
 hipError_t launch_route(const RouteArgs& a, RouteVariant variant, hipStream_t stream) {

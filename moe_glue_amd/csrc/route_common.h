@@ -112,17 +112,27 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, con
     }
 }
 
-// Per-expert token bitmaps of `ntok` tokens (ids in ids_lds, token-major [ntok][k]):
-// masks[c * Epad + e] bit b set <=> token c*64 + b picked expert e.
+// Per-expert token bitmaps: masks[c * Epad + e] bit b set <=> token c*64 + b
+// picked expert e.  clear_masks zeroes them (and the per-expert counts, when
+// given); callers run it before the top-k, so the barrier that follows the
+// top-k orders the clearing before mark_masks.  mark_masks sets each slot's
+// bit with an LDS atomic OR (order-free) and counts it, then waits for the
+// workgroup.
 template <int THREADS>
-__device__ __forceinline__ void build_masks(const int32_t* ids_lds, int ntok, int k, int Epad, int nchunks,
-                                            unsigned long long* masks) {
-    for (int i = threadIdx.x; i < nchunks * Epad; i += THREADS) masks[i] = 0ull;
-    __syncthreads();
+__device__ __forceinline__ void clear_masks(unsigned long long* masks, int n, int32_t* s_cnt, int E) {
+    for (int i = threadIdx.x; i < n; i += THREADS) masks[i] = 0ull;
+    if (s_cnt != nullptr)
+        for (int e = threadIdx.x; e < E; e += THREADS) s_cnt[e] = 0;
+}
+
+template <int THREADS>
+__device__ __forceinline__ void mark_masks(const int32_t* ids_lds, int ntok, int k, int Epad,
+                                           unsigned long long* masks, int32_t* s_cnt) {
     for (int s = threadIdx.x; s < ntok * k; s += THREADS) {
         const int tl = s / k;
         const int e = ids_lds[s];
         atomicOr(&masks[(tl >> 6) * Epad + e], 1ull << (tl & 63));
+        if (s_cnt != nullptr) atomicAdd(&s_cnt[e], 1);
     }
     __syncthreads();
 }
@@ -134,12 +144,6 @@ __device__ __forceinline__ int slot_rank(const unsigned long long* masks, int Ep
     int r = __popcll(masks[c * Epad + e] & below);
     for (int c2 = 0; c2 < c; ++c2) r += __popcll(masks[c2 * Epad + e]);
     return r;
-}
-
-__device__ __forceinline__ int mask_count(const unsigned long long* masks, int Epad, int nchunks, int e) {
-    int n = 0;
-    for (int c = 0; c < nchunks; ++c) n += __popcll(masks[c * Epad + e]);
-    return n;
 }
 
 // Segment length of an expert with `count` rows: count rounded up to a
@@ -228,16 +232,15 @@ __device__ __forceinline__ void route_small(const float* __restrict__ logits, co
     const int grp = threadIdx.x / G;
     const int gl = threadIdx.x % G;
     const int wave_first = (threadIdx.x / kWave) * (kWave / G);  // first token slot of this wave in a pass
+    const int nchunks = (T + kChunk - 1) / kChunk;
+    clear_masks<S::THREADS>(masks, nchunks * Epad, s_cnt, E);
     for (int t0 = 0; t0 < T; t0 += S::TOK_PER_PASS) {
         if (t0 + wave_first < T)  // wave-uniform: the lane exchange stays whole-wave
             topk_token<G, V>(logits, bias, T, E, k, t0 + grp, t0 + grp, gl, write ? topk_ids : nullptr,
                              topk_weights, ids_lds);
     }
     __syncthreads();
-    const int nchunks = (T + kChunk - 1) / kChunk;
-    build_masks<S::THREADS>(ids_lds, T, k, Epad, nchunks, masks);
-    for (int e = threadIdx.x; e < E; e += S::THREADS) s_cnt[e] = mask_count(masks, Epad, nchunks, e);
-    __syncthreads();
+    mark_masks<S::THREADS>(ids_lds, T, k, Epad, masks, s_cnt);
     wave0_exclusive_scan(s_cnt, s_off, E, pad);
     __syncthreads();
     if (write) {
