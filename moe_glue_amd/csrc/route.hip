@@ -18,8 +18,10 @@
 //     3. place     per workgroup of step 1: scan the totals into offsets (in
 //                  LDS) and write dest = offset + prefix + rank and its inverse.
 //   Each launch costs a few microseconds on its own, so while the histogram
-//   matrix is small (up to 128 KiB) steps 2 and 3 run as one launch in which
-//   every workgroup reads the whole matrix.
+//   matrix is small (up to 128 KiB of count bytes) steps 2 and 3 run as one
+//   launch in which every workgroup reads the whole matrix.  For
+//   moe_route_expand the place step also writes the row list of the grouped
+//   expand (expand.hip).
 //
 // The page's blocks claim slots with shared-memory atomic increments, which
 // gives each expert's list in arbitrary order.  Here the order is fixed
