@@ -286,7 +286,6 @@ __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
     const int32_t* __restrict__ topk_ids, int32_t* __restrict__ dest_of_src, int32_t* __restrict__ src_of_dest,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ expert_counts, RowGroups groups,
     int2* __restrict__ row_list) {
-    // column sums over rows below: nb (all), row0, and with LIST the group's first and last row
     constexpr int NACC = LIST ? 4 : 2;
     __shared__ uint32_t part[NACC][kFusedWaves][kMaxRowVectors][8];
     __shared__ __attribute__((aligned(16))) uint8_t s_rows[kFusedRows][kEMax];
@@ -302,13 +301,8 @@ __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
     const int tok0 = row0 * tok_per_row;
     const int nslot = min(kFusedRows * tok_per_row, T - tok0) * k;
     const int gj = LIST ? group_of_unit(groups, blockIdx.x) : 0;  // the token group of this workgroup
-    int bound[NACC];
-    bound[0] = nb;
-    bound[1] = row0;
-    if constexpr (LIST) {
-        bound[2] = group_row(groups, gj);
-        bound[3] = group_row(groups, gj + 1);
-    }
+    const int gfirst = LIST ? group_row(groups, gj) : 0;          // its rows [gfirst, gend)
+    const int gend = LIST ? group_row(groups, gj + 1) : 0;
 
     // every independent load first: the slots, then the histogram columns
     int my_e[kFusedSlots], my_r[kFusedSlots];
@@ -320,7 +314,10 @@ __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
             my_r[u] = dest_of_src[(size_t)tok0 * k + s];
         }
     }
-    // acc[a][2j] / acc[a][2j+1]: 16-bit sums of bytes (0,2) / (1,3) of word j
+    // acc[a][2j] / acc[a][2j+1]: 16-bit sums of bytes (0,2) / (1,3) of word j,
+    // over [0] every row, [1] the rows before row0, and with LIST [2] the
+    // group's rows before row0, [3] the group's rows from row0 on (only the
+    // waves that hold group rows do any work for these two)
     uint32_t acc[NACC][8];
 #pragma unroll
     for (int a = 0; a < NACC; ++a)
@@ -336,11 +333,20 @@ __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
             half[2 * j] = w[j] & 0x00FF00FFu;
             half[2 * j + 1] = (w[j] >> 8) & 0x00FF00FFu;
         }
+        const uint32_t before_row0 = row < row0 ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-        for (int a = 0; a < NACC; ++a) {
-            const uint32_t keep = row < bound[a] ? 0xFFFFFFFFu : 0u;
+        for (int j = 0; j < 8; ++j) {
+            acc[0][j] += half[j];
+            acc[1][j] += half[j] & before_row0;
+        }
+        if constexpr (LIST) {
+            if (row >= gfirst && row < gend) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[a][j] += half[j] & keep;
+                for (int j = 0; j < 8; ++j) {
+                    acc[2][j] += half[j] & before_row0;
+                    acc[3][j] += half[j] & ~before_row0;
+                }
+            }
         }
     }
     // inside the wave: lanes of one column sit Qp apart
@@ -370,7 +376,7 @@ __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
     }
     __syncthreads();
     wave_exclusive_scan(s_acc[0], s_off, E, pad, 0);
-    if constexpr (LIST) wave_exclusive_scan(s_acc[3], s_gcum, E, 1, 1, s_acc[2]);  // the group's own counts
+    if constexpr (LIST) wave_exclusive_scan(s_acc[2], s_gcum, E, 1, 1, s_acc[3]);  // the group's own counts
     __syncthreads();
     if (blockIdx.x == 0) {
         for (int e = threadIdx.x; e <= E; e += kFusedThreads) expert_offsets[e] = s_off[e];
@@ -390,8 +396,8 @@ __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
             const int d = s_off[e] + before;
             dest_of_src[gs] = d;
             src_of_dest[d] = (int32_t)gs;
-            if constexpr (LIST)
-                row_list[(size_t)group_tok(groups, gj) * k + s_gcum[e] + (before - s_acc[2][e])] =
+            if constexpr (LIST)  // earlier tokens of the group that picked e: its rows before row0, then own
+                row_list[(size_t)group_tok(groups, gj) * k + s_gcum[e] + s_acc[2][e] + (before - s_acc[1][e])] =
                     make_int2(d, tok0 + s / k);
         }
     }

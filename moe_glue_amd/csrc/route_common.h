@@ -150,18 +150,18 @@ __device__ __forceinline__ int slot_rank(const unsigned long long* masks, int Ep
 // multiple of pad (pad = 1: unpadded).
 __device__ __forceinline__ int padded_len(int count, int pad) { return pad == 1 ? count : (count + pad - 1) / pad * pad; }
 
-// Exclusive prefix sum of the padded lengths of in[0..n) (minus minus[i] when
+// Exclusive prefix sum of the padded lengths of in[0..n) (plus add[i] when
 // given) into out[0..n], out[n] = total; n <= 512.  Run by wave `w` of the
 // workgroup only: each lane owns ceil(n/64) consecutive entries.
 __device__ __forceinline__ void wave_exclusive_scan(const int32_t* in, int32_t* out, int n, int pad, int w,
-                                                    const int32_t* minus = nullptr) {
+                                                    const int32_t* add = nullptr) {
     if ((int)(threadIdx.x / kWave) != w) return;
     const int lane = threadIdx.x % kWave;
     const int per = (n + kWave - 1) / kWave;
     const int base = lane * per;
     int local = 0;
     for (int i = 0; i < per; ++i)
-        if (base + i < n) local += padded_len(in[base + i] - (minus ? minus[base + i] : 0), pad);
+        if (base + i < n) local += padded_len(in[base + i] + (add ? add[base + i] : 0), pad);
     int incl = local;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -172,7 +172,7 @@ __device__ __forceinline__ void wave_exclusive_scan(const int32_t* in, int32_t* 
     for (int i = 0; i < per; ++i) {
         if (base + i < n) {
             out[base + i] = run;
-            run += padded_len(in[base + i] - (minus ? minus[base + i] : 0), pad);
+            run += padded_len(in[base + i] + (add ? add[base + i] : 0), pad);
         }
     }
     if (lane == kWave - 1) out[n] = incl;
