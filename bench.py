@@ -307,8 +307,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by tokens, see the design notes)", file=sys.stderr)
+        print(f"bench.py: the MoE glue path runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(no multi-GPU dispatch/combine is implemented)", file=sys.stderr)
         return 2
 
     import torch
