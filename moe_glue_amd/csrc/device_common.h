@@ -116,5 +116,20 @@ __device__ __forceinline__ uint32_t group_reduce(uint32_t v) {
     return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (every lane active):
+// Hillis-Steele shifts of 1, 2, 4 and 8 lanes inside each 16-lane row by DPP
+// row_shr (lanes shifted in from outside the row read 0), then each row adds
+// the totals of the rows below it, read with v_readlane.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+    v += (int)dpp<0x111>((uint32_t)v);  // row_shr:1
+    v += (int)dpp<0x112>((uint32_t)v);  // row_shr:2
+    v += (int)dpp<0x114>((uint32_t)v);  // row_shr:4
+    v += (int)dpp<0x118>((uint32_t)v);  // row_shr:8
+    const int row = (int)(threadIdx.x % kWave) >> 4;
+    const int r0 = __builtin_amdgcn_readlane(v, 15);
+    const int r1 = __builtin_amdgcn_readlane(v, 31);
+    const int r2 = __builtin_amdgcn_readlane(v, 47);
+    return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
 
 }  // namespace moe

@@ -115,14 +115,9 @@ __device__ __forceinline__ i32x4 block_exclusive_scan4(i32x4 v, i32x4& total, i3
     constexpr int NW = THREADS / kWave;
     const int lane = threadIdx.x % kWave;
     const int w = threadIdx.x / kWave;
-    i32x4 incl = v;
+    i32x4 incl;
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        i32x4 y;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) y[c] = __shfl_up(incl[c], d);
-        if (lane >= d) incl += y;
-    }
+    for (int c = 0; c < 4; ++c) incl[c] = wave_inclusive_sum(v[c]);
     if (lane == kWave - 1) wave_tot[w] = incl;
     __syncthreads();
     i32x4 before = {0, 0, 0, 0};

@@ -162,12 +162,7 @@ __device__ __forceinline__ void wave_exclusive_scan(const int32_t* in, int32_t* 
     int local = 0;
     for (int i = 0; i < per; ++i)
         if (base + i < n) local += padded_len(in[base + i] + (add ? add[base + i] : 0), pad);
-    int incl = local;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int y = __shfl_up(incl, d);
-        if (lane >= d) incl += y;
-    }
+    const int incl = wave_inclusive_sum(local);
     int run = incl - local;
     for (int i = 0; i < per; ++i) {
         if (base + i < n) {
