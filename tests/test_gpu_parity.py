@@ -268,6 +268,28 @@ def test_route_expand_matches_oracle(dev, oracle_lib, monkeypatch, order, T, E, 
     compare.assert_equal(got["x_expanded"], oracle_lib.expand_rows(inp["x"], ref["dest_of_src"], k), "x_expanded")
 
 
+@pytest.mark.parametrize("variant", ["auto", "two", "three"])
+@pytest.mark.parametrize("T,E,k,H", [(70000, 64, 2, 64), (65535, 8, 2, 16), (20000, 512, 16, 8)])
+def test_route_expand_large_batches(dev, oracle_lib, monkeypatch, variant, T, E, k, H):
+    """Batches past the two-launch route's 2^16-token limit (a forced two-launch
+    request falls back to three launches), many token groups, E = 512 with
+    k = 16; grouped destination order throughout."""
+    import torch
+    import moe_glue_amd as mg
+
+    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
+    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", "grouped")
+    _log(f"[route_expand] large T={T} E={E} k={k} H={H} variant={variant}")
+    cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
+    inp = inputs.make_inputs(cfg, 13, parts=("x", "logits"))
+    r = mg.route_expand(G.to_dev(inp["logits"], dev), k, G.to_dev(inp["x"], dev))
+    torch.cuda.synchronize()
+    got = G.route_host(r)
+    ref = oracle_lib.route(inp["logits"], k)
+    compare.assert_route_equal(got, ref, f"route_expand large T={T}")
+    compare.assert_equal(got["x_expanded"], oracle_lib.expand_rows(inp["x"], ref["dest_of_src"], k), "x_expanded")
+
+
 @pytest.mark.parametrize("variant", ["single", "two", "three"])
 @pytest.mark.parametrize("T", [48, 700])
 def test_route_expand_equals_separate_calls(dev, monkeypatch, variant, T):
