@@ -9,6 +9,7 @@
  *   moe_route_expand route + expand (one launch for small decode batches,
  *                    destination-order copy above)
  *   moe_route_padded route with expert segments padded to a row multiple
+ *   moe_route_expand_padded  moe_route_padded + expand in one call
  *   moe_expand_rows_fp8  expand with FP8 (E4M3) quantisation per column group
  *
  * The problem statement these calls follow:
@@ -182,6 +183,20 @@ moe_status moe_route_expand(const float* logits, const float* bias, int32_t T, i
                             int32_t* expert_offsets, int32_t* expert_counts, int32_t* dest_of_src,
                             int32_t* src_of_dest, uint16_t* x_expanded, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/* moe_route_padded followed by moe_expand_rows, in one call: exactly their
+ * results on the same arguments (all outputs of both calls are written;
+ * x_expanded has moe_route_padded_rows rows, its padding rows are not
+ * written).  As in moe_route_expand, large batches copy in destination-row
+ * order from the route's row list.  The workspace must hold
+ * moe_route_workspace_bytes(T, E, k) bytes (16-byte aligned) whenever
+ * T > 64; for T <= 64 it may be NULL.  Layouts, limits, alignment and errors:
+ * the union of moe_route_padded's and moe_expand_rows'. */
+moe_status moe_route_expand_padded(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                                   int32_t pad_to, const uint16_t* x, int32_t H, int32_t* topk_ids,
+                                   float* topk_weights, int32_t* expert_offsets, int32_t* expert_counts,
+                                   int32_t* dest_of_src, int32_t* src_of_dest, uint16_t* x_expanded,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------- SwiGLU */
 

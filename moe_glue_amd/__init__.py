@@ -123,6 +123,35 @@ def route_padded(logits, k: int, pad_to: int, bias=None, out: dict | None = None
     return out
 
 
+def route_expand_padded(logits, k: int, pad_to: int, x, bias=None, out: dict | None = None) -> dict:
+    """route_padded() and expand_rows() in one call; see moe_route_expand_padded
+    in include/moe_glue.h.  x_expanded has padded_rows() rows (padding rows
+    are not written)."""
+    torch = _torch()
+    _need_gpu("logits", logits, torch.float32, 2)
+    _need_gpu("x", x, torch.bfloat16, 2)
+    T, E = logits.shape
+    if x.shape[0] != T:
+        raise MoEGlueArgumentError(2, f"x has {x.shape[0]} rows, logits has T={T}")
+    H = x.shape[1]
+    if bias is not None:
+        _need_gpu("bias", bias, torch.float32, 1)
+    P = max(1, padded_rows(T, E, k, pad_to))
+    if out is None:
+        out = alloc_route_outputs(T, E, k, logits.device)
+        out["src_of_dest"] = torch.empty((P,), dtype=torch.int32, device=logits.device)
+    if out.get("x_expanded") is None:
+        out["x_expanded"] = torch.empty((P, H), dtype=torch.bfloat16, device=x.device)
+    ws = out["workspace"]
+    st = load().moe_route_expand_padded(_ptr(logits), _ptr(bias), T, E, k, pad_to, _ptr(x), H, _ptr(out["topk_ids"]),
+                                        _ptr(out["topk_weights"]), _ptr(out["expert_offsets"]),
+                                        _ptr(out.get("expert_counts")), _ptr(out["dest_of_src"]),
+                                        _ptr(out["src_of_dest"]), _ptr(out["x_expanded"]), _ptr(ws),
+                                        ws.numel() if ws is not None else 0, _stream(logits.device))
+    check(st, "moe_route_expand_padded")
+    return out
+
+
 def expand_rows(x, dest_of_src, k: int, out=None):
     """x_expanded[dest_of_src[t*k+j]] = x[t]; see moe_expand_rows in include/moe_glue.h."""
     torch = _torch()

@@ -244,6 +244,41 @@ moe_status moe_route_expand(const float* logits, const float* bias, int32_t T, i
                     "moe_route_expand launch (expand)");
 }
 
+moe_status moe_route_expand_padded(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                                   int32_t pad_to, const uint16_t* x, int32_t H, int32_t* topk_ids,
+                                   float* topk_weights, int32_t* expert_offsets, int32_t* expert_counts,
+                                   int32_t* dest_of_src, int32_t* src_of_dest, uint16_t* x_expanded,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "moe_route_expand_padded";
+    moe_status s = check_route_args(fn, logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, dest_of_src,
+                                    src_of_dest);
+    if (s != MOE_OK) return s;
+    s = check_pad(fn, T, E, k, pad_to);
+    if (s != MOE_OK) return s;
+    s = check_expand_args(fn, x, dest_of_src, T, H, k, x_expanded);
+    if (s != MOE_OK) return s;
+    const moe::RouteVariant v = moe::route_pick_variant(T, E, requested_route_variant());
+    s = check_route_workspace(fn, T, E, k, true, v, workspace, workspace_bytes);
+    if (s != MOE_OK) return s;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    moe::RouteArgs a{logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, expert_counts,
+                     dest_of_src, src_of_dest, workspace, pad_to, /*row_list=*/nullptr, {}};
+    // the row list holds the real rows only, so the grouped copy leaves the
+    // padding rows untouched exactly as moe_expand_rows does
+    const bool grouped = v != moe::RouteVariant::SingleWorkgroup && T > 0 && use_grouped_expand(T, H, k);
+    if (grouped) {
+        a.row_list = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + moe::route_histogram_bytes(T, E));
+        a.groups = moe::route_row_groups(T, E, H);
+    }
+    s = from_hip(moe::launch_route(a, v, st), "moe_route_expand_padded launch (route)");
+    if (s != MOE_OK || T == 0) return s;
+    if (grouped)
+        return from_hip(moe::launch_expand_grouped(x, a.row_list, a.groups, H, k, x_expanded, st),
+                        "moe_route_expand_padded launch (expand)");
+    return from_hip(moe::launch_expand_rows(x, dest_of_src, T, H, k, x_expanded, st),
+                    "moe_route_expand_padded launch (expand)");
+}
+
 moe_status moe_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, int32_t T, int32_t H, int32_t k,
                                int32_t group, uint8_t* x_expanded, float* scales, void* stream) {
     const char* fn = "moe_expand_rows_fp8";

@@ -197,6 +197,22 @@ def test_route_padded_argument_errors(lib):
     assert lib.moe_route_padded_rows(10, 4, 2, 0) == 0
 
 
+def test_route_expand_padded_argument_errors(lib):
+    def call(T=4, E=8, k=2, pad=16, x=FAKE, H=256, xe=FAKE, ws=None, wsb=0):
+        return status(lib, lib.moe_route_expand_padded(FAKE, None, T, E, k, pad, x, H, FAKE, FAKE, FAKE, None, FAKE,
+                                                       FAKE, xe, ws, wsb, None))
+
+    assert call(pad=0) == "MOE_ERR_SHAPE"
+    assert call(pad=4097) == "MOE_ERR_UNSUPPORTED"
+    assert call(k=9) == "MOE_ERR_SHAPE"
+    assert call(x=None) == "MOE_ERR_NULL"
+    assert call(H=12) == "MOE_ERR_ALIGN"
+    assert call(T=65) == "MOE_ERR_WORKSPACE"
+    need = lib.moe_route_workspace_bytes(4096, 128, 8)
+    assert call(T=4096, E=128, k=8, H=2048, ws=FAKE, wsb=need - 1) == "MOE_ERR_WORKSPACE"
+    assert b"moe_route_expand_padded" in lib.moe_last_error()
+
+
 def test_expand_fp8_argument_errors(lib):
     def call(x=FAKE, d=FAKE, T=4, H=256, k=2, group=128, q=FAKE, sc=FAKE):
         return status(lib, lib.moe_expand_rows_fp8(x, d, T, H, k, group, q, sc, None))

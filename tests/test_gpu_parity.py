@@ -364,6 +364,39 @@ def test_expand_combine_on_padded_layout(dev, oracle_lib, T, E, k, M, H):
                               "combine on padded y")
 
 
+@pytest.mark.parametrize("order", ["auto", "grouped", "token"])
+@pytest.mark.parametrize("T,E,k,M,H", [(20, 8, 2, 16, 256), (300, 128, 8, 128, 2048), (77, 17, 5, 16, 520),
+                                       (1023, 64, 6, 64, 4096), (4096, 128, 8, 128, 2048), (2000, 256, 8, 3, 264)])
+def test_route_expand_padded_matches_oracle(dev, oracle_lib, monkeypatch, order, T, E, k, M, H):
+    """moe_route_expand_padded: the padded maps, every real row copied, the
+    padding rows untouched (sentinel), in every expand order."""
+    import torch
+    import moe_glue_amd as mg
+
+    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", order)
+    _log(f"[route_expand_padded] T={T} E={E} k={k} pad_to={M} H={H} order={order}")
+    cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8, bias_std=0.5 if E % 2 == 0 else 0.0)
+    inp = inputs.make_inputs(cfg, 14, parts=("x", "logits"))
+    ref = oracle_lib.route_padded(inp["logits"], k, M, inp["bias"])
+    P = int(ref["expert_offsets"][E])
+    rows = mg.padded_rows(T, E, k, M)
+    out = mg.alloc_route_outputs(T, E, k, dev)
+    out["src_of_dest"] = torch.empty((rows,), dtype=torch.int32, device=dev)
+    sentinel = 0x7F7F
+    out["x_expanded"] = torch.full((rows, H), sentinel, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    bias = None if inp["bias"] is None else G.to_dev(inp["bias"], dev)
+    r = mg.route_expand_padded(G.to_dev(inp["logits"], dev), k, M, G.to_dev(inp["x"], dev), bias, out=out)
+    torch.cuda.synchronize()
+    got = G.route_host(r)
+    got["src_of_dest"] = got["src_of_dest"][:P]
+    xe = got.pop("x_expanded")[:P]
+    compare.assert_route_equal(got, ref, f"route_expand_padded T={T} E={E} k={k} M={M}")
+    want = oracle_lib.expand_rows(inp["x"], ref["dest_of_src"], k, rows=P)
+    pad_rows = ref["src_of_dest"] < 0
+    compare.assert_equal(xe[~pad_rows], want[~pad_rows], "padded x_expanded (real rows)")
+    assert np.all(xe[pad_rows] == sentinel), "the fused call wrote into padding rows"
+
+
 # ------------------------------------------------------------------ FP8 quantising expand
 @pytest.mark.parametrize("T,H,E,k,group", [(1, 8, 4, 1, 8), (17, 256, 8, 2, 32), (300, 2048, 128, 8, 128),
                                            (77, 520, 17, 5, 8), (65, 4096, 64, 16, 512), (33, 7168, 256, 8, 128),
