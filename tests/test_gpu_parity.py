@@ -268,6 +268,33 @@ def test_route_expand_matches_oracle(dev, oracle_lib, monkeypatch, order, T, E, 
     compare.assert_equal(got["x_expanded"], oracle_lib.expand_rows(inp["x"], ref["dest_of_src"], k), "x_expanded")
 
 
+@pytest.mark.parametrize("variant", ["two", "three"])
+def test_route_expand_workspace_needs_no_initialisation(dev, oracle_lib, monkeypatch, variant):
+    """The workspace (histogram rows and row list) may hold anything: fill it
+    with 0xFF bytes, then with zeros, and get the same results both times."""
+    import torch
+    import moe_glue_amd as mg
+
+    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
+    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", "grouped")
+    T, E, k, H = 1500, 96, 6, 256
+    _log(f"[route_expand] garbage workspace T={T} E={E} k={k} variant={variant}")
+    cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
+    inp = inputs.make_inputs(cfg, 15, parts=("x", "logits"))
+    logits, x = G.to_dev(inp["logits"], dev), G.to_dev(inp["x"], dev)
+    results = []
+    for fill in (0xFF, 0x00):
+        out = mg.alloc_route_outputs(T, E, k, dev)
+        out["workspace"].fill_(fill)
+        results.append(G.route_host(mg.route_expand(logits, k, x, out=out)))
+    torch.cuda.synchronize()
+    ref = oracle_lib.route(inp["logits"], k)
+    for got in results:
+        compare.assert_route_equal(got, ref, f"route_expand garbage workspace ({variant})")
+        compare.assert_equal(got["x_expanded"], oracle_lib.expand_rows(inp["x"], ref["dest_of_src"], k),
+                             "x_expanded")
+
+
 @pytest.mark.parametrize("variant", ["auto", "two", "three"])
 @pytest.mark.parametrize("T,E,k,H", [(70000, 64, 2, 64), (65535, 8, 2, 16), (20000, 512, 16, 8)])
 def test_route_expand_large_batches(dev, oracle_lib, monkeypatch, variant, T, E, k, H):
