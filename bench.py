@@ -14,6 +14,8 @@ the 256 MiB Infinity Cache left behind by the previous step on the same set.
 Prints ONE JSON line: whole-job tokens/s, per-call device times from HIP
 events recorded on the launch stream inside the timed region, the roofline of
 the dominant kernel, and the CPU oracle timed on the host as a baseline.
+`value` and ms_per_step come from eager calls (each pays the host's launch
+cost); ms_per_step_graph is the same steps replayed from a HIP graph.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 """
@@ -198,14 +200,16 @@ class Sets:
         else:
             self.calls = ["route_expand_padded", "swiglu", "combine"]
 
-    def step(self, s, events=None):
+    def step(self, s, events=None, stream=None):
+        """One pass of the path over input set s % nsets; `stream` (a raw
+        hipStream_t) replaces the stream the argument tuples were built with."""
         a = self.sets[s % len(self.sets)]["args"]
         f = self.fns
         rc = 0
         if events is not None:
             events[0].record()
         for i, name in enumerate(self.calls):
-            rc |= f[name](*a[name])
+            rc |= f[name](*(a[name] if stream is None else a[name][:-1] + (stream,)))
             if events is not None:
                 events[i + 1].record()
         if rc:
@@ -268,6 +272,34 @@ def launch_floor_us(dev, n=100):
         return None
 
 
+def graph_ms_per_step(sets, dev, steps):
+    """Device time per step with the host's launch cost taken out: one pass
+    over every input set captured in a HIP graph on a side stream, replayed
+    back to back for about `steps` steps.  None if capture fails."""
+    import torch
+
+    try:
+        side = torch.cuda.Stream(device=dev)
+        n = len(sets.sets)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for s in range(n):
+                sets.step(s, stream=side.cuda_stream)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // n)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        return round(1e3 * (time.perf_counter() - t0) / (reps * n), 4)
+    except Exception as ex:  # capture unsupported: report nothing rather than a wrong time
+        print(f"bench.py: graph replay not measured ({type(ex).__name__}: {ex})", file=sys.stderr)
+        return None
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -309,6 +341,8 @@ def main(argv=None):
     ap.add_argument("--fp8-group", type=int, default=0,
                     help="expand with FP8 E4M3 quantisation, one scale per this many columns (0: bf16 expand)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="skip the HIP-graph replay timing (ms_per_step_graph)")
     ap.add_argument("--events", choices=["nofence", "torch", "none"], default="nofence",
                     help="per-call HIP events inside the timed region (default: without the system fence)")
     args = ap.parse_args(argv)
@@ -364,6 +398,10 @@ def main(argv=None):
         torch.cuda.synchronize()
         events_elapsed = time.perf_counter() - t1
 
+    # Timed region 3: the same steps replayed from a HIP graph (no per-call
+    # host cost) -> ms_per_step_graph, reported beside the eager figure.
+    graph_ms = graph_ms_per_step(sets, dev, args.steps) if args.graph else None
+
     ab = algorithmic_bytes(cfg, args.fp8_group)
     kernels = {}
     if use_events:
@@ -407,6 +445,7 @@ def main(argv=None):
         "host_us_per_step": round(1e6 * host_s / args.steps, 2),
         "events": args.events,
         "ms_per_step_with_events": None if events_elapsed is None else round(1e3 * events_elapsed / args.steps, 4),
+        "ms_per_step_graph": graph_ms,
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": None,

@@ -12,19 +12,27 @@
 // (top-k, bitmaps, scan, destinations), then copies its own share of the
 // rows.  Workgroup 0 also writes the routing outputs.  Each workgroup issues
 // the loads of its rows first, so their latency hides behind the routing.
+// A block of columns (one 16-byte vector per lane) is shared by `ks`
+// workgroups, each storing every ks-th of the k destination rows: at decode
+// sizes the column blocks alone would leave a handful of CUs issuing all the
+// stores, and routing once more per workgroup costs less than that.
 #include "route_common.h"
+
+#include <algorithm>
 
 namespace moe {
 namespace {
 
 using namespace route_detail;
 
+constexpr uint32_t kSmallDispatchWorkgroups = 64;
+
 template <int G, int V>
 __global__ __launch_bounds__((SingleShape<G>::THREADS)) void route_expand_small_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ expert_counts, int32_t* __restrict__ dest_of_src, int32_t* __restrict__ src_of_dest,
-    const u32x4* __restrict__ x, uint32_t H16, FastDiv div_h16, u32x4* __restrict__ x_exp) {
+    const u32x4* __restrict__ x, uint32_t H16, FastDiv div_h16, int ks, u32x4* __restrict__ x_exp) {
     using S = SingleShape<G>;
     __shared__ int32_t ids_lds[kRouteSmallDispatchMaxTokens * kKMax];
     __shared__ unsigned long long masks[kEMax];
@@ -34,7 +42,8 @@ __global__ __launch_bounds__((SingleShape<G>::THREADS)) void route_expand_small_
 
     // this workgroup's item of x (one 16-byte vector per lane), loaded first
     const uint32_t n = (uint32_t)T * H16;
-    const uint32_t i = blockIdx.x * S::THREADS + threadIdx.x;
+    const int js = (int)(blockIdx.x % (uint32_t)ks);  // first of this workgroup's destination slots j
+    const uint32_t i = (blockIdx.x / (uint32_t)ks) * S::THREADS + threadIdx.x;
     u32x4 v = {0u, 0u, 0u, 0u};
     if (i < n) v = load_stream(x + i);
 
@@ -55,7 +64,7 @@ __global__ __launch_bounds__((SingleShape<G>::THREADS)) void route_expand_small_
     if (i < n) {
         const uint32_t t = fastdiv(i, div_h16);
         const uint32_t c = i - t * H16;
-        for (int j = 0; j < k; ++j) store_stream(x_exp + (size_t)s_dest[t * k + j] * H16 + c, v);
+        for (int j = js; j < k; j += ks) store_stream(x_exp + (size_t)s_dest[t * k + j] * H16 + c, v);
     }
 }
 
@@ -65,9 +74,12 @@ hipError_t launch_gv(const RouteArgs& a, const void* x, int H, void* x_expanded,
     const uint32_t H16 = (uint32_t)H / 8;
     const uint32_t n = (uint32_t)a.T * H16;
     const uint32_t blocks = n == 0 ? 1 : (n + S::THREADS - 1) / S::THREADS;
-    route_expand_small_kernel<G, V><<<blocks, S::THREADS, 0, stream>>>(
+    // split the k destination rows until about kSmallDispatchWorkgroups workgroups store
+    const uint32_t want = (kSmallDispatchWorkgroups + blocks - 1) / blocks;
+    const int ks = (int)std::min<uint32_t>((uint32_t)a.k, std::max<uint32_t>(1u, want));
+    route_expand_small_kernel<G, V><<<blocks * ks, S::THREADS, 0, stream>>>(
         a.logits, a.bias, a.T, a.E, a.k, a.topk_ids, a.topk_weights, a.expert_offsets, a.expert_counts,
-        a.dest_of_src, a.src_of_dest, static_cast<const u32x4*>(x), H16, make_fastdiv(H16),
+        a.dest_of_src, a.src_of_dest, static_cast<const u32x4*>(x), H16, make_fastdiv(H16), ks,
         static_cast<u32x4*>(x_expanded));
     return hipGetLastError();
 }

@@ -465,3 +465,57 @@ def test_expand_fp8_qwen_workload_and_padded_layout(dev, oracle_lib):
     compare.assert_equal(qh[valid], qr[valid], "fp8 codes (valid rows)")
     compare.assert_equal(sch[valid], scr[valid], "fp8 scales (valid rows)")
     assert np.all(qh[~valid] == 0xAB), "fp8 expand wrote into padding rows"
+
+
+@pytest.mark.parametrize("T,E,k,H,I,variant,order", [(32, 128, 8, 2048, 768, "auto", "auto"),
+                                                     (700, 64, 6, 256, 64, "two", "grouped"),
+                                                     (300, 128, 8, 512, 32, "three", "token")])
+def test_graph_replay_matches_eager(dev, monkeypatch, T, E, k, H, I, variant, order):
+    """route_expand, swiglu and combine captured in one HIP graph: every replay
+    (outputs overwritten with garbage by eager work in between) gives exactly
+    the eager results."""
+    import torch
+    import moe_glue_amd as mg
+
+    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
+    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", order)
+    _log(f"[graph] T={T} E={E} k={k} H={H} I={I} variant={variant} order={order}")
+    cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=I)
+    inp = inputs.make_inputs(cfg, 21, parts=("x", "logits", "h", "y"))
+    logits, x = G.to_dev(inp["logits"], dev), G.to_dev(inp["x"], dev)
+    h, y = G.to_dev(inp["h"], dev), G.to_dev(inp["y"], dev)
+
+    def run(out, act, comb):
+        mg.route_expand(logits, k, x, out=out)
+        mg.swiglu(h, out=act)
+        mg.combine(y, out["topk_weights"], out["dest_of_src"], out=comb)
+
+    def alloc():
+        out = mg.alloc_route_outputs(T, E, k, dev)
+        out["x_expanded"] = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+        return out, torch.empty((T * k, I), dtype=torch.bfloat16, device=dev), \
+            torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    ref = alloc()
+    run(*ref)
+    torch.cuda.synchronize()
+    want = {key: G.to_host(v) for key, v in ref[0].items() if key != "workspace"}
+    want["act"], want["out"] = G.to_host(ref[1]), G.to_host(ref[2])
+
+    bufs = alloc()
+    side = torch.cuda.Stream(device=dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        run(*bufs)
+    for rep in range(3):
+        for key, v in bufs[0].items():
+            v.view(torch.uint8).fill_(0xA5 + rep)
+        bufs[1].view(torch.uint8).fill_(0x5A)
+        bufs[2].view(torch.uint8).fill_(0x3C)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = {key: G.to_host(v) for key, v in bufs[0].items() if key != "workspace"}
+        got["act"], got["out"] = G.to_host(bufs[1]), G.to_host(bufs[2])
+        for key in want:
+            compare.assert_equal(got[key], want[key], f"graph replay {rep}: {key}")
