@@ -166,7 +166,7 @@ def test_skewed_tie_rows(dev, oracle_lib):
 
 # ------------------------------------------------------------------ expand / combine
 @pytest.mark.parametrize("T,H,E,k", [(1, 8, 4, 1), (3, 8, 4, 4), (77, 520, 17, 5), (300, 2048, 128, 8),
-                                     (65, 4096, 64, 16), (513, 264, 8, 2)])
+                                     (65, 4096, 64, 16), (513, 264, 8, 2), (50, 32768, 16, 4)])
 def test_expand_combine_shapes(dev, oracle_lib, T, H, E, k):
     cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
     _log(f"[rows] T={T} H={H} E={E} k={k}")
@@ -232,7 +232,7 @@ def test_swiglu_every_finite_bf16_gate(dev, oracle_lib):
         compare.assert_bf16_close(got, oracle_lib.swiglu(h), f"swiglu u={u_bits:#06x}")
 
 
-@pytest.mark.parametrize("R,I", [(1, 8), (3, 16), (257, 768), (1023, 1408), (64, 2048), (7, 2056)])
+@pytest.mark.parametrize("R,I", [(1, 8), (3, 16), (257, 768), (1023, 1408), (64, 2048), (7, 2056), (5, 16384)])
 def test_swiglu_shapes(dev, oracle_lib, R, I):
     import torch
     import moe_glue_amd as mg
@@ -249,7 +249,8 @@ def test_swiglu_shapes(dev, oracle_lib, R, I):
                                      (64, 256, 8, 7168), (64, 512, 16, 264), (33, 64, 6, 4096), (20, 3, 3, 520),
                                      (65, 128, 8, 2048), (300, 64, 6, 256), (100, 17, 5, 8), (777, 8, 2, 264),
                                      (1023, 64, 6, 4096), (2000, 256, 8, 7168), (130, 512, 16, 264),
-                                     (5000, 3, 3, 8), (4096, 128, 8, 2048), (9000, 300, 4, 64)])
+                                     (5000, 3, 3, 8), (4096, 128, 8, 2048), (9000, 300, 4, 64),
+                                     (40, 16, 4, 32768), (300, 16, 4, 32768)])
 @pytest.mark.parametrize("order", ["auto", "grouped", "token"])
 def test_route_expand_matches_oracle(dev, oracle_lib, monkeypatch, order, T, E, k, H):
     import torch
