@@ -7,7 +7,8 @@
  *   moe_swiglu       gated SiLU on the first grouped GEMM's output
  *   moe_combine      routing-weighted sum of each token's k expert outputs
  *   moe_route_expand route + expand (one launch for small decode batches,
- *                    destination-order copy above)
+ *                    the copy folded into the route's last launch for
+ *                    mid-size ones, destination-order copy for large ones)
  *   moe_route_padded route with expert segments padded to a row multiple
  *   moe_route_expand_padded  moe_route_padded + expand in one call
  *   moe_expand_rows_fp8  expand with FP8 (E4M3) quantisation per column group
@@ -71,8 +72,8 @@ typedef enum moe_status {
  * moe_route_expand need for (T, E, k); 0 is never returned for valid
  * arguments, and a negative/invalid argument gives 0.  (moe_route and
  * moe_route_padded use only the front part: the per-workgroup expert
- * histograms; moe_route_expand also keeps T*k row-list entries of 8 bytes
- * there.)  The workspace needs no initialisation and may be reused by later
+ * histograms; moe_route_expand also keeps T*k row-list entries of 8 bytes,
+ * or T*k slot ranks of 4 bytes, there.)  The workspace needs no initialisation and may be reused by later
  * calls on the same stream. */
 size_t moe_route_workspace_bytes(int32_t T, int32_t E, int32_t k);
 
@@ -173,7 +174,9 @@ moe_status moe_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, in
  * of the rows (the workspace is not touched and may be NULL).  For larger T
  * the route runs as in moe_route; when the expanded rows are large (about
  * 100 MB and up) it also lists them per token group in the workspace and the
- * copy runs in destination-row order from that list, else in token order.
+ * copy runs in destination-row order from that list, else in token order --
+ * on the two-launch route done by its second launch itself, which then keeps
+ * the slot ranks in the workspace instead of in dest_of_src.
  * The workspace must hold moe_route_workspace_bytes(T, E, k) bytes (16-byte
  * aligned) whenever T > 64.
  * Layouts, limits, alignment and errors: the union of moe_route's and
@@ -188,7 +191,7 @@ moe_status moe_route_expand(const float* logits, const float* bias, int32_t T, i
  * results on the same arguments (all outputs of both calls are written;
  * x_expanded has moe_route_padded_rows rows, its padding rows are not
  * written).  As in moe_route_expand, large batches copy in destination-row
- * order from the route's row list.  The workspace must hold
+ * order from the route's row list, mid-size ones in the route's last launch.  The workspace must hold
  * moe_route_workspace_bytes(T, E, k) bytes (16-byte aligned) whenever
  * T > 64; for T <= 64 it may be NULL.  Layouts, limits, alignment and errors:
  * the union of moe_route_padded's and moe_expand_rows'. */

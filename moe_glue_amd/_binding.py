@@ -48,6 +48,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"moe_glue HIP library not built: {path} is missing "
                            "(run python -m moe_glue_amd.build or __graft_entry__.build())")
+    # PyTorch ships its own HIP runtime under the same soname; load it first so
+    # that the library binds to that one runtime (the one that owns the device
+    # memory and streams handed in) rather than pulling in a second copy.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     lib.moe_route_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_route_workspace_bytes.argtypes = [_i32, _i32, _i32]

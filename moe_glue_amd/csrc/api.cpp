@@ -48,19 +48,29 @@ moe::RouteVariant requested_route_variant() {
     return moe::RouteVariant::Auto;
 }
 
-// Expand order of moe_route_expand above the one-launch size.  The grouped
-// (destination-order) copy saves about a sixth of the expand's time, but the
-// route then also builds the row list (about 2 us more on the histogram path);
-// measured on this part it pays from about 100 MB of expanded rows.
+// Expand of moe_route_expand above the one-launch size:
+//   Grouped  destination order from the route's row list (expand.hip); saves
+//            about a sixth of the expand's time, but the route then also
+//            builds the row list (about 2 us more on the histogram path);
+//            measured on this part it pays from about 100 MB of expanded rows;
+//   Fused    token order, copied by the route's scan+place launch itself
+//            (two-launch route only), one launch less;
+//   Token    token order, a launch of its own after the route.
 // Override for tests and measurements:
-// MOE_GLUE_EXPAND_ORDER = token | grouped | auto (anything else: auto).
+// MOE_GLUE_EXPAND_ORDER = token | fused | grouped | auto (anything else: auto).
 constexpr int64_t kGroupedExpandMinBytes = 96ll << 20;
 
-bool use_grouped_expand(int32_t T, int32_t H, int32_t k) {
-    const char* v = std::getenv("MOE_GLUE_EXPAND_ORDER");
-    if (v != nullptr && std::strcmp(v, "token") == 0) return false;
-    if (v != nullptr && std::strcmp(v, "grouped") == 0) return true;
-    return (int64_t)T * k * H * 2 >= kGroupedExpandMinBytes;
+enum class ExpandOrder { Token, Fused, Grouped };
+
+ExpandOrder expand_order(int32_t T, int32_t H, int32_t k, moe::RouteVariant v) {
+    const char* e = std::getenv("MOE_GLUE_EXPAND_ORDER");
+    const bool two = v == moe::RouteVariant::TwoPass;
+    if (v == moe::RouteVariant::SingleWorkgroup || T == 0) return ExpandOrder::Token;
+    if (e != nullptr && std::strcmp(e, "token") == 0) return ExpandOrder::Token;
+    if (e != nullptr && std::strcmp(e, "grouped") == 0) return ExpandOrder::Grouped;
+    if (e != nullptr && std::strcmp(e, "fused") == 0) return two ? ExpandOrder::Fused : ExpandOrder::Token;
+    if ((int64_t)T * k * H * 2 >= kGroupedExpandMinBytes) return ExpandOrder::Grouped;
+    return two ? ExpandOrder::Fused : ExpandOrder::Token;
 }
 
 moe_status check_route_sizes(int32_t T, int32_t E, int32_t k) {
@@ -228,16 +238,20 @@ moe_status moe_route_expand(const float* logits, const float* bias, int32_t T, i
     const moe::RouteVariant v = moe::route_pick_variant(T, E, requested);
     s = check_route_workspace("moe_route_expand", T, E, k, true, v, workspace, workspace_bytes);
     if (s != MOE_OK) return s;
-    // the multi-workgroup route also lists the rows per token group; the expand
-    // then runs in destination order (the single-workgroup route lists nothing)
-    const bool grouped = v != moe::RouteVariant::SingleWorkgroup && T > 0 && use_grouped_expand(T, H, k);
-    if (grouped) {
+    // the multi-workgroup route either lists the rows per token group for the
+    // destination-order expand, or copies them itself in token order
+    const ExpandOrder order = expand_order(T, H, k, v);
+    if (order == ExpandOrder::Grouped) {
         a.row_list = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + moe::route_histogram_bytes(T, E));
         a.groups = moe::route_row_groups(T, E, H);
+    } else if (order == ExpandOrder::Fused) {
+        a.copy_x = x;
+        a.copy_out = x_expanded;
+        a.copy_H = H;
     }
     s = from_hip(moe::launch_route(a, v, st), "moe_route_expand launch (route)");
-    if (s != MOE_OK || T == 0) return s;
-    if (grouped)
+    if (s != MOE_OK || T == 0 || order == ExpandOrder::Fused) return s;
+    if (order == ExpandOrder::Grouped)
         return from_hip(moe::launch_expand_grouped(x, a.row_list, a.groups, H, k, x_expanded, st),
                         "moe_route_expand launch (expand)");
     return from_hip(moe::launch_expand_rows(x, dest_of_src, T, H, k, x_expanded, st),
@@ -264,15 +278,20 @@ moe_status moe_route_expand_padded(const float* logits, const float* bias, int32
     moe::RouteArgs a{logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, expert_counts,
                      dest_of_src, src_of_dest, workspace, pad_to, /*row_list=*/nullptr, {}};
     // the row list holds the real rows only, so the grouped copy leaves the
-    // padding rows untouched exactly as moe_expand_rows does
-    const bool grouped = v != moe::RouteVariant::SingleWorkgroup && T > 0 && use_grouped_expand(T, H, k);
-    if (grouped) {
+    // padding rows untouched exactly as moe_expand_rows does; so does the
+    // token-order copy of the place step
+    const ExpandOrder order = expand_order(T, H, k, v);
+    if (order == ExpandOrder::Grouped) {
         a.row_list = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + moe::route_histogram_bytes(T, E));
         a.groups = moe::route_row_groups(T, E, H);
+    } else if (order == ExpandOrder::Fused) {
+        a.copy_x = x;
+        a.copy_out = x_expanded;
+        a.copy_H = H;
     }
     s = from_hip(moe::launch_route(a, v, st), "moe_route_expand_padded launch (route)");
-    if (s != MOE_OK || T == 0) return s;
-    if (grouped)
+    if (s != MOE_OK || T == 0 || order == ExpandOrder::Fused) return s;
+    if (order == ExpandOrder::Grouped)
         return from_hip(moe::launch_expand_grouped(x, a.row_list, a.groups, H, k, x_expanded, st),
                         "moe_route_expand_padded launch (expand)");
     return from_hip(moe::launch_expand_rows(x, dest_of_src, T, H, k, x_expanded, st),

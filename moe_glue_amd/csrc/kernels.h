@@ -77,6 +77,12 @@ struct RouteArgs {
     // token), group i at [tok(i)*k, tok(i+1)*k), each group in dest-row order.
     int32_t* row_list;
     RowGroups groups;
+    // When set (two-launch variant only, not with row_list): the place step
+    // also copies x [T, copy_H] bf16 to copy_out in token order (the expand),
+    // keeping the slot ranks in the workspace's row-list area meanwhile.
+    const void* copy_x;
+    void* copy_out;
+    int copy_H;
 };
 
 // Keys per lane (8 above 32 experts, else 4) and lanes that cooperate on one token.

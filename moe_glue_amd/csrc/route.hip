@@ -275,38 +275,65 @@ __device__ __forceinline__ uint32_t add_lanes(uint32_t v) {
     return p[0] + p[1];
 }
 
-template <bool LIST, int QP>
+// With COPY the same launch also expands the unit's token rows in token
+// order: the unit's kFusedRows*tok_per_row tokens times H/8 columns are cut
+// into `chunks` column slices of 2^cw_shift vectors (2048 items: two per
+// lane), one workgroup each.  Every workgroup of a unit repeats the unit's
+// scan+place (cheap: the histogram matrix is small on this path) and issues
+// its row loads before it; the first (`owner`) also writes the unit's route
+// outputs.  The slot ranks then come from `ranks`, a workspace array, since
+// the owner overwrites dest_of_src while its siblings may still read them.
+constexpr int kCopyItems = 2;  // row vectors per lane
+
+template <bool LIST, int QP, bool COPY>
 __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
     const u32x4* __restrict__ rows8, int nb, int tok_per_row, int T, int E, int k, int pad,
-    const int32_t* __restrict__ topk_ids, int32_t* __restrict__ dest_of_src, int32_t* __restrict__ src_of_dest,
-    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ expert_counts, RowGroups groups,
-    int2* __restrict__ row_list) {
+    const int32_t* __restrict__ topk_ids, const int32_t* ranks, int32_t* dest_of_src,
+    int32_t* __restrict__ src_of_dest, int32_t* __restrict__ expert_offsets, int32_t* __restrict__ expert_counts,
+    RowGroups groups, int2* __restrict__ row_list, const u32x4* __restrict__ x, u32x4* __restrict__ x_exp,
+    uint32_t H16, int cw_shift, uint32_t chunks) {
+    static_assert(!(LIST && COPY), "the fused copy runs in token order, without the row list");
     constexpr int NACC = LIST ? 4 : 2;
     __shared__ uint32_t part[NACC][kFusedWaves][kMaxRowVectors][8];
     __shared__ __attribute__((aligned(16))) uint8_t s_rows[kFusedRows][kEMax];
     __shared__ int32_t s_acc[NACC][kEMax];
     __shared__ int32_t s_off[kEMax + 1];
     __shared__ int32_t s_gcum[LIST ? kEMax + 1 : 1];
+    __shared__ int32_t s_dest[COPY ? kFusedRows * kChunk * kKMax : 1];
 
     constexpr int Qp = QP;                     // route_byte_row_vectors(E) <= 32
     constexpr int RP = kFusedThreads / Qp;     // row groups (>= 32)
     const int q = threadIdx.x % Qp;
     const int rg = threadIdx.x / Qp;
-    const int row0 = blockIdx.x * kFusedRows;
+    const int unit = COPY ? (int)(blockIdx.x / chunks) : (int)blockIdx.x;
+    const uint32_t chunk = COPY ? blockIdx.x % chunks : 0u;
+    const bool owner = chunk == 0;
+    const int row0 = unit * kFusedRows;
     const int tok0 = row0 * tok_per_row;
-    const int nslot = min(kFusedRows * tok_per_row, T - tok0) * k;
-    const int gj = LIST ? group_of_unit(groups, blockIdx.x) : 0;  // the token group of this workgroup
-    const int gfirst = LIST ? group_row(groups, gj) : 0;          // its rows [gfirst, gend)
+    const int ntok = min(kFusedRows * tok_per_row, T - tok0);
+    const int nslot = ntok * k;
+    const int gj = LIST ? group_of_unit(groups, unit) : 0;  // the token group of this workgroup
+    const int gfirst = LIST ? group_row(groups, gj) : 0;    // its rows [gfirst, gend)
     const int gend = LIST ? group_row(groups, gj + 1) : 0;
 
-    // every independent load first: the slots, then the histogram columns
+    // every independent load first: the row vectors to copy, the slots, then the histogram columns
+    u32x4 xv[COPY ? kCopyItems : 1];
+    if constexpr (COPY) {
+#pragma unroll
+        for (int m = 0; m < kCopyItems; ++m) {
+            const uint32_t item = threadIdx.x + m * kFusedThreads;
+            const int tl = (int)(item >> cw_shift);
+            const uint32_t col = (chunk << cw_shift) + (item & ((1u << cw_shift) - 1u));
+            if (tl < ntok && col < H16) xv[m] = load_stream(x + (size_t)(tok0 + tl) * H16 + col);
+        }
+    }
     int my_e[kFusedSlots], my_r[kFusedSlots];
 #pragma unroll
     for (int u = 0; u < kFusedSlots; ++u) {
         const int s = threadIdx.x + u * kFusedThreads;
         if (s < nslot) {
             my_e[u] = topk_ids[(size_t)tok0 * k + s];
-            my_r[u] = dest_of_src[(size_t)tok0 * k + s];
+            my_r[u] = ranks[(size_t)tok0 * k + s];
         }
     }
     // acc[a][2j] / acc[a][2j+1]: 16-bit sums of bytes (0,2) / (1,3) of word j,
@@ -373,7 +400,7 @@ __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
     wave_exclusive_scan(s_acc[0], s_off, E, pad, 0);
     if constexpr (LIST) wave_exclusive_scan(s_acc[2], s_gcum, E, 1, 1, s_acc[3]);  // the group's own counts
     __syncthreads();
-    if (blockIdx.x == 0) {
+    if (unit == 0 && owner) {
         for (int e = threadIdx.x; e <= E; e += kFusedThreads) expert_offsets[e] = s_off[e];
         if (expert_counts != nullptr)
             for (int e = threadIdx.x; e < E; e += kFusedThreads) expert_counts[e] = s_acc[0][e];
@@ -389,26 +416,51 @@ __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
             int before = s_acc[1][e] + my_r[u];  // earlier tokens that picked e
             for (int r2 = 0; r2 < r; ++r2) before += s_rows[r2][e];
             const int d = s_off[e] + before;
-            dest_of_src[gs] = d;
-            src_of_dest[d] = (int32_t)gs;
+            if (owner) {
+                dest_of_src[gs] = d;
+                src_of_dest[d] = (int32_t)gs;
+            }
+            if constexpr (COPY) s_dest[s] = d;
             if constexpr (LIST)  // earlier tokens of the group that picked e: its rows before row0, then own
                 row_list[(size_t)group_tok(groups, gj) * k + s_gcum[e] + s_acc[2][e] + (before - s_acc[1][e])] =
                     make_int2(d, tok0 + s / k);
+        }
+    }
+    if constexpr (COPY) {
+        __syncthreads();  // every destination of the unit is in s_dest
+#pragma unroll
+        for (int m = 0; m < kCopyItems; ++m) {
+            const uint32_t item = threadIdx.x + m * kFusedThreads;
+            const int tl = (int)(item >> cw_shift);
+            const uint32_t col = (chunk << cw_shift) + (item & ((1u << cw_shift) - 1u));
+            if (tl < ntok && col < H16)
+                for (int j = 0; j < k; ++j) store_stream(x_exp + (size_t)s_dest[tl * k + j] * H16 + col, xv[m]);
         }
     }
 }
 
 template <int QP>
 void launch_scan_place(bool list, int nwg, const u32x4* rows8, int nb, int tok_per_row, const RouteArgs& a,
-                       int2* row_list, hipStream_t stream) {
-    if (list)
-        route_scan_place_kernel<true, QP><<<nwg, kFusedThreads, 0, stream>>>(
-            rows8, nb, tok_per_row, a.T, a.E, a.k, a.pad_to, a.topk_ids, a.dest_of_src, a.src_of_dest,
-            a.expert_offsets, a.expert_counts, a.groups, row_list);
-    else
-        route_scan_place_kernel<false, QP><<<nwg, kFusedThreads, 0, stream>>>(
-            rows8, nb, tok_per_row, a.T, a.E, a.k, a.pad_to, a.topk_ids, a.dest_of_src, a.src_of_dest,
-            a.expert_offsets, a.expert_counts, a.groups, row_list);
+                       const int32_t* ranks, int2* row_list, hipStream_t stream) {
+    if (a.copy_out != nullptr) {
+        const uint32_t H16 = (uint32_t)a.copy_H / 8;
+        const int unit_tokens = kFusedRows * tok_per_row;  // 64, 128 or 256
+        int cw_shift = 0;
+        while ((unit_tokens << (cw_shift + 1)) <= kCopyItems * kFusedThreads) ++cw_shift;
+        const uint32_t chunks = (H16 + (1u << cw_shift) - 1) >> cw_shift;
+        route_scan_place_kernel<false, QP, true><<<nwg * chunks, kFusedThreads, 0, stream>>>(
+            rows8, nb, tok_per_row, a.T, a.E, a.k, a.pad_to, a.topk_ids, ranks, a.dest_of_src, a.src_of_dest,
+            a.expert_offsets, a.expert_counts, a.groups, row_list, static_cast<const u32x4*>(a.copy_x),
+            static_cast<u32x4*>(a.copy_out), H16, cw_shift, chunks);
+    } else if (list) {
+        route_scan_place_kernel<true, QP, false><<<nwg, kFusedThreads, 0, stream>>>(
+            rows8, nb, tok_per_row, a.T, a.E, a.k, a.pad_to, a.topk_ids, ranks, a.dest_of_src, a.src_of_dest,
+            a.expert_offsets, a.expert_counts, a.groups, row_list, nullptr, nullptr, 0, 0, 1);
+    } else {
+        route_scan_place_kernel<false, QP, false><<<nwg, kFusedThreads, 0, stream>>>(
+            rows8, nb, tok_per_row, a.T, a.E, a.k, a.pad_to, a.topk_ids, ranks, a.dest_of_src, a.src_of_dest,
+            a.expert_offsets, a.expert_counts, a.groups, row_list, nullptr, nullptr, 0, 0, 1);
+    }
 }
 
 template <int G, int V>
@@ -424,9 +476,15 @@ hipError_t launch_route_gv(const RouteArgs& a, RouteVariant v, hipStream_t strea
     const int Epad = route_padded_experts(a.E);
     int32_t* counts = static_cast<int32_t*>(a.workspace);
     int32_t* totals = counts + (size_t)nb * Epad;
+    // the slot ranks go to dest_of_src (finished in place), or with the fused
+    // copy to the row-list area of the workspace
+    const bool copy = v == RouteVariant::TwoPass && a.copy_out != nullptr;
+    int32_t* ranks = copy ? reinterpret_cast<int32_t*>(static_cast<char*>(a.workspace) +
+                                                        route_histogram_bytes(a.T, a.E))
+                          : a.dest_of_src;
     if (v == RouteVariant::TwoPass)
         route_topk_kernel<G, V, true><<<nb, S::THREADS, 0, stream>>>(a.logits, a.bias, a.T, a.E, a.k, a.topk_ids,
-                                                                     a.topk_weights, a.dest_of_src, counts);
+                                                                     a.topk_weights, ranks, counts);
     else
         route_topk_kernel<G, V, false><<<nb, S::THREADS, 0, stream>>>(a.logits, a.bias, a.T, a.E, a.k, a.topk_ids,
                                                                       a.topk_weights, a.dest_of_src, counts);
@@ -438,12 +496,12 @@ hipError_t launch_route_gv(const RouteArgs& a, RouteVariant v, hipStream_t strea
         const int nwg = (nb + kFusedRows - 1) / kFusedRows;
         const u32x4* rows8 = reinterpret_cast<const u32x4*>(counts);
         switch (route_byte_row_vectors(a.E)) {
-            case 1: launch_scan_place<1>(list, nwg, rows8, nb, S::TOK, a, row_list, stream); break;
-            case 2: launch_scan_place<2>(list, nwg, rows8, nb, S::TOK, a, row_list, stream); break;
-            case 4: launch_scan_place<4>(list, nwg, rows8, nb, S::TOK, a, row_list, stream); break;
-            case 8: launch_scan_place<8>(list, nwg, rows8, nb, S::TOK, a, row_list, stream); break;
-            case 16: launch_scan_place<16>(list, nwg, rows8, nb, S::TOK, a, row_list, stream); break;
-            default: launch_scan_place<32>(list, nwg, rows8, nb, S::TOK, a, row_list, stream); break;
+            case 1: launch_scan_place<1>(list, nwg, rows8, nb, S::TOK, a, ranks, row_list, stream); break;
+            case 2: launch_scan_place<2>(list, nwg, rows8, nb, S::TOK, a, ranks, row_list, stream); break;
+            case 4: launch_scan_place<4>(list, nwg, rows8, nb, S::TOK, a, ranks, row_list, stream); break;
+            case 8: launch_scan_place<8>(list, nwg, rows8, nb, S::TOK, a, ranks, row_list, stream); break;
+            case 16: launch_scan_place<16>(list, nwg, rows8, nb, S::TOK, a, ranks, row_list, stream); break;
+            default: launch_scan_place<32>(list, nwg, rows8, nb, S::TOK, a, ranks, row_list, stream); break;
         }
         return hipGetLastError();
     }

@@ -52,7 +52,7 @@ def test_workload_full_size(dev, oracle_lib, name):
     check_path(got, ref, cfg, name)
 
 
-@pytest.mark.parametrize("order", ["auto", "grouped"])
+@pytest.mark.parametrize("order", ["auto", "grouped", "fused"])
 @pytest.mark.parametrize("name", inputs.CONFIG_ORDER)
 def test_workload_full_size_route_expand(dev, oracle_lib, monkeypatch, name, order):
     """Route + expand as one moe_route_expand call at full size (the form the
@@ -251,7 +251,7 @@ def test_swiglu_shapes(dev, oracle_lib, R, I):
                                      (1023, 64, 6, 4096), (2000, 256, 8, 7168), (130, 512, 16, 264),
                                      (5000, 3, 3, 8), (4096, 128, 8, 2048), (9000, 300, 4, 64),
                                      (40, 16, 4, 32768), (300, 16, 4, 32768)])
-@pytest.mark.parametrize("order", ["auto", "grouped", "token"])
+@pytest.mark.parametrize("order", ["auto", "grouped", "token", "fused"])
 def test_route_expand_matches_oracle(dev, oracle_lib, monkeypatch, order, T, E, k, H):
     import torch
     import moe_glue_amd as mg
@@ -269,17 +269,19 @@ def test_route_expand_matches_oracle(dev, oracle_lib, monkeypatch, order, T, E, 
     compare.assert_equal(got["x_expanded"], oracle_lib.expand_rows(inp["x"], ref["dest_of_src"], k), "x_expanded")
 
 
+@pytest.mark.parametrize("order", ["grouped", "fused"])
 @pytest.mark.parametrize("variant", ["two", "three"])
-def test_route_expand_workspace_needs_no_initialisation(dev, oracle_lib, monkeypatch, variant):
-    """The workspace (histogram rows and row list) may hold anything: fill it
-    with 0xFF bytes, then with zeros, and get the same results both times."""
+def test_route_expand_workspace_needs_no_initialisation(dev, oracle_lib, monkeypatch, variant, order):
+    """The workspace (histogram rows, row list or slot ranks) may hold
+    anything: fill it with 0xFF bytes, then with zeros, and get the same
+    results both times."""
     import torch
     import moe_glue_amd as mg
 
     monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
-    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", "grouped")
+    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", order)
     T, E, k, H = 1500, 96, 6, 256
-    _log(f"[route_expand] garbage workspace T={T} E={E} k={k} variant={variant}")
+    _log(f"[route_expand] garbage workspace T={T} E={E} k={k} variant={variant} order={order}")
     cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
     inp = inputs.make_inputs(cfg, 15, parts=("x", "logits"))
     logits, x = G.to_dev(inp["logits"], dev), G.to_dev(inp["x"], dev)
@@ -296,18 +298,20 @@ def test_route_expand_workspace_needs_no_initialisation(dev, oracle_lib, monkeyp
                              "x_expanded")
 
 
+@pytest.mark.parametrize("order", ["grouped", "fused"])
 @pytest.mark.parametrize("variant", ["auto", "two", "three"])
 @pytest.mark.parametrize("T,E,k,H", [(70000, 64, 2, 64), (65535, 8, 2, 16), (20000, 512, 16, 8)])
-def test_route_expand_large_batches(dev, oracle_lib, monkeypatch, variant, T, E, k, H):
+def test_route_expand_large_batches(dev, oracle_lib, monkeypatch, variant, T, E, k, H, order):
     """Batches past the two-launch route's 2^16-token limit (a forced two-launch
     request falls back to three launches), many token groups, E = 512 with
-    k = 16; grouped destination order throughout."""
+    k = 16; grouped destination order, or the copy fused into the place step
+    (token order after three launches)."""
     import torch
     import moe_glue_amd as mg
 
     monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
-    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", "grouped")
-    _log(f"[route_expand] large T={T} E={E} k={k} H={H} variant={variant}")
+    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", order)
+    _log(f"[route_expand] large T={T} E={E} k={k} H={H} variant={variant} order={order}")
     cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
     inp = inputs.make_inputs(cfg, 13, parts=("x", "logits"))
     r = mg.route_expand(G.to_dev(inp["logits"], dev), k, G.to_dev(inp["x"], dev))
@@ -392,7 +396,7 @@ def test_expand_combine_on_padded_layout(dev, oracle_lib, T, E, k, M, H):
                               "combine on padded y")
 
 
-@pytest.mark.parametrize("order", ["auto", "grouped", "token"])
+@pytest.mark.parametrize("order", ["auto", "grouped", "token", "fused"])
 @pytest.mark.parametrize("T,E,k,M,H", [(20, 8, 2, 16, 256), (300, 128, 8, 128, 2048), (77, 17, 5, 16, 520),
                                        (1023, 64, 6, 64, 4096), (4096, 128, 8, 128, 2048), (2000, 256, 8, 3, 264)])
 def test_route_expand_padded_matches_oracle(dev, oracle_lib, monkeypatch, order, T, E, k, M, H):
@@ -470,7 +474,8 @@ def test_expand_fp8_qwen_workload_and_padded_layout(dev, oracle_lib):
 
 @pytest.mark.parametrize("T,E,k,H,I,variant,order", [(32, 128, 8, 2048, 768, "auto", "auto"),
                                                      (700, 64, 6, 256, 64, "two", "grouped"),
-                                                     (300, 128, 8, 512, 32, "three", "token")])
+                                                     (300, 128, 8, 512, 32, "three", "token"),
+                                                     (1023, 64, 6, 4096, 1408, "auto", "fused")])
 def test_graph_replay_matches_eager(dev, monkeypatch, T, E, k, H, I, variant, order):
     """route_expand, swiglu and combine captured in one HIP graph: every replay
     (outputs overwritten with garbage by eager work in between) gives exactly
