@@ -173,7 +173,7 @@ moe_status moe_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, in
  * in which every workgroup recomputes the routing in LDS and copies its share
  * of the rows (the workspace is not touched and may be NULL).  For larger T
  * the route runs as in moe_route; when the expanded rows are large (about
- * 100 MB and up) it also lists them per token group in the workspace and the
+ * 72 MB and up) it also lists them per token group in the workspace and the
  * copy runs in destination-row order from that list, else in token order --
  * on the two-launch route done by its second launch itself, which then keeps
  * the slot ranks in the workspace instead of in dest_of_src.

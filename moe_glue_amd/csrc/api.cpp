@@ -52,13 +52,14 @@ moe::RouteVariant requested_route_variant() {
 //   Grouped  destination order from the route's row list (expand.hip); saves
 //            about a sixth of the expand's time, but the route then also
 //            builds the row list (about 2 us more on the histogram path);
-//            measured on this part it pays from about 100 MB of expanded rows;
+//            measured on this part it pays from about 72 MB of expanded rows
+//            (at H = 2048 the two orders cross between 65 and 82 MB);
 //   Fused    token order, copied by the route's scan+place launch itself
 //            (two-launch route only), one launch less;
 //   Token    token order, a launch of its own after the route.
 // Override for tests and measurements:
 // MOE_GLUE_EXPAND_ORDER = token | fused | grouped | auto (anything else: auto).
-constexpr int64_t kGroupedExpandMinBytes = 96ll << 20;
+constexpr int64_t kGroupedExpandMinBytes = 72ll << 20;
 
 enum class ExpandOrder { Token, Fused, Grouped };
 
