@@ -311,21 +311,24 @@ def cpu_model() -> str:
     return "unknown CPU"
 
 
-def cpu_baseline(inp, passes=3):
-    """The CPU oracle as it stands, single-threaded, on the same workload."""
+def cpu_baseline(inp, budget_s=10.0, max_passes=60):
+    """The CPU oracle as it stands, single-threaded, on the same workload:
+    whole passes over the batch for about `budget_s` seconds of CPU work."""
     import oracle
 
     o = oracle.get()
+    t0 = time.perf_counter()
     o.path(inp)  # warm: page in, build
-    times = []
+    warm = time.perf_counter() - t0
+    passes = max(1, min(max_passes, int(budget_s / max(warm, 1e-3))))
+    t0 = time.perf_counter()
     for _ in range(passes):
-        t0 = time.perf_counter()
         o.path(inp)
-        times.append(time.perf_counter() - t0)
-    t = sum(times) / len(times)
+    total = time.perf_counter() - t0
+    t = total / passes
     return {"value": inp["cfg"].T / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"the full {inp['cfg'].name} batch (T={inp['cfg'].T}), route+expand+swiglu+combine, "
-                      f"mean of {passes} passes after one warm pass, single thread, {t:.3f} s per pass, "
+                      f"{passes} passes ({total:.1f} s) after one warm pass, single thread, {t:.3f} s per pass, "
                       f"{cpu_model()}, {os.cpu_count()} logical CPUs visible"}
 
 
