@@ -3,8 +3,8 @@
 One step = the whole path on one batch: moe_route_expand (route, then the
 expansion of the token rows) -> moe_swiglu -> moe_combine (the GEMM outputs
 are seeded stand-ins already in HBM).  With --pad the first call is
-moe_route_expand_padded; with --fp8-group the route and the quantising
-expand are separate calls.  The default workload is the Qwen3-30B-A3B-shaped prefill batch
+moe_route_expand_padded; with --fp8-group it is moe_route_expand_fp8 (the
+route and the quantising expand).  The default workload is the Qwen3-30B-A3B-shaped prefill batch
 (T=4096, H=2048, E=128, k=8, I=768).
 
 Inputs are resident in HBM before the timed region.  Steps rotate over
@@ -37,10 +37,11 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "moe_glue_amd", "csrc")
 # Source files each call's kernels are built from (a traffic figure is valid
 # only while these are unchanged).
-KERNEL_SOURCES = {"route": ("route.hip", "route_common.h"), "expand": ("expand.hip",), "expand_fp8": ("quant.hip",),
-                  "swiglu": ("swiglu.hip",), "combine": ("combine.hip",),
-                  "route_expand": ("route.hip", "route_common.h", "dispatch.hip", "expand.hip"),
-                  "route_expand_padded": ("route.hip", "route_common.h", "expand.hip")}
+KERNEL_SOURCES = {"route": ("route.hip", "route_common.h", "fp8_common.h"), "expand": ("expand.hip",),
+                  "expand_fp8": ("quant.hip", "fp8_common.h"), "swiglu": ("swiglu.hip",), "combine": ("combine.hip",),
+                  "route_expand": ("route.hip", "route_common.h", "fp8_common.h", "dispatch.hip", "expand.hip"),
+                  "route_expand_padded": ("route.hip", "route_common.h", "fp8_common.h", "expand.hip"),
+                  "route_expand_fp8": ("route.hip", "route_common.h", "fp8_common.h", "quant.hip")}
 
 
 def algorithmic_bytes(cfg, fp8_group: int = 0) -> dict:
@@ -52,7 +53,7 @@ def algorithmic_bytes(cfg, fp8_group: int = 0) -> dict:
     combine = R * H * 2 + R * 4 + R * 4 + T * H * 2
     expand_fp8 = T * H * 2 + R * 4 + R * H + (R * (H // fp8_group) * 4 if fp8_group else 0)
     return {"route": route, "expand": expand, "swiglu": swiglu, "combine": combine, "route_expand": route + expand,
-            "route_expand_padded": route + expand, "expand_fp8": expand_fp8}
+            "route_expand_padded": route + expand, "expand_fp8": expand_fp8, "route_expand_fp8": route + expand_fp8}
 
 
 def source_digest(kernel: str) -> str:
@@ -181,6 +182,10 @@ class Sets:
                 "expand": (p("x"), p("dest_of_src"), T, H, k, p("x_exp"), stream),
                 "expand_fp8": ((p("x"), p("dest_of_src"), T, H, k, fp8_group, p("x_exp"), p("x_scales"), stream)
                                if fp8_group else None),
+                "route_expand_fp8": ((p("logits"), p("bias"), T, E, k, pad_to, p("x"), H, fp8_group, p("topk_ids"),
+                                      p("topk_weights"), p("expert_offsets"), p("expert_counts"), p("dest_of_src"),
+                                      p("src_of_dest"), p("x_exp"), p("x_scales"), p("workspace"),
+                                      d["workspace"].numel(), stream) if fp8_group else None),
                 "swiglu": (p("h"), R, I, p("act"), stream),
                 "combine": (p("y"), p("topk_weights"), p("dest_of_src"), T, H, k, p("out"), stream),
             }
@@ -188,13 +193,14 @@ class Sets:
         self.fns = {"route": self.lib.moe_route if pad_to == 1 else self.lib.moe_route_padded,
                     "expand": self.lib.moe_expand_rows, "expand_fp8": self.lib.moe_expand_rows_fp8,
                     "route_expand": self.lib.moe_route_expand,
-                    "route_expand_padded": self.lib.moe_route_expand_padded, "swiglu": self.lib.moe_swiglu,
+                    "route_expand_padded": self.lib.moe_route_expand_padded,
+                    "route_expand_fp8": self.lib.moe_route_expand_fp8, "swiglu": self.lib.moe_swiglu,
                     "combine": self.lib.moe_combine}
-        # Route and expand run as one moe_route_expand(_padded) call (one
-        # launch for decode batches, destination-order expand above); the
-        # quantising expand has no fused form.
+        # Route and expand run as one moe_route_expand(_padded, _fp8) call
+        # (one launch for decode batches, destination-order expand for large
+        # ones, the copy in the route's place launch in between).
         if fp8_group:
-            self.calls = ["route", "expand_fp8", "swiglu", "combine"]
+            self.calls = ["route_expand_fp8", "swiglu", "combine"]
         elif pad_to == 1:
             self.calls = ["route_expand", "swiglu", "combine"]
         else:
@@ -418,7 +424,7 @@ def main(argv=None):
                           "traffic": measured_traffic(n, cfg.name)}
     # the roofline kernel: the longest call that is a single kernel (route and
     # route_expand launch several)
-    single = [n for n in names if n not in ("route", "route_expand", "route_expand_padded")]
+    single = [n for n in names if n not in ("route", "route_expand", "route_expand_padded", "route_expand_fp8")]
     dominant = max(single, key=lambda n: kernels[n]["us"]) if kernels else None
     roofline = None
     if kernels:

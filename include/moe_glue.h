@@ -12,6 +12,7 @@
  *   moe_route_padded route with expert segments padded to a row multiple
  *   moe_route_expand_padded  moe_route_padded + expand in one call
  *   moe_expand_rows_fp8  expand with FP8 (E4M3) quantisation per column group
+ *   moe_route_expand_fp8 moe_route_padded + moe_expand_rows_fp8 in one call
  *
  * The problem statement these calls follow:
  *   - "CuTeDSL at Perplexity" (Perplexity blog), section "Mixture of Experts
@@ -173,7 +174,7 @@ moe_status moe_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, in
  * in which every workgroup recomputes the routing in LDS and copies its share
  * of the rows (the workspace is not touched and may be NULL).  For larger T
  * the route runs as in moe_route; when the expanded rows are large (about
- * 72 MB and up) it also lists them per token group in the workspace and the
+ * 120 MB and up) it also lists them per token group in the workspace and the
  * copy runs in destination-row order from that list, else in token order --
  * on the two-launch route done by its second launch itself, which then keeps
  * the slot ranks in the workspace instead of in dest_of_src.
@@ -200,6 +201,22 @@ moe_status moe_route_expand_padded(const float* logits, const float* bias, int32
                                    float* topk_weights, int32_t* expert_offsets, int32_t* expert_counts,
                                    int32_t* dest_of_src, int32_t* src_of_dest, uint16_t* x_expanded,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_route_padded followed by moe_expand_rows_fp8, in one call: exactly their
+ * results on the same arguments (pad_to = 1: moe_route; all outputs of both
+ * calls are written; padding rows of x_expanded and scales are not written).
+ * On the two-launch route with H <= 16384 and at most ~20 MB of codes the
+ * quantising copy runs in the route's place launch; otherwise the route is
+ * followed by the quantising expand.
+ * The workspace must hold moe_route_workspace_bytes(T, E, k) bytes (16-byte
+ * aligned) whenever T > 64; for T <= 64 it may be NULL.  Layouts, limits,
+ * alignment and errors: the union of moe_route_padded's and
+ * moe_expand_rows_fp8's. */
+moe_status moe_route_expand_fp8(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                                int32_t pad_to, const uint16_t* x, int32_t H, int32_t group, int32_t* topk_ids,
+                                float* topk_weights, int32_t* expert_offsets, int32_t* expert_counts,
+                                int32_t* dest_of_src, int32_t* src_of_dest, uint8_t* x_expanded, float* scales,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------- SwiGLU */
 

@@ -52,16 +52,20 @@ moe::RouteVariant requested_route_variant() {
 //   Grouped  destination order from the route's row list (expand.hip); saves
 //            about a sixth of the expand's time, but the route then also
 //            builds the row list (about 2 us more on the histogram path);
-//            measured on this part it pays from about 72 MB of expanded rows
-//            (at H = 2048 the two orders cross between 65 and 82 MB);
+//            measured on this part against the copy in the place launch it
+//            pays from about 120 MB of expanded rows (H = 2048: fused ahead
+//            by ~0.8 us at 82-108 MB, grouped ahead by 1 us at 134 MB; wider
+//            rows favour the fused copy longer);
 //   Fused    token order, copied by the route's scan+place launch itself
 //            (two-launch route only), one launch less;
 //   Token    token order, a launch of its own after the route.
 // Override for tests and measurements:
 // MOE_GLUE_EXPAND_ORDER = token | fused | grouped | auto (anything else: auto).
-constexpr int64_t kGroupedExpandMinBytes = 72ll << 20;
+constexpr int64_t kGroupedExpandMinBytes = 120ll << 20;
 
 enum class ExpandOrder { Token, Fused, Grouped };
+
+constexpr int64_t kQuantisingFoldMaxBytes = 20ll << 20;  // E4M3 codes of moe_route_expand_fp8
 
 ExpandOrder expand_order(int32_t T, int32_t H, int32_t k, moe::RouteVariant v) {
     const char* e = std::getenv("MOE_GLUE_EXPAND_ORDER");
@@ -137,6 +141,22 @@ moe_status check_expand_args(const char* fn, const uint16_t* x, const int32_t* d
     if (!x || !dest_of_src || !x_expanded) return fail(MOE_ERR_NULL, "%s: NULL tensor pointer", fn);
     if (!aligned16(x) || !aligned16(x_expanded))
         return fail(MOE_ERR_ALIGN, "%s: x and x_expanded must be 16-byte aligned", fn);
+    return MOE_OK;
+}
+
+moe_status check_fp8_args(const char* fn, const uint16_t* x, const int32_t* dest_of_src, int32_t T, int32_t H,
+                          int32_t k, int32_t group, const uint8_t* x_expanded, const float* scales) {
+    moe_status s = check_rows(fn, T, H, "H");
+    if (s != MOE_OK) return s;
+    if (k < 1 || k > MOE_K_MAX) return fail(MOE_ERR_SHAPE, "%s: k=%d must be in [1, %d]", fn, k, MOE_K_MAX);
+    if ((int64_t)T * k >= INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "%s: T*k too large", fn);
+    if (group < 8 || group > 512 || (group & (group - 1)) != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: group=%d must be a power of two in [8, 512]", fn, group);
+    if (H % group != 0) return fail(MOE_ERR_SHAPE, "%s: H=%d is not a multiple of group=%d", fn, H, group);
+    if (T == 0) return ok();
+    if (!x || !dest_of_src || !x_expanded || !scales) return fail(MOE_ERR_NULL, "%s: NULL tensor pointer", fn);
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(x_expanded) & 7u) != 0 || !aligned4(scales))
+        return fail(MOE_ERR_ALIGN, "%s: x must be 16-byte, codes 8-byte and scales 4-byte aligned", fn);
     return MOE_OK;
 }
 
@@ -302,20 +322,56 @@ moe_status moe_route_expand_padded(const float* logits, const float* bias, int32
 moe_status moe_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, int32_t T, int32_t H, int32_t k,
                                int32_t group, uint8_t* x_expanded, float* scales, void* stream) {
     const char* fn = "moe_expand_rows_fp8";
-    moe_status s = check_rows(fn, T, H, "H");
-    if (s != MOE_OK) return s;
-    if (k < 1 || k > MOE_K_MAX) return fail(MOE_ERR_SHAPE, "%s: k=%d must be in [1, %d]", fn, k, MOE_K_MAX);
-    if ((int64_t)T * k >= INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "%s: T*k too large", fn);
-    if (group < 8 || group > 512 || (group & (group - 1)) != 0)
-        return fail(MOE_ERR_UNSUPPORTED, "%s: group=%d must be a power of two in [8, 512]", fn, group);
-    if (H % group != 0) return fail(MOE_ERR_SHAPE, "%s: H=%d is not a multiple of group=%d", fn, H, group);
-    if (T == 0) return ok();
-    if (!x || !dest_of_src || !x_expanded || !scales) return fail(MOE_ERR_NULL, "%s: NULL tensor pointer", fn);
-    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(x_expanded) & 7u) != 0 || !aligned4(scales))
-        return fail(MOE_ERR_ALIGN, "%s: x must be 16-byte, codes 8-byte and scales 4-byte aligned", fn);
+    moe_status s = check_fp8_args(fn, x, dest_of_src, T, H, k, group, x_expanded, scales);
+    if (s != MOE_OK || T == 0) return s;
     return from_hip(moe::launch_expand_rows_fp8(x, dest_of_src, T, H, k, group, x_expanded, scales,
                                                 static_cast<hipStream_t>(stream)),
                     "moe_expand_rows_fp8 launch");
+}
+
+moe_status moe_route_expand_fp8(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                                int32_t pad_to, const uint16_t* x, int32_t H, int32_t group, int32_t* topk_ids,
+                                float* topk_weights, int32_t* expert_offsets, int32_t* expert_counts,
+                                int32_t* dest_of_src, int32_t* src_of_dest, uint8_t* x_expanded, float* scales,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "moe_route_expand_fp8";
+    moe_status s = check_route_args(fn, logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, dest_of_src,
+                                    src_of_dest);
+    if (s != MOE_OK) return s;
+    s = check_pad(fn, T, E, k, pad_to);
+    if (s != MOE_OK) return s;
+    s = check_fp8_args(fn, x, dest_of_src, T, H, k, group, x_expanded, scales);
+    if (s != MOE_OK) return s;
+    const moe::RouteVariant v = moe::route_pick_variant(T, E, requested_route_variant());
+    s = check_route_workspace(fn, T, E, k, true, v, workspace, workspace_bytes);
+    if (s != MOE_OK) return s;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    moe::RouteArgs a{logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, expert_counts,
+                     dest_of_src, src_of_dest, workspace, pad_to, /*row_list=*/nullptr, {}};
+    // The quantising copy folds into the two-launch route's place step when
+    // one of its workgroups holds a whole row and the codes are small: measured
+    // at H = 2048, k = 8, group 128, folding saves 2-3 us up to 16 MB of codes
+    // (T = 1000) but costs 3 us at 33 MB and 9 us at 67 MB (the copy then runs
+    // well below the separate quantising expand's rate).
+    // MOE_GLUE_EXPAND_ORDER = token keeps the separate expand, = fused folds
+    // whenever possible (tests and measurements).
+    const char* e = std::getenv("MOE_GLUE_EXPAND_ORDER");
+    const bool forced_token = e != nullptr && std::strcmp(e, "token") == 0;
+    const bool forced_fold = e != nullptr && std::strcmp(e, "fused") == 0;
+    const bool small = (int64_t)T * k * H <= kQuantisingFoldMaxBytes;
+    const bool fold = v == moe::RouteVariant::TwoPass && T > 0 && H <= moe::route_quantising_place_max_h() &&
+                      !forced_token && (small || forced_fold);
+    if (fold) {
+        a.copy_x = x;
+        a.copy_out = x_expanded;
+        a.copy_H = H;
+        a.copy_group = group;
+        a.copy_scales = scales;
+    }
+    s = from_hip(moe::launch_route(a, v, st), "moe_route_expand_fp8 launch (route)");
+    if (s != MOE_OK || T == 0 || fold) return s;
+    return from_hip(moe::launch_expand_rows_fp8(x, dest_of_src, T, H, k, group, x_expanded, scales, st),
+                    "moe_route_expand_fp8 launch (expand)");
 }
 
 moe_status moe_swiglu(const uint16_t* h, int32_t R, int32_t I, uint16_t* act, void* stream) {

@@ -1,0 +1,60 @@
+// OCP E4M3 quantisation of 16-byte bf16 vectors, shared by the quantising
+// expand (quant.hip) and the route's place step when it copies the rows
+// itself (route.hip).  A scale group of `group` columns is group/8
+// consecutive lanes; its absolute maximum is a max over those lanes of the
+// fp32 bit patterns of |x| (order-preserving for non-negative values).  Then
+// scale = amax/448 and inv = 448/amax (IEEE fp32 divisions; 0 for an all-zero
+// group), the products x*inv are clamped to +-448 and converted two at a time
+// by v_cvt_pk_fp8_f32 (E4M3, nearest-even; the clamp makes it saturating).
+#pragma once
+
+#include "device_common.h"
+
+namespace moe {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+
+// Largest |f[e]| of the lane's 8 values, as fp32 bits.
+__device__ __forceinline__ uint32_t abs_max_bits8(const float (&f)[8]) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t b = __builtin_bit_cast(uint32_t, f[e]) & 0x7FFFFFFFu;
+        m = b > m ? b : m;
+    }
+    return m;
+}
+
+// The group maximum over gl = group/8 consecutive lanes (a power of two <= 64;
+// wave-uniform), by DPP/permlane reductions.
+__device__ __forceinline__ uint32_t group_abs_max(uint32_t m, int gl) {
+    switch (gl) {
+        case 1: return m;
+        case 2: return group_reduce<2, Op::Max>(m);
+        case 4: return group_reduce<4, Op::Max>(m);
+        case 8: return group_reduce<8, Op::Max>(m);
+        case 16: return group_reduce<16, Op::Max>(m);
+        case 32: return group_reduce<32, Op::Max>(m);
+        default: return group_reduce<64, Op::Max>(m);
+    }
+}
+
+__device__ __forceinline__ float e4m3_scale(float amax) { return amax / 448.0f; }
+__device__ __forceinline__ float e4m3_inverse_scale(float amax) { return amax > 0.0f ? 448.0f / amax : 0.0f; }
+
+// The 8 codes of f[0..7] times inv, in memory order.
+__device__ __forceinline__ u32x2 quantize8_e4m3(const float (&f)[8], float inv) {
+    u32x2 codes;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        int packed = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(f[4 * w] * inv), clamp448(f[4 * w + 1] * inv), 0, false);
+        packed = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(f[4 * w + 2] * inv), clamp448(f[4 * w + 3] * inv), packed,
+                                                 true);
+        codes[w] = (uint32_t)packed;
+    }
+    return codes;
+}
+
+}  // namespace moe

@@ -78,11 +78,15 @@ struct RouteArgs {
     int32_t* row_list;
     RowGroups groups;
     // When set (two-launch variant only, not with row_list): the place step
-    // also copies x [T, copy_H] bf16 to copy_out in token order (the expand),
-    // keeping the slot ranks in the workspace's row-list area meanwhile.
+    // also copies x [T, copy_H] bf16 to copy_out in token order (the expand;
+    // with copy_group > 0 quantised to E4M3 codes plus copy_scales, one scale
+    // per copy_group columns), keeping the slot ranks in the workspace's
+    // row-list area meanwhile.
     const void* copy_x;
     void* copy_out;
     int copy_H;
+    int copy_group;
+    float* copy_scales;
 };
 
 // Keys per lane (8 above 32 experts, else 4) and lanes that cooperate on one token.
@@ -90,6 +94,9 @@ int route_keys_per_lane(int E);
 int route_lanes_per_token(int E);
 // Tokens per workgroup of the multi-workgroup top-k (one workspace row each).
 int route_tokens_per_block(int E);
+// Widest row (H) whose FP8 quantising copy the place step can take on: one
+// workgroup holds at least one whole row.
+int route_quantising_place_max_h();
 // Experts padded to a multiple of 4 (one int4 per 4 experts in the workspace).
 inline int route_padded_experts(int E) { return (E + 3) & ~3; }
 // 16-byte vectors per byte histogram row (one count byte per expert): E/16

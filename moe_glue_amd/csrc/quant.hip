@@ -5,17 +5,13 @@
 // absolute maxima over small groups of elements).
 //
 // Same work items as the bf16 expand: one 16-byte vector (8 bf16) of one token
-// row per lane, token-major, so x is read once.  The `group` columns of a
-// scale group are group/8 consecutive lanes; their absolute maximum is a DPP /
-// permlane max over those lanes on the fp32 bit patterns of |x| (order-
-// preserving for non-negative values).  Then scale = amax/448 and
-// inv = 448/amax (IEEE fp32 divisions), the products x*inv are clamped to
-// +-448 and converted two at a time by v_cvt_pk_fp8_f32 (OCP E4M3,
-// nearest-even; the clamp makes it saturating).  The 8 codes (8 bytes) are
-// stored to each of the token's k expanded rows, and the group's first lane
-// stores its scale k times.  HBM traffic: T*H*2 read, R*H + R*(H/group)*4
-// written -- about 0.57x the bf16 expand at group 128.
+// row per lane, token-major, so x is read once.  The vector is quantised as in
+// fp8_common.h (group absolute maximum over group/8 lanes, OCP E4M3 codes);
+// the 8 codes (8 bytes) are stored to each of the token's k expanded rows, and
+// the group's first lane stores its scale k times.  HBM traffic: T*H*2 read,
+// R*H + R*(H/group)*4 written -- about 0.57x the bf16 expand at group 128.
 #include "device_common.h"
+#include "fp8_common.h"
 #include "kernels.h"
 
 namespace moe {
@@ -23,9 +19,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kKMax = 16;
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
 
 template <int GL, bool ROW_PER_WAVE>
 __global__ __launch_bounds__(kThreads) void expand_rows_fp8_kernel(const u32x4* __restrict__ x,
@@ -41,25 +34,11 @@ __global__ __launch_bounds__(kThreads) void expand_rows_fp8_kernel(const u32x4* 
     if (live) v = load_stream(x + i);
     float f[8];
     unpack8(v, f);
-    uint32_t amax_bits = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t b = __builtin_bit_cast(uint32_t, f[e]) & 0x7FFFFFFFu;
-        amax_bits = b > amax_bits ? b : amax_bits;
-    }
-    amax_bits = group_reduce<GL, Op::Max>(amax_bits);
+    const uint32_t amax_bits = group_reduce<GL, Op::Max>(abs_max_bits8(f));
     if (!live) return;
     const float amax = __builtin_bit_cast(float, amax_bits);
-    const float scale = amax / 448.0f;
-    const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
-    u32x2 codes;
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-        int packed = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(f[4 * w] * inv), clamp448(f[4 * w + 1] * inv), 0, false);
-        packed = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(f[4 * w + 2] * inv), clamp448(f[4 * w + 3] * inv), packed,
-                                                 true);
-        codes[w] = (uint32_t)packed;
-    }
+    const float scale = e4m3_scale(amax);
+    const u32x2 codes = quantize8_e4m3(f, e4m3_inverse_scale(amax));
     uint32_t t = fastdiv(i, div_h16);
     if constexpr (ROW_PER_WAVE) t = uniform(t);
     const uint32_t c = i - t * H16;

@@ -35,6 +35,7 @@
 // expert holding it, with two DPP/permlane reductions over the G lanes; the
 // lane that owns the winner retires it.  Each lane then computes only the
 // exponentials of the slots it writes, and one more reduction sums them.
+#include "fp8_common.h"
 #include "route_common.h"
 
 #include <algorithm>
@@ -275,38 +276,78 @@ __device__ __forceinline__ uint32_t add_lanes(uint32_t v) {
     return p[0] + p[1];
 }
 
-// With COPY the same launch also expands the unit's token rows in token
-// order: the unit's kFusedRows*tok_per_row tokens times H/8 columns are cut
-// into `chunks` column slices of 2^cw_shift vectors (2048 items: two per
-// lane), one workgroup each.  Every workgroup of a unit repeats the unit's
-// scan+place (cheap: the histogram matrix is small on this path) and issues
-// its row loads before it; the first (`owner`) also writes the unit's route
-// outputs.  The slot ranks then come from `ranks`, a workspace array, since
-// the owner overwrites dest_of_src while its siblings may still read them.
+// With a COPY mode the same launch also expands the unit's token rows in
+// token order (kCopyBf16: plain copy; kCopyFp8: quantised to E4M3 with one
+// scale per `group` columns, as moe_expand_rows_fp8 does).  The unit's
+// kFusedRows*tok_per_row tokens times H/8 columns are cut into `chunks`
+// slices of at most 2048 items (two per lane), one workgroup each:
+//   kCopyBf16  column slices of 2^cw_shift vectors across all the unit's
+//              tokens;
+//   kCopyFp8   row slices of tpw whole token rows, so that one workgroup
+//              writes all of an expanded row's scales.
+// Every workgroup of a unit repeats the unit's scan+place (cheap: the
+// histogram matrix is small on this path) and issues its row loads before
+// it; the first (`owner`) also writes the unit's route outputs.  The slot
+// ranks then come from `ranks`, a workspace array, since the owner
+// overwrites dest_of_src while its siblings may still read them.
+constexpr int kCopyNone = 0;
+constexpr int kCopyBf16 = 1;
+constexpr int kCopyFp8 = 2;
 constexpr int kCopyItems = 2;  // row vectors per lane
 
-template <bool LIST, int QP, bool COPY>
-__global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
+struct PlaceCopy {
+    const u32x4* x;
+    void* out;        // u32x4 rows (bf16) or u32x2 rows (E4M3 codes)
+    float* scales;    // kCopyFp8: [rows, G]
+    uint32_t H16;
+    uint32_t G;       // kCopyFp8: scale groups per row
+    int gl;           // kCopyFp8: lanes per scale group (group / 8)
+    int cw_shift;     // kCopyBf16: 2^cw_shift vectors per column slice
+    uint32_t tpw;     // kCopyFp8: token rows per slice (tpw * H16 <= 2048)
+    FastDiv div_h16;  // kCopyFp8
+    uint32_t chunks;  // slices per unit
+};
+
+// The unit-local token and the column of item `item` of slice `chunk`;
+// false if the slice has no such item.
+template <int COPY>
+__device__ __forceinline__ bool copy_item(const PlaceCopy& cp, uint32_t chunk, uint32_t item, int ntok, int& tl,
+                                          uint32_t& col) {
+    if constexpr (COPY == kCopyFp8) {
+        const uint32_t r = fastdiv(item, cp.div_h16);
+        col = item - r * cp.H16;
+        tl = (int)(chunk * cp.tpw + r);
+        return r < cp.tpw && tl < ntok;
+    } else {
+        tl = (int)(item >> cp.cw_shift);
+        col = (chunk << cp.cw_shift) + (item & ((1u << cp.cw_shift) - 1u));
+        return tl < ntok && col < cp.H16;
+    }
+}
+
+template <bool LIST, int QP, int COPY>
+__device__ __forceinline__ void scan_place(
     const u32x4* __restrict__ rows8, int nb, int tok_per_row, int T, int E, int k, int pad,
     const int32_t* __restrict__ topk_ids, const int32_t* ranks, int32_t* dest_of_src,
     int32_t* __restrict__ src_of_dest, int32_t* __restrict__ expert_offsets, int32_t* __restrict__ expert_counts,
-    RowGroups groups, int2* __restrict__ row_list, const u32x4* __restrict__ x, u32x4* __restrict__ x_exp,
-    uint32_t H16, int cw_shift, uint32_t chunks) {
-    static_assert(!(LIST && COPY), "the fused copy runs in token order, without the row list");
+    RowGroups groups, int2* __restrict__ row_list, const PlaceCopy& cp) {
+    static_assert(!(LIST && COPY != kCopyNone), "the fused copy runs in token order, without the row list");
+    const uint32_t chunks = COPY != kCopyNone ? cp.chunks : 1u;
+    const uint32_t H16 = cp.H16;
     constexpr int NACC = LIST ? 4 : 2;
     __shared__ uint32_t part[NACC][kFusedWaves][kMaxRowVectors][8];
     __shared__ __attribute__((aligned(16))) uint8_t s_rows[kFusedRows][kEMax];
     __shared__ int32_t s_acc[NACC][kEMax];
     __shared__ int32_t s_off[kEMax + 1];
     __shared__ int32_t s_gcum[LIST ? kEMax + 1 : 1];
-    __shared__ int32_t s_dest[COPY ? kFusedRows * kChunk * kKMax : 1];
+    __shared__ int32_t s_dest[COPY != kCopyNone ? kFusedRows * kChunk * kKMax : 1];
 
     constexpr int Qp = QP;                     // route_byte_row_vectors(E) <= 32
     constexpr int RP = kFusedThreads / Qp;     // row groups (>= 32)
     const int q = threadIdx.x % Qp;
     const int rg = threadIdx.x / Qp;
-    const int unit = COPY ? (int)(blockIdx.x / chunks) : (int)blockIdx.x;
-    const uint32_t chunk = COPY ? blockIdx.x % chunks : 0u;
+    const int unit = (int)(blockIdx.x / chunks);
+    const uint32_t chunk = blockIdx.x % chunks;
     const bool owner = chunk == 0;
     const int row0 = unit * kFusedRows;
     const int tok0 = row0 * tok_per_row;
@@ -317,14 +358,15 @@ __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
     const int gend = LIST ? group_row(groups, gj + 1) : 0;
 
     // every independent load first: the row vectors to copy, the slots, then the histogram columns
-    u32x4 xv[COPY ? kCopyItems : 1];
-    if constexpr (COPY) {
+    u32x4 xv[COPY != kCopyNone ? kCopyItems : 1];
+    if constexpr (COPY != kCopyNone) {
 #pragma unroll
         for (int m = 0; m < kCopyItems; ++m) {
-            const uint32_t item = threadIdx.x + m * kFusedThreads;
-            const int tl = (int)(item >> cw_shift);
-            const uint32_t col = (chunk << cw_shift) + (item & ((1u << cw_shift) - 1u));
-            if (tl < ntok && col < H16) xv[m] = load_stream(x + (size_t)(tok0 + tl) * H16 + col);
+            int tl;
+            uint32_t col;
+            xv[m] = (u32x4){0u, 0u, 0u, 0u};  // an absent item counts as zeros in a scale group
+            if (copy_item<COPY>(cp, chunk, threadIdx.x + m * kFusedThreads, ntok, tl, col))
+                xv[m] = load_stream(cp.x + (size_t)(tok0 + tl) * H16 + col);
         }
     }
     int my_e[kFusedSlots], my_r[kFusedSlots];
@@ -345,7 +387,8 @@ __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
     for (int a = 0; a < NACC; ++a)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[a][j] = 0;
-#pragma unroll 4
+    constexpr int kRowUnroll = COPY != kCopyNone ? 1 : 4;  // the copying form keeps registers for its rows
+#pragma unroll kRowUnroll
     for (int row = rg; row < nb; row += RP) {
         const u32x4 w = rows8[(size_t)row * Qp + q];
         if (row >= row0 && row < row0 + kFusedRows) *reinterpret_cast<u32x4*>(&s_rows[row - row0][q * 16]) = w;
@@ -420,46 +463,116 @@ __global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
                 dest_of_src[gs] = d;
                 src_of_dest[d] = (int32_t)gs;
             }
-            if constexpr (COPY) s_dest[s] = d;
+            if constexpr (COPY != kCopyNone) s_dest[s] = d;
             if constexpr (LIST)  // earlier tokens of the group that picked e: its rows before row0, then own
                 row_list[(size_t)group_tok(groups, gj) * k + s_gcum[e] + s_acc[2][e] + (before - s_acc[1][e])] =
                     make_int2(d, tok0 + s / k);
         }
     }
-    if constexpr (COPY) {
+    if constexpr (COPY == kCopyBf16) {
         __syncthreads();  // every destination of the unit is in s_dest
+        u32x4* x_exp = static_cast<u32x4*>(cp.out);
 #pragma unroll
         for (int m = 0; m < kCopyItems; ++m) {
-            const uint32_t item = threadIdx.x + m * kFusedThreads;
-            const int tl = (int)(item >> cw_shift);
-            const uint32_t col = (chunk << cw_shift) + (item & ((1u << cw_shift) - 1u));
-            if (tl < ntok && col < H16)
+            int tl;
+            uint32_t col;
+            if (copy_item<COPY>(cp, chunk, threadIdx.x + m * kFusedThreads, ntok, tl, col))
                 for (int j = 0; j < k; ++j) store_stream(x_exp + (size_t)s_dest[tl * k + j] * H16 + col, xv[m]);
         }
     }
+    if constexpr (COPY == kCopyFp8) {
+        // a scale group is gl consecutive lanes of one token row (gl divides
+        // H/8 and 64), present or absent as a whole
+        __syncthreads();
+        u32x2* q_out = static_cast<u32x2*>(cp.out);
+#pragma unroll
+        for (int m = 0; m < kCopyItems; ++m) {
+            int tl;
+            uint32_t col;
+            const bool present = copy_item<COPY>(cp, chunk, threadIdx.x + m * kFusedThreads, ntok, tl, col);
+            float f[8];
+            unpack8(xv[m], f);
+            const float amax = __builtin_bit_cast(float, group_abs_max(abs_max_bits8(f), cp.gl));
+            if (present) {
+                const float scale = e4m3_scale(amax);
+                const u32x2 codes = quantize8_e4m3(f, e4m3_inverse_scale(amax));
+                const bool first_of_group = (threadIdx.x % (uint32_t)cp.gl) == 0;
+                const uint32_t g = col / (uint32_t)cp.gl;
+                for (int j = 0; j < k; ++j) {
+                    const size_t d = (size_t)s_dest[tl * k + j];
+                    __builtin_nontemporal_store(codes, q_out + d * H16 + col);
+                    if (first_of_group) cp.scales[d * cp.G + g] = scale;
+                }
+            }
+        }
+    }
+}
+
+template <bool LIST, int QP>
+__global__ __launch_bounds__(kFusedThreads) void route_scan_place_kernel(
+    const u32x4* __restrict__ rows8, int nb, int tok_per_row, int T, int E, int k, int pad,
+    const int32_t* __restrict__ topk_ids, int32_t* dest_of_src, int32_t* __restrict__ src_of_dest,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ expert_counts, RowGroups groups,
+    int2* __restrict__ row_list) {
+    scan_place<LIST, QP, kCopyNone>(rows8, nb, tok_per_row, T, E, k, pad, topk_ids, dest_of_src, dest_of_src,
+                                    src_of_dest, expert_offsets, expert_counts, groups, row_list, PlaceCopy{});
+}
+
+// The copying form: two workgroups per CU (at most 64 VGPRs), so that a grid
+// of a few hundred workgroups runs in one round rather than two.
+template <int QP, int COPY>
+__global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void route_place_copy_kernel(
+    const u32x4* __restrict__ rows8, int nb, int tok_per_row, int T, int E, int k, int pad,
+    const int32_t* __restrict__ topk_ids, const int32_t* ranks, int32_t* dest_of_src,
+    int32_t* __restrict__ src_of_dest, int32_t* __restrict__ expert_offsets, int32_t* __restrict__ expert_counts,
+    PlaceCopy cp) {
+    scan_place<false, QP, COPY>(rows8, nb, tok_per_row, T, E, k, pad, topk_ids, ranks, dest_of_src, src_of_dest,
+                                expert_offsets, expert_counts, RowGroups{}, nullptr, cp);
+}
+
+// log2 of the column slice width (vectors) of the copying place step.
+int copy_slice_shift(int tok_per_row) {
+    const int unit_tokens = kFusedRows * tok_per_row;  // 64, 128 or 256
+    int cw_shift = 0;
+    while ((unit_tokens << (cw_shift + 1)) <= kCopyItems * kFusedThreads) ++cw_shift;
+    return cw_shift;
 }
 
 template <int QP>
 void launch_scan_place(bool list, int nwg, const u32x4* rows8, int nb, int tok_per_row, const RouteArgs& a,
                        const int32_t* ranks, int2* row_list, hipStream_t stream) {
+    PlaceCopy cp{};
+    cp.chunks = 1;
     if (a.copy_out != nullptr) {
-        const uint32_t H16 = (uint32_t)a.copy_H / 8;
-        const int unit_tokens = kFusedRows * tok_per_row;  // 64, 128 or 256
-        int cw_shift = 0;
-        while ((unit_tokens << (cw_shift + 1)) <= kCopyItems * kFusedThreads) ++cw_shift;
-        const uint32_t chunks = (H16 + (1u << cw_shift) - 1) >> cw_shift;
-        route_scan_place_kernel<false, QP, true><<<nwg * chunks, kFusedThreads, 0, stream>>>(
-            rows8, nb, tok_per_row, a.T, a.E, a.k, a.pad_to, a.topk_ids, ranks, a.dest_of_src, a.src_of_dest,
-            a.expert_offsets, a.expert_counts, a.groups, row_list, static_cast<const u32x4*>(a.copy_x),
-            static_cast<u32x4*>(a.copy_out), H16, cw_shift, chunks);
+        cp.x = static_cast<const u32x4*>(a.copy_x);
+        cp.out = a.copy_out;
+        cp.scales = a.copy_scales;
+        cp.H16 = (uint32_t)a.copy_H / 8;
+        cp.cw_shift = copy_slice_shift(tok_per_row);
+        cp.chunks = (cp.H16 + (1u << cp.cw_shift) - 1) >> cp.cw_shift;
+        if (a.copy_group > 0) {  // row slices (the caller checked H/8 <= 2048)
+            const uint32_t unit_tokens = (uint32_t)(kFusedRows * tok_per_row);
+            cp.gl = a.copy_group / 8;
+            cp.G = (uint32_t)(a.copy_H / a.copy_group);
+            cp.tpw = std::min<uint32_t>(unit_tokens, (uint32_t)(kCopyItems * kFusedThreads) / cp.H16);
+            cp.div_h16 = make_fastdiv(cp.H16);
+            cp.chunks = (unit_tokens + cp.tpw - 1) / cp.tpw;
+            route_place_copy_kernel<QP, kCopyFp8><<<nwg * cp.chunks, kFusedThreads, 0, stream>>>(
+                rows8, nb, tok_per_row, a.T, a.E, a.k, a.pad_to, a.topk_ids, ranks, a.dest_of_src, a.src_of_dest,
+                a.expert_offsets, a.expert_counts, cp);
+        } else {
+            route_place_copy_kernel<QP, kCopyBf16><<<nwg * cp.chunks, kFusedThreads, 0, stream>>>(
+                rows8, nb, tok_per_row, a.T, a.E, a.k, a.pad_to, a.topk_ids, ranks, a.dest_of_src, a.src_of_dest,
+                a.expert_offsets, a.expert_counts, cp);
+        }
     } else if (list) {
-        route_scan_place_kernel<true, QP, false><<<nwg, kFusedThreads, 0, stream>>>(
-            rows8, nb, tok_per_row, a.T, a.E, a.k, a.pad_to, a.topk_ids, ranks, a.dest_of_src, a.src_of_dest,
-            a.expert_offsets, a.expert_counts, a.groups, row_list, nullptr, nullptr, 0, 0, 1);
+        route_scan_place_kernel<true, QP><<<nwg, kFusedThreads, 0, stream>>>(
+            rows8, nb, tok_per_row, a.T, a.E, a.k, a.pad_to, a.topk_ids, a.dest_of_src, a.src_of_dest,
+            a.expert_offsets, a.expert_counts, a.groups, row_list);
     } else {
-        route_scan_place_kernel<false, QP, false><<<nwg, kFusedThreads, 0, stream>>>(
-            rows8, nb, tok_per_row, a.T, a.E, a.k, a.pad_to, a.topk_ids, ranks, a.dest_of_src, a.src_of_dest,
-            a.expert_offsets, a.expert_counts, a.groups, row_list, nullptr, nullptr, 0, 0, 1);
+        route_scan_place_kernel<false, QP><<<nwg, kFusedThreads, 0, stream>>>(
+            rows8, nb, tok_per_row, a.T, a.E, a.k, a.pad_to, a.topk_ids, a.dest_of_src, a.src_of_dest,
+            a.expert_offsets, a.expert_counts, a.groups, row_list);
     }
 }
 
@@ -530,6 +643,8 @@ int route_lanes_per_token(int E) {
     while (G < need) G <<= 1;
     return G;
 }
+
+int route_quantising_place_max_h() { return 8 * kCopyItems * kFusedThreads; }
 
 int route_tokens_per_block(int E) {
     const int G = route_lanes_per_token(E);

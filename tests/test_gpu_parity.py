@@ -472,6 +472,51 @@ def test_expand_fp8_qwen_workload_and_padded_layout(dev, oracle_lib):
     assert np.all(qh[~valid] == 0xAB), "fp8 expand wrote into padding rows"
 
 
+# T, E, k, H, group, pad_to; order auto folds the quantising copy into the
+# route's place step for small batches, token never, fused whenever possible
+FP8_FUSED_CASES = [(1, 8, 2, 256, 8, 1), (40, 64, 6, 512, 128, 1), (300, 128, 8, 2048, 128, 1),
+                   (300, 128, 8, 2048, 128, 128), (1023, 64, 6, 4096, 256, 1), (1023, 64, 6, 4096, 512, 16),
+                   (500, 8, 2, 1024, 128, 16), (500, 8, 2, 1024, 256, 1), (500, 4, 2, 512, 64, 1),
+                   (500, 4, 2, 512, 128, 3), (77, 17, 5, 520, 8, 16), (4096, 128, 8, 2048, 128, 1),
+                   (2000, 512, 16, 264, 8, 1)]
+
+
+@pytest.mark.parametrize("order", ["auto", "token", "fused"])
+@pytest.mark.parametrize("T,E,k,H,group,M", FP8_FUSED_CASES)
+def test_route_expand_fp8_matches_oracle(dev, oracle_lib, monkeypatch, order, T, E, k, H, group, M):
+    """moe_route_expand_fp8 = route (padded for M > 1) then the quantising
+    expand; padding rows of the codes and scales stay untouched."""
+    import torch
+    import moe_glue_amd as mg
+
+    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", order)
+    _log(f"[route_expand_fp8] T={T} E={E} k={k} H={H} group={group} pad_to={M} order={order}")
+    cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8, bias_std=0.5 if E % 2 == 0 else 0.0)
+    inp = inputs.make_inputs(cfg, 9, parts=("x", "logits"))
+    bias = None if inp["bias"] is None else G.to_dev(inp["bias"], dev)
+    P = mg.padded_rows(T, E, k, M) if M > 1 else T * k
+    out = mg.alloc_route_outputs(T, E, k, dev)
+    out["src_of_dest"] = torch.empty((P,), dtype=torch.int32, device=dev)
+    out["x_expanded"] = torch.full((P, H), 0xAB, dtype=torch.uint8, device=dev)
+    out["scales"] = torch.full((P, H // group), -7.0, dtype=torch.float32, device=dev)
+    r = mg.route_expand_fp8(G.to_dev(inp["logits"], dev), k, G.to_dev(inp["x"], dev), group, M, bias, out=out)
+    torch.cuda.synchronize()
+    got = G.route_host(r)
+    ref = (oracle_lib.route_padded(inp["logits"], k, M, inp["bias"]) if M > 1
+           else oracle_lib.route(inp["logits"], k, inp["bias"]))
+    n = int(ref["expert_offsets"][E])
+    got["src_of_dest"] = got["src_of_dest"][:n]
+    compare.assert_route_equal({key: v for key, v in got.items() if key not in ("x_expanded", "scales")}, ref,
+                               f"route_expand_fp8 T={T} E={E} k={k} M={M}")
+    qr, scr = oracle_lib.expand_rows_fp8(inp["x"], ref["dest_of_src"], k, group, rows=n)
+    valid = ref["src_of_dest"] >= 0
+    qh, sch = got["x_expanded"][:n], got["scales"][:n]
+    compare.assert_equal(qh[valid], qr[valid], "fp8 codes (valid rows)")
+    compare.assert_equal(sch[valid], scr[valid], "fp8 scales (valid rows)")
+    assert np.all(qh[~valid] == 0xAB) and np.all(got["x_expanded"][n:] == 0xAB), "codes written into padding rows"
+    assert np.all(sch[~valid] == -7.0) and np.all(got["scales"][n:] == -7.0), "scales written into padding rows"
+
+
 @pytest.mark.parametrize("T,E,k,H,I,variant,order", [(32, 128, 8, 2048, 768, "auto", "auto"),
                                                      (700, 64, 6, 256, 64, "two", "grouped"),
                                                      (300, 128, 8, 512, 32, "three", "token"),
