@@ -332,7 +332,10 @@ def cpu_baseline(inp, budget_s=10.0, max_passes=60):
         o.path(inp)
     total = time.perf_counter() - t0
     t = total / passes
+    ab = algorithmic_bytes(inp["cfg"])
+    path_bytes = ab["route"] + ab["expand"] + ab["swiglu"] + ab["combine"]
     return {"value": inp["cfg"].T / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "GBps": round(path_bytes / t / 1e9, 3),
             "sample": f"the full {inp['cfg'].name} batch (T={inp['cfg'].T}), route+expand+swiglu+combine, "
                       f"{passes} passes ({total:.1f} s) after one warm pass, single thread, {t:.3f} s per pass, "
                       f"{cpu_model()}, {os.cpu_count()} logical CPUs visible"}
