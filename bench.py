@@ -37,11 +37,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "moe_glue_amd", "csrc")
 # Source files each call's kernels are built from (a traffic figure is valid
 # only while these are unchanged).
-KERNEL_SOURCES = {"route": ("route.hip", "route_common.h", "fp8_common.h"), "expand": ("expand.hip",),
-                  "expand_fp8": ("quant.hip", "fp8_common.h"), "swiglu": ("swiglu.hip",), "combine": ("combine.hip",),
-                  "route_expand": ("route.hip", "route_common.h", "fp8_common.h", "dispatch.hip", "expand.hip"),
-                  "route_expand_padded": ("route.hip", "route_common.h", "fp8_common.h", "expand.hip"),
-                  "route_expand_fp8": ("route.hip", "route_common.h", "fp8_common.h", "quant.hip")}
+_ROUTE_SOURCES = ("route.hip", "route_common.h", "fp8_common.h", "place_copy.h")
+KERNEL_SOURCES = {"route": _ROUTE_SOURCES, "expand": ("expand.hip",), "expand_fp8": ("quant.hip", "fp8_common.h"),
+                  "swiglu": ("swiglu.hip",), "combine": ("combine.hip",),
+                  "route_expand": _ROUTE_SOURCES + ("dispatch.hip", "expand.hip"),
+                  "route_expand_padded": _ROUTE_SOURCES + ("expand.hip",),
+                  "route_expand_fp8": _ROUTE_SOURCES + ("quant.hip",)}
 
 
 def algorithmic_bytes(cfg, fp8_group: int = 0) -> dict:

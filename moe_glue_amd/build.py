@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "expand.hip", "quant.hip", "swiglu.hip", "combine.hip",
            "probe.hip"]
-HEADERS = ["device_common.h", "kernels.h", "route_common.h", "fp8_common.h"]
+HEADERS = ["device_common.h", "kernels.h", "route_common.h", "fp8_common.h", "place_copy.h"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: hipcc would otherwise form v_pk_{add,mul,fma}_f32 from

@@ -36,6 +36,7 @@
 // lane that owns the winner retires it.  Each lane then computes only the
 // exponentials of the slots it writes, and one more reduction sums them.
 #include "fp8_common.h"
+#include "place_copy.h"
 #include "route_common.h"
 
 #include <algorithm>
@@ -278,52 +279,13 @@ __device__ __forceinline__ uint32_t add_lanes(uint32_t v) {
 
 // With a COPY mode the same launch also expands the unit's token rows in
 // token order (kCopyBf16: plain copy; kCopyFp8: quantised to E4M3 with one
-// scale per `group` columns, as moe_expand_rows_fp8 does).  The unit's
-// kFusedRows*tok_per_row tokens times H/8 columns are cut into `chunks`
-// slices of at most 2048 items (two per lane), one workgroup each:
-//   kCopyBf16  column slices of 2^cw_shift vectors across all the unit's
-//              tokens;
-//   kCopyFp8   row slices of tpw whole token rows, so that one workgroup
-//              writes all of an expanded row's scales.
-// Every workgroup of a unit repeats the unit's scan+place (cheap: the
-// histogram matrix is small on this path) and issues its row loads before
-// it; the first (`owner`) also writes the unit's route outputs.  The slot
-// ranks then come from `ranks`, a workspace array, since the owner
+// scale per `group` columns, as moe_expand_rows_fp8 does), over the slices of
+// place_copy.h.  Every workgroup of a unit repeats the unit's scan+place
+// (cheap: the histogram matrix is small on this path) and issues its row
+// loads before it; the first (`owner`) also writes the unit's route outputs.
+// The slot ranks then come from `ranks`, a workspace array, since the owner
 // overwrites dest_of_src while its siblings may still read them.
-constexpr int kCopyNone = 0;
-constexpr int kCopyBf16 = 1;
-constexpr int kCopyFp8 = 2;
-constexpr int kCopyItems = 2;  // row vectors per lane
-
-struct PlaceCopy {
-    const u32x4* x;
-    void* out;        // u32x4 rows (bf16) or u32x2 rows (E4M3 codes)
-    float* scales;    // kCopyFp8: [rows, G]
-    uint32_t H16;
-    uint32_t G;       // kCopyFp8: scale groups per row
-    int gl;           // kCopyFp8: lanes per scale group (group / 8)
-    int cw_shift;     // kCopyBf16: 2^cw_shift vectors per column slice
-    uint32_t tpw;     // kCopyFp8: token rows per slice (tpw * H16 <= 2048)
-    FastDiv div_h16;  // kCopyFp8
-    uint32_t chunks;  // slices per unit
-};
-
-// The unit-local token and the column of item `item` of slice `chunk`;
-// false if the slice has no such item.
-template <int COPY>
-__device__ __forceinline__ bool copy_item(const PlaceCopy& cp, uint32_t chunk, uint32_t item, int ntok, int& tl,
-                                          uint32_t& col) {
-    if constexpr (COPY == kCopyFp8) {
-        const uint32_t r = fastdiv(item, cp.div_h16);
-        col = item - r * cp.H16;
-        tl = (int)(chunk * cp.tpw + r);
-        return r < cp.tpw && tl < ntok;
-    } else {
-        tl = (int)(item >> cp.cw_shift);
-        col = (chunk << cp.cw_shift) + (item & ((1u << cp.cw_shift) - 1u));
-        return tl < ntok && col < cp.H16;
-    }
-}
+static_assert(kPlaceCopyThreads == kFusedThreads, "the copying place step runs in the scan+place workgroup");
 
 template <bool LIST, int QP, int COPY>
 __device__ __forceinline__ void scan_place(
@@ -530,33 +492,19 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(8
                                 expert_offsets, expert_counts, RowGroups{}, nullptr, cp);
 }
 
-// log2 of the column slice width (vectors) of the copying place step.
-int copy_slice_shift(int tok_per_row) {
-    const int unit_tokens = kFusedRows * tok_per_row;  // 64, 128 or 256
-    int cw_shift = 0;
-    while ((unit_tokens << (cw_shift + 1)) <= kCopyItems * kFusedThreads) ++cw_shift;
-    return cw_shift;
-}
-
 template <int QP>
 void launch_scan_place(bool list, int nwg, const u32x4* rows8, int nb, int tok_per_row, const RouteArgs& a,
                        const int32_t* ranks, int2* row_list, hipStream_t stream) {
     PlaceCopy cp{};
     cp.chunks = 1;
     if (a.copy_out != nullptr) {
+        // the caller checked H/8 <= kCopyItems * kFusedThreads for the quantising copy
+        const int mode = a.copy_group > 0 ? kCopyFp8 : kCopyBf16;
+        cp = make_place_copy(mode, kFusedRows * tok_per_row, a.copy_H, a.copy_group);
         cp.x = static_cast<const u32x4*>(a.copy_x);
         cp.out = a.copy_out;
         cp.scales = a.copy_scales;
-        cp.H16 = (uint32_t)a.copy_H / 8;
-        cp.cw_shift = copy_slice_shift(tok_per_row);
-        cp.chunks = (cp.H16 + (1u << cp.cw_shift) - 1) >> cp.cw_shift;
-        if (a.copy_group > 0) {  // row slices (the caller checked H/8 <= 2048)
-            const uint32_t unit_tokens = (uint32_t)(kFusedRows * tok_per_row);
-            cp.gl = a.copy_group / 8;
-            cp.G = (uint32_t)(a.copy_H / a.copy_group);
-            cp.tpw = std::min<uint32_t>(unit_tokens, (uint32_t)(kCopyItems * kFusedThreads) / cp.H16);
-            cp.div_h16 = make_fastdiv(cp.H16);
-            cp.chunks = (unit_tokens + cp.tpw - 1) / cp.tpw;
+        if (mode == kCopyFp8) {
             route_place_copy_kernel<QP, kCopyFp8><<<nwg * cp.chunks, kFusedThreads, 0, stream>>>(
                 rows8, nb, tok_per_row, a.T, a.E, a.k, a.pad_to, a.topk_ids, ranks, a.dest_of_src, a.src_of_dest,
                 a.expert_offsets, a.expert_counts, cp);

@@ -178,6 +178,19 @@ def test_row_groups_host(tmp_path):
     assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout + out.stderr
 
 
+def test_place_copy_slices_host(tmp_path):
+    """The slices of the place step's token-order copy cover every (token,
+    column) of a unit once, and keep FP8 scale groups whole, on the host
+    (tests/host/place_copy_check.cpp)."""
+    exe = tmp_path / "place_copy_check"
+    src = os.path.join(ROOT, "tests", "host", "place_copy_check.cpp")
+    csrc = os.path.join(ROOT, "moe_glue_amd", "csrc")
+    subprocess.run(["hipcc", "-O2", "-std=c++17", "-x", "hip", "--offload-arch=gfx950", "-I", csrc, src, "-o",
+                    str(exe)], check=True, capture_output=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout + out.stderr
+
+
 def test_route_expand_argument_errors(lib):
     def call(T=4, E=8, k=2, x=FAKE, H=256, ids=FAKE, xe=FAKE, ws=None, wsb=0):
         return status(lib, lib.moe_route_expand(FAKE, None, T, E, k, x, H, ids, FAKE, FAKE, None, FAKE, FAKE, xe,
