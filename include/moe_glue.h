@@ -191,8 +191,9 @@ moe_status moe_route_expand(const float* logits, const float* bias, int32_t T, i
 /* moe_route_padded followed by moe_expand_rows, in one call: exactly their
  * results on the same arguments (all outputs of both calls are written;
  * x_expanded has moe_route_padded_rows rows, its padding rows are not
- * written).  As in moe_route_expand, large batches copy in destination-row
- * order from the route's row list, mid-size ones in the route's last launch.  The workspace must hold
+ * written).  As in moe_route_expand: one launch for T <= 64, mid-size
+ * batches copy in the route's last launch, large ones in destination-row
+ * order from the route's row list.  The workspace must hold
  * moe_route_workspace_bytes(T, E, k) bytes (16-byte aligned) whenever
  * T > 64; for T <= 64 it may be NULL.  Layouts, limits, alignment and errors:
  * the union of moe_route_padded's and moe_expand_rows'. */
@@ -205,9 +206,10 @@ moe_status moe_route_expand_padded(const float* logits, const float* bias, int32
 /* moe_route_padded followed by moe_expand_rows_fp8, in one call: exactly their
  * results on the same arguments (pad_to = 1: moe_route; all outputs of both
  * calls are written; padding rows of x_expanded and scales are not written).
- * On the two-launch route with H <= 16384 and at most ~20 MB of codes the
- * quantising copy runs in the route's place launch; otherwise the route is
- * followed by the quantising expand.
+ * For T <= 64 routing and quantising copy are one launch (as in
+ * moe_route_expand).  On the two-launch route with H <= 16384 and at most
+ * ~20 MB of codes the quantising copy runs in the route's place launch;
+ * otherwise the route is followed by the quantising expand.
  * The workspace must hold moe_route_workspace_bytes(T, E, k) bytes (16-byte
  * aligned) whenever T > 64; for T <= 64 it may be NULL.  Layouts, limits,
  * alignment and errors: the union of moe_route_padded's and

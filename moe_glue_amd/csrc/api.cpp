@@ -254,8 +254,12 @@ moe_status moe_route_expand(const float* logits, const float* bias, int32_t T, i
     const hipStream_t st = static_cast<hipStream_t>(stream);
     moe::RouteArgs a{logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, expert_counts,
                      dest_of_src, src_of_dest, workspace, /*pad_to=*/1, /*row_list=*/nullptr, {}};
-    if (T <= moe::kRouteSmallDispatchMaxTokens && requested == moe::RouteVariant::Auto)
-        return from_hip(moe::launch_route_expand_small(a, x, H, x_expanded, st), "moe_route_expand launch");
+    if (T <= moe::kRouteSmallDispatchMaxTokens && requested == moe::RouteVariant::Auto) {
+        a.copy_x = x;
+        a.copy_out = x_expanded;
+        a.copy_H = H;
+        return from_hip(moe::launch_route_expand_small(a, st), "moe_route_expand launch");
+    }
     const moe::RouteVariant v = moe::route_pick_variant(T, E, requested);
     s = check_route_workspace("moe_route_expand", T, E, k, true, v, workspace, workspace_bytes);
     if (s != MOE_OK) return s;
@@ -292,12 +296,19 @@ moe_status moe_route_expand_padded(const float* logits, const float* bias, int32
     if (s != MOE_OK) return s;
     s = check_expand_args(fn, x, dest_of_src, T, H, k, x_expanded);
     if (s != MOE_OK) return s;
-    const moe::RouteVariant v = moe::route_pick_variant(T, E, requested_route_variant());
-    s = check_route_workspace(fn, T, E, k, true, v, workspace, workspace_bytes);
-    if (s != MOE_OK) return s;
+    const moe::RouteVariant requested = requested_route_variant();
     const hipStream_t st = static_cast<hipStream_t>(stream);
     moe::RouteArgs a{logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, expert_counts,
                      dest_of_src, src_of_dest, workspace, pad_to, /*row_list=*/nullptr, {}};
+    if (T <= moe::kRouteSmallDispatchMaxTokens && requested == moe::RouteVariant::Auto) {
+        a.copy_x = x;
+        a.copy_out = x_expanded;
+        a.copy_H = H;
+        return from_hip(moe::launch_route_expand_small(a, st), "moe_route_expand_padded launch");
+    }
+    const moe::RouteVariant v = moe::route_pick_variant(T, E, requested);
+    s = check_route_workspace(fn, T, E, k, true, v, workspace, workspace_bytes);
+    if (s != MOE_OK) return s;
     // the row list holds the real rows only, so the grouped copy leaves the
     // padding rows untouched exactly as moe_expand_rows does; so does the
     // token-order copy of the place step
@@ -342,12 +353,21 @@ moe_status moe_route_expand_fp8(const float* logits, const float* bias, int32_t 
     if (s != MOE_OK) return s;
     s = check_fp8_args(fn, x, dest_of_src, T, H, k, group, x_expanded, scales);
     if (s != MOE_OK) return s;
-    const moe::RouteVariant v = moe::route_pick_variant(T, E, requested_route_variant());
-    s = check_route_workspace(fn, T, E, k, true, v, workspace, workspace_bytes);
-    if (s != MOE_OK) return s;
+    const moe::RouteVariant requested = requested_route_variant();
     const hipStream_t st = static_cast<hipStream_t>(stream);
     moe::RouteArgs a{logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, expert_counts,
                      dest_of_src, src_of_dest, workspace, pad_to, /*row_list=*/nullptr, {}};
+    if (T <= moe::kRouteSmallDispatchMaxTokens && requested == moe::RouteVariant::Auto) {
+        a.copy_x = x;
+        a.copy_out = x_expanded;
+        a.copy_H = H;
+        a.copy_group = group;
+        a.copy_scales = scales;
+        return from_hip(moe::launch_route_expand_small(a, st), "moe_route_expand_fp8 launch");
+    }
+    const moe::RouteVariant v = moe::route_pick_variant(T, E, requested);
+    s = check_route_workspace(fn, T, E, k, true, v, workspace, workspace_bytes);
+    if (s != MOE_OK) return s;
     // The quantising copy folds into the two-launch route's place step when
     // one of its workgroups holds a whole row and the codes are small: measured
     // at H = 2048, k = 8, group 128, folding saves 2-3 us up to 16 MB of codes

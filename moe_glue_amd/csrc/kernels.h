@@ -126,7 +126,9 @@ hipError_t launch_route(const RouteArgs& a, RouteVariant variant, hipStream_t st
 // Route + expand in one launch for T <= kRouteSmallDispatchMaxTokens: every
 // workgroup recomputes the routing in LDS and copies its share of the rows.
 constexpr int kRouteSmallDispatchMaxTokens = 64;
-hipError_t launch_route_expand_small(const RouteArgs& a, const void* x, int H, void* x_expanded, hipStream_t stream);
+// The copy is RouteArgs::copy_* (bf16, or E4M3 with copy_group > 0); segments
+// padded to pad_to rows.
+hipError_t launch_route_expand_small(const RouteArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------- streaming row kernels
 hipError_t launch_expand_rows(const void* x, const int32_t* dest_of_src, int T, int H, int k, void* x_expanded,

@@ -397,7 +397,8 @@ def test_expand_combine_on_padded_layout(dev, oracle_lib, T, E, k, M, H):
 
 
 @pytest.mark.parametrize("order", ["auto", "grouped", "token", "fused"])
-@pytest.mark.parametrize("T,E,k,M,H", [(20, 8, 2, 16, 256), (300, 128, 8, 128, 2048), (77, 17, 5, 16, 520),
+@pytest.mark.parametrize("T,E,k,M,H", [(20, 8, 2, 16, 256), (64, 512, 16, 32, 264), (32, 128, 8, 128, 2048),
+                                       (1, 3, 2, 5, 8), (300, 128, 8, 128, 2048), (77, 17, 5, 16, 520),
                                        (1023, 64, 6, 64, 4096), (4096, 128, 8, 128, 2048), (2000, 256, 8, 3, 264)])
 def test_route_expand_padded_matches_oracle(dev, oracle_lib, monkeypatch, order, T, E, k, M, H):
     """moe_route_expand_padded: the padded maps, every real row copied, the
@@ -478,7 +479,8 @@ FP8_FUSED_CASES = [(1, 8, 2, 256, 8, 1), (40, 64, 6, 512, 128, 1), (300, 128, 8,
                    (300, 128, 8, 2048, 128, 128), (1023, 64, 6, 4096, 256, 1), (1023, 64, 6, 4096, 512, 16),
                    (500, 8, 2, 1024, 128, 16), (500, 8, 2, 1024, 256, 1), (500, 4, 2, 512, 64, 1),
                    (500, 4, 2, 512, 128, 3), (77, 17, 5, 520, 8, 16), (4096, 128, 8, 2048, 128, 1),
-                   (2000, 512, 16, 264, 8, 1)]
+                   (2000, 512, 16, 264, 8, 1), (32, 128, 8, 2048, 128, 1), (64, 256, 8, 7168, 128, 128),
+                   (0, 16, 4, 256, 64, 1), (64, 4, 2, 512, 512, 8)]
 
 
 @pytest.mark.parametrize("order", ["auto", "token", "fused"])
