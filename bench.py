@@ -8,8 +8,11 @@ route and the quantising expand).  The default workload is the Qwen3-30B-A3B-sha
 (T=4096, H=2048, E=128, k=8, I=768).
 
 Inputs are resident in HBM before the timed region.  Steps rotate over
-several complete input/output sets, so that no step finds its working set in
-the 256 MiB Infinity Cache left behind by the previous step on the same set.
+several complete input/output sets, so that no step finds its inputs in the
+256 MiB Infinity Cache left behind by the previous step on the same set.  The
+default number of sets is sized from the token rows x: the expand reads them
+through the caches (each row is wanted k times), so the copies of x together
+must exceed the Infinity Cache twice over, or a step would be served by it.
 
 Prints ONE JSON line: whole-job tokens/s, per-call device times from HIP
 events recorded on the launch stream inside the timed region, the roofline of
@@ -223,6 +226,31 @@ class Sets:
             raise RuntimeError(f"a MoE glue call failed: {self.lib.moe_last_error().decode()}")
 
 
+INFINITY_CACHE_BYTES = 256 << 20
+MAX_SETS = 256
+MAX_SET_BYTES = 32 << 30
+
+
+def set_bytes(cfg, pad_to=1, fp8_group=0) -> int:
+    """Device bytes of one input/output set (inputs, route outputs, workspace
+    upper bound, expanded rows, activation, output)."""
+    T, H, E, k, I, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.R
+    inputs = T * H * 2 + T * E * 4 + E * 4 + R * 2 * I * 2 + R * H * 2
+    route = R * 16 + (E + 1) * 4 + E * 4 + R * 8 + (T + 1) * E * 4
+    rows = R + (pad_to - 1) * E if pad_to > 1 else R
+    expanded = rows * H * (1 if fp8_group else 2) + (rows * (H // fp8_group) * 4 if fp8_group else 0)
+    return inputs + route + expanded + R * I * 2 + T * H * 2 + (rows * H * 2 if pad_to > 1 else 0)
+
+
+def default_sets(cfg, pad_to=1, fp8_group=0) -> int:
+    """Input sets to rotate: the copies of x together at least twice the
+    Infinity Cache, at least 4 sets, at most MAX_SETS and MAX_SET_BYTES."""
+    x_bytes = cfg.T * cfg.H * 2
+    want = -(-2 * INFINITY_CACHE_BYTES // max(1, x_bytes))
+    fit = MAX_SET_BYTES // max(1, set_bytes(cfg, pad_to, fp8_group))
+    return max(4, min(want, MAX_SETS, fit))
+
+
 def copy_probe_gbps(dev, nbytes=1 << 30, reps=5):
     """Achievable HBM bandwidth: the library's 16 B/lane copy over 1 GiB."""
     import torch
@@ -348,7 +376,9 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="qwen3_30b_a3b")
-    ap.add_argument("--sets", type=int, default=4, help="input/output sets rotated across steps")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input/output sets rotated across steps (0: sized so that the copies of x "
+                         "exceed the Infinity Cache twice over)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--pad", type=int, default=1, help="pad expert segments to a multiple of this many rows")
     ap.add_argument("--fp8-group", type=int, default=0,
@@ -374,7 +404,8 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     cfg = I.CONFIGS[args.config]
     inp = I.make_inputs(cfg, args.seed)
-    sets = Sets(inp, args.sets, dev, args.pad, args.fp8_group)
+    nsets = args.sets if args.sets > 0 else default_sets(cfg, args.pad, args.fp8_group)
+    sets = Sets(inp, nsets, dev, args.pad, args.fp8_group)
     achievable, _ = copy_probe_gbps(dev)
     floor_us = launch_floor_us(dev)
 
@@ -451,7 +482,7 @@ def main(argv=None):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}", "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
-                   "input_sets": args.sets, "seed": args.seed, "pad_to": args.pad, "fp8_group": args.fp8_group},
+                   "input_sets": nsets, "seed": args.seed, "pad_to": args.pad, "fp8_group": args.fp8_group},
         "path_GBps": round(sum(ab[n] for n in names) / (elapsed / args.steps) / 1e9, 1),
         "achievable_copy_GBps": round(achievable, 1),
         "launch_floor_us": floor_us,

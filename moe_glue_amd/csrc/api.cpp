@@ -49,19 +49,21 @@ moe::RouteVariant requested_route_variant() {
 }
 
 // Expand of moe_route_expand above the one-launch size:
-//   Grouped  destination order from the route's row list (expand.hip); saves
-//            about a sixth of the expand's time, but the route then also
-//            builds the row list (about 2 us more on the histogram path);
-//            measured on this part against the copy in the place launch it
-//            pays from about 120 MB of expanded rows (H = 2048: fused ahead
-//            by ~0.8 us at 82-108 MB, grouped ahead by 1 us at 134 MB; wider
-//            rows favour the fused copy longer);
+//   Grouped  destination order from the route's row list (expand.hip); the
+//            route then also builds the row list (about 2 us more on the
+//            histogram path).  Measured on this part with x coming from HBM
+//            (enough rotating input sets that no copy of x stays in the
+//            Infinity Cache), against the copy in the place launch: the
+//            grouped call is ahead once x reaches about 60 MiB (by 7.4 us at
+//            H = 2048 and 3.1 us at H = 4096 with 64 MiB of x, by 5 us at
+//            H = 7168 with 112 MiB) and behind below (by 4.7 us at H = 7168
+//            with 56 MiB, by 2.3-3.6 us at 4-16 MiB); at 32 MiB the two tie;
 //   Fused    token order, copied by the route's scan+place launch itself
 //            (two-launch route only), one launch less;
 //   Token    token order, a launch of its own after the route.
 // Override for tests and measurements:
 // MOE_GLUE_EXPAND_ORDER = token | fused | grouped | auto (anything else: auto).
-constexpr int64_t kGroupedExpandMinBytes = 120ll << 20;
+constexpr int64_t kGroupedExpandMinSourceBytes = 60ll << 20;
 
 enum class ExpandOrder { Token, Fused, Grouped };
 
@@ -74,7 +76,7 @@ ExpandOrder expand_order(int32_t T, int32_t H, int32_t k, moe::RouteVariant v) {
     if (e != nullptr && std::strcmp(e, "token") == 0) return ExpandOrder::Token;
     if (e != nullptr && std::strcmp(e, "grouped") == 0) return ExpandOrder::Grouped;
     if (e != nullptr && std::strcmp(e, "fused") == 0) return two ? ExpandOrder::Fused : ExpandOrder::Token;
-    if ((int64_t)T * k * H * 2 >= kGroupedExpandMinBytes) return ExpandOrder::Grouped;
+    if ((int64_t)T * H * 2 >= kGroupedExpandMinSourceBytes) return ExpandOrder::Grouped;
     return two ? ExpandOrder::Fused : ExpandOrder::Token;
 }
 

@@ -250,7 +250,8 @@ def test_swiglu_shapes(dev, oracle_lib, R, I):
                                      (65, 128, 8, 2048), (300, 64, 6, 256), (100, 17, 5, 8), (777, 8, 2, 264),
                                      (1023, 64, 6, 4096), (2000, 256, 8, 7168), (130, 512, 16, 264),
                                      (5000, 3, 3, 8), (4096, 128, 8, 2048), (9000, 300, 4, 64),
-                                     (40, 16, 4, 32768), (300, 16, 4, 32768)])
+                                     (40, 16, 4, 32768), (300, 16, 4, 32768), (150, 64, 6, 4104),
+                                     (90, 128, 8, 8800)])
 @pytest.mark.parametrize("order", ["auto", "grouped", "token", "fused"])
 def test_route_expand_matches_oracle(dev, oracle_lib, monkeypatch, order, T, E, k, H):
     import torch
