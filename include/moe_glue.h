@@ -173,10 +173,10 @@ moe_status moe_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, in
  * the tokens into the experts' buffer.  For T <= 64 this call uses one launch
  * in which every workgroup recomputes the routing in LDS and copies its share
  * of the rows (the workspace is not touched and may be NULL).  For larger T
- * the route runs as in moe_route; when the token rows x are large (about
- * 60 MiB and up) it also lists the expanded rows per token group in the
- * workspace and the copy runs in destination-row order from that list, else
- * in token order --
+ * the route runs as in moe_route; when there are many expanded rows (T*k of
+ * about 24576 and up) it also lists them per token group in the workspace
+ * and the copy runs in destination-row order from that list, else in token
+ * order --
  * on the two-launch route done by its second launch itself, which then keeps
  * the slot ranks in the workspace instead of in dest_of_src.
  * The workspace must hold moe_route_workspace_bytes(T, E, k) bytes (16-byte

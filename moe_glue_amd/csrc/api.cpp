@@ -51,32 +51,34 @@ moe::RouteVariant requested_route_variant() {
 // Expand of moe_route_expand above the one-launch size:
 //   Grouped  destination order from the route's row list (expand.hip); the
 //            route then also builds the row list (about 2 us more on the
-//            histogram path).  Measured on this part with x coming from HBM
-//            (enough rotating input sets that no copy of x stays in the
-//            Infinity Cache), against the copy in the place launch: the
-//            grouped call is ahead once x reaches about 60 MiB (by 7.4 us at
-//            H = 2048 and 3.1 us at H = 4096 with 64 MiB of x, by 5 us at
-//            H = 7168 with 112 MiB) and behind below (by 4.7 us at H = 7168
-//            with 56 MiB, by 2.3-3.6 us at 4-16 MiB); at 32 MiB the two tie;
+//            histogram path).  Token order scatters every token's k rows
+//            over k expert segments, a cost per expanded row; the list's cost
+//            is fixed.  Measured on this part with x coming from HBM (enough
+//            rotating input sets that no copy of x stays in the Infinity
+//            Cache), moe_route_expand per call against the copy in the place
+//            launch: at 16384 expanded rows the grouped call is 1.6-1.7 us
+//            behind (H = 2048 and 7168), from 24576 rows ahead at every width
+//            measured (H = 2048, 4096, 7168; by 1.2 us at the Qwen3-30B-A3B
+//            shape, 13 us at DeepSeek-V3);
 //   Fused    token order, copied by the route's scan+place launch itself
 //            (two-launch route only), one launch less;
 //   Token    token order, a launch of its own after the route.
 // Override for tests and measurements:
 // MOE_GLUE_EXPAND_ORDER = token | fused | grouped | auto (anything else: auto).
-constexpr int64_t kGroupedExpandMinSourceBytes = 60ll << 20;
+constexpr int64_t kGroupedExpandMinRows = 24576;
 
 enum class ExpandOrder { Token, Fused, Grouped };
 
 constexpr int64_t kQuantisingFoldMaxBytes = 20ll << 20;  // E4M3 codes of moe_route_expand_fp8
 
-ExpandOrder expand_order(int32_t T, int32_t H, int32_t k, moe::RouteVariant v) {
+ExpandOrder expand_order(int32_t T, int32_t k, moe::RouteVariant v) {
     const char* e = std::getenv("MOE_GLUE_EXPAND_ORDER");
     const bool two = v == moe::RouteVariant::TwoPass;
     if (v == moe::RouteVariant::SingleWorkgroup || T == 0) return ExpandOrder::Token;
     if (e != nullptr && std::strcmp(e, "token") == 0) return ExpandOrder::Token;
     if (e != nullptr && std::strcmp(e, "grouped") == 0) return ExpandOrder::Grouped;
     if (e != nullptr && std::strcmp(e, "fused") == 0) return two ? ExpandOrder::Fused : ExpandOrder::Token;
-    if ((int64_t)T * H * 2 >= kGroupedExpandMinSourceBytes) return ExpandOrder::Grouped;
+    if ((int64_t)T * k >= kGroupedExpandMinRows) return ExpandOrder::Grouped;
     return two ? ExpandOrder::Fused : ExpandOrder::Token;
 }
 
@@ -267,7 +269,7 @@ moe_status moe_route_expand(const float* logits, const float* bias, int32_t T, i
     if (s != MOE_OK) return s;
     // the multi-workgroup route either lists the rows per token group for the
     // destination-order expand, or copies them itself in token order
-    const ExpandOrder order = expand_order(T, H, k, v);
+    const ExpandOrder order = expand_order(T, k, v);
     if (order == ExpandOrder::Grouped) {
         a.row_list = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + moe::route_histogram_bytes(T, E));
         a.groups = moe::route_row_groups(T, E, H);
@@ -314,7 +316,7 @@ moe_status moe_route_expand_padded(const float* logits, const float* bias, int32
     // the row list holds the real rows only, so the grouped copy leaves the
     // padding rows untouched exactly as moe_expand_rows does; so does the
     // token-order copy of the place step
-    const ExpandOrder order = expand_order(T, H, k, v);
+    const ExpandOrder order = expand_order(T, k, v);
     if (order == ExpandOrder::Grouped) {
         a.row_list = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + moe::route_histogram_bytes(T, E));
         a.groups = moe::route_row_groups(T, E, H);
