@@ -38,6 +38,7 @@ template <int G, int V>
 __device__ __forceinline__ void topk_token(const float* __restrict__ logits, const float* __restrict__ bias, int T,
                                            int E, int k, int t, int tl, int gl, int32_t* __restrict__ topk_ids,
                                            float* __restrict__ topk_weights, int32_t* ids_lds) {
+    static_assert(V > 0 && (V & (V - 1)) == 0, "the tournament pairs keys: V must be a power of two");
     constexpr int NJ = (kKMax + G - 1) / G;  // slots a lane may own: r = gl + G*j
     const bool live = t < T;
     float vals[V];
@@ -62,15 +63,26 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, con
 #pragma unroll
     for (int r = 0; r < kKMax; ++r) {
         if (r < k) {  // k is uniform: no divergence around the lane exchange
-            // the lane's best: largest key, lowest expert on equal keys
-            uint32_t best = key[0];
-            int bi = 0;
+            // the lane's best: largest key, lowest expert on equal keys, by a
+            // pairwise tournament (log2 V dependent steps, not V - 1): the
+            // left candidate holds the lower experts, so it keeps ties
+            uint32_t tk[V];
+            int ti[V];
 #pragma unroll
-            for (int i = 1; i < V; ++i)
-                if (key[i] > best) {
-                    best = key[i];
-                    bi = i;
-                }
+            for (int i = 0; i < V; ++i) {
+                tk[i] = key[i];
+                ti[i] = i;
+            }
+#pragma unroll
+            for (int w = 1; w < V; w *= 2)
+#pragma unroll
+                for (int i = 0; i + w < V; i += 2 * w)
+                    if (tk[i + w] > tk[i]) {
+                        tk[i] = tk[i + w];
+                        ti[i] = ti[i + w];
+                    }
+            const uint32_t best = tk[0];
+            const int bi = ti[0];
             // the group's best key, then the lowest expert holding it
             const uint32_t top = group_reduce<G, Op::Max>(best);
             const uint32_t mine = (best == top) ? (uint32_t)(gl + G * bi) : 0xFFFFFFFFu;
