@@ -7,7 +7,9 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
+// One wave per workgroup: the fastest plain copy measured on this part
+// (1 GiB each way: 6.68 TB/s against 6.44 with 256 lanes).
+constexpr int kThreads = 64;
 constexpr int kU = 1;
 
 __global__ __launch_bounds__(kThreads) void copy_probe_kernel(const u32x4* __restrict__ src,
