@@ -305,7 +305,14 @@ __device__ __forceinline__ void scan_place(
     __shared__ int32_t s_dest[COPY != kCopyNone ? kFusedRows * kChunk * kKMax : 1];
 
     constexpr int Qp = QP;                     // route_byte_row_vectors(E) <= 32
-    constexpr int RP = kFusedThreads / Qp;     // row groups (>= 32)
+    // Only as many waves sum the histogram rows as give each lane about
+    // kRowsPerLane rows (one batch of loads); the others skip the sums and
+    // their lane reductions, which otherwise take most of the workgroup's
+    // issue slots on small matrices.  sum_waves is wave-uniform.
+    constexpr int kRowsPerLane = COPY != kCopyNone ? 1 : 4;
+    const int sum_waves = min(kFusedWaves, max(1, (nb * Qp + kRowsPerLane * kWave - 1) / (kRowsPerLane * kWave)));
+    const int RP = sum_waves * (kWave / Qp);  // row groups: lane (rg, q) sums rows rg, rg + RP, ...
+    const bool summer = (int)(threadIdx.x / kWave) < sum_waves;
     const int q = threadIdx.x % Qp;
     const int rg = threadIdx.x / Qp;
     const int unit = (int)(blockIdx.x / chunks);
@@ -350,53 +357,55 @@ __device__ __forceinline__ void scan_place(
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[a][j] = 0;
     constexpr int kRowUnroll = COPY != kCopyNone ? 1 : 4;  // the copying form keeps registers for its rows
+    if (summer) {
 #pragma unroll kRowUnroll
-    for (int row = rg; row < nb; row += RP) {
-        const u32x4 w = rows8[(size_t)row * Qp + q];
-        if (row >= row0 && row < row0 + kFusedRows) *reinterpret_cast<u32x4*>(&s_rows[row - row0][q * 16]) = w;
-        uint32_t half[8];
+        for (int row = rg; row < nb; row += RP) {
+            const u32x4 w = rows8[(size_t)row * Qp + q];
+            if (row >= row0 && row < row0 + kFusedRows) *reinterpret_cast<u32x4*>(&s_rows[row - row0][q * 16]) = w;
+            uint32_t half[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            half[2 * j] = w[j] & 0x00FF00FFu;
-            half[2 * j + 1] = (w[j] >> 8) & 0x00FF00FFu;
-        }
-        const uint32_t before_row0 = row < row0 ? 0xFFFFFFFFu : 0u;
+            for (int j = 0; j < 4; ++j) {
+                half[2 * j] = w[j] & 0x00FF00FFu;
+                half[2 * j + 1] = (w[j] >> 8) & 0x00FF00FFu;
+            }
+            const uint32_t before_row0 = row < row0 ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            acc[0][j] += half[j];
-            acc[1][j] += half[j] & before_row0;
-        }
-        if constexpr (LIST) {
-            if (row >= gfirst && row < gend) {
+            for (int j = 0; j < 8; ++j) {
+                acc[0][j] += half[j];
+                acc[1][j] += half[j] & before_row0;
+            }
+            if constexpr (LIST) {
+                if (row >= gfirst && row < gend) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    acc[2][j] += half[j] & before_row0;
-                    acc[3][j] += half[j] & ~before_row0;
+                    for (int j = 0; j < 8; ++j) {
+                        acc[2][j] += half[j] & before_row0;
+                        acc[3][j] += half[j] & ~before_row0;
+                    }
                 }
             }
         }
-    }
-    // inside the wave: lanes of one column sit Qp apart
-#pragma unroll
-    for (int a = 0; a < NACC; ++a)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[a][j] = add_lanes<QP>(acc[a][j]);
-    const int w = threadIdx.x / kWave;
-    if ((int)(threadIdx.x % kWave) < Qp) {
+        // inside the wave: lanes of one column sit Qp apart
 #pragma unroll
         for (int a = 0; a < NACC; ++a)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) part[a][w][q][j] = acc[a][j];
+            for (int j = 0; j < 8; ++j) acc[a][j] = add_lanes<QP>(acc[a][j]);
+        const int w = threadIdx.x / kWave;
+        if ((int)(threadIdx.x % kWave) < Qp) {
+#pragma unroll
+            for (int a = 0; a < NACC; ++a)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) part[a][w][q][j] = acc[a][j];
+        }
     }
     __syncthreads();
-    // lane (a, column, word): sum the 16 waves, split the halves into experts
+    // lane (a, column, word): sum the summing waves, split the halves into experts
     for (int i = threadIdx.x; i < NACC * Qp * 8; i += kFusedThreads) {
         const int a = i / (Qp * 8);
         const int qq = (i / 8) % Qp;
         const int j = i % 8;
         uint32_t sum = 0;
 #pragma unroll
-        for (int v = 0; v < kFusedWaves; ++v) sum += part[a][v][qq][j];
+        for (int v = 0; v < sum_waves; ++v) sum += part[a][v][qq][j];
         const int e = qq * 16 + (j / 2) * 4 + (j % 2);  // bytes 0/1 of word j/2; +2 for bytes 2/3
         if (e < E) s_acc[a][e] = (int32_t)(sum & 0xFFFFu);
         if (e + 2 < E) s_acc[a][e + 2] = (int32_t)(sum >> 16);
