@@ -48,6 +48,9 @@ class Oracle:
         lib.moe_ref_expand_rows_fp8.restype = None
         lib.moe_ref_expand_rows_fp8.argtypes = [_u16p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                 ctypes.c_int, ctypes.POINTER(ctypes.c_uint8), _f32p]
+        lib.moe_ref_expand_rows_mxfp8.restype = None
+        lib.moe_ref_expand_rows_mxfp8.argtypes = [_u16p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                  ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_uint8)]
         lib.moe_ref_e4m3_from_f32.restype = ctypes.c_uint8
         lib.moe_ref_e4m3_from_f32.argtypes = [ctypes.c_float]
         lib.moe_ref_f64_from_e4m3.restype = ctypes.c_double
@@ -135,6 +138,20 @@ class Oracle:
         sc = np.zeros((n, H // group), np.float32)
         self.lib.moe_ref_expand_rows_fp8(_ptr(x, _u16p), _ptr(dest_of_src, _i32p), T, H, k, group,
                                          q.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), _ptr(sc, _f32p))
+        return q, sc
+
+    def expand_rows_mxfp8(self, x: np.ndarray, dest_of_src: np.ndarray, k: int, rows: int | None = None):
+        """MXFP8 quantising expand; returns (codes uint8 [rows, H], E8M0 scale bytes uint8 [rows, H/32])."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        dest_of_src = np.ascontiguousarray(dest_of_src, dtype=np.int32).reshape(-1)
+        T, H = x.shape
+        assert dest_of_src.size == T * k and H % 32 == 0
+        n = T * k if rows is None else rows
+        q = np.zeros((n, H), np.uint8)
+        sc = np.zeros((n, H // 32), np.uint8)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        self.lib.moe_ref_expand_rows_mxfp8(_ptr(x, _u16p), _ptr(dest_of_src, _i32p), T, H, k,
+                                           q.ctypes.data_as(u8p), sc.ctypes.data_as(u8p))
         return q, sc
 
     def e4m3_from_f32(self, v: np.ndarray) -> np.ndarray:

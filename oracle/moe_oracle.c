@@ -266,6 +266,48 @@ void moe_ref_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, int 
     }
 }
 
+/* MXFP8 quantising expand.  "CuTeDSL at Perplexity", Blackwell support,
+ * names MXFP8 among the block-scaled formats and takes its absolute maximum
+ * over 32 elements.  How the block scale is encoded is not on the pages;
+ * reading (the OCP Microscaling formats definition): for each token t and
+ * block b of 32 consecutive columns,
+ *   amax = max |x[t, c]| over the block
+ *   e    = floor(log2 amax) - 8, at least -127 (8 is the exponent of E4M3's
+ *          largest normal, 448 = 1.75 * 2^8); e = -127 when amax = 0
+ *   scale byte (E8M0) = e + 127, the value 2^e
+ *   q[c] = e4m3(x[t, c] / 2^e)   saturating, nearest-even (the division by a
+ *          power of two is exact)
+ * and every expanded row dest_of_src[t*k + j] receives the token's codes
+ * (q_out [rows, H]) and scale bytes (scales [rows, H/32]). */
+void moe_ref_expand_rows_mxfp8(const uint16_t* x, const int32_t* dest_of_src, int T, int H, int k,
+                               uint8_t* q_out, uint8_t* scales) {
+    const int B = H / 32;
+    for (int t = 0; t < T; ++t) {
+        for (int b = 0; b < B; ++b) {
+            double amax = 0.0;
+            for (int c = b * 32; c < (b + 1) * 32; ++c) {
+                const double v = fabs(moe_ref_f64_from_bf16(x[(size_t)t * H + c]));
+                if (v > amax) amax = v;
+            }
+            int e = -127;
+            if (amax > 0.0) {
+                int ex;
+                (void)frexp(amax, &ex);  /* amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
+                e = ex - 1 - 8;
+                if (e < -127) e = -127;
+            }
+            for (int j = 0; j < k; ++j) {
+                const int64_t dst_row = dest_of_src[(size_t)t * k + j];
+                scales[(size_t)dst_row * B + b] = (uint8_t)(e + 127);
+                for (int c = b * 32; c < (b + 1) * 32; ++c) {
+                    const double xv = moe_ref_f64_from_bf16(x[(size_t)t * H + c]);
+                    q_out[(size_t)dst_row * H + c] = moe_ref_e4m3_from_f32((float)ldexp(xv, -e));
+                }
+            }
+        }
+    }
+}
+
 /* ---------------------------------------------------------------- SwiGLU */
 
 /* FlashInfer PR analysis, sections 1-2 (doActivationKernel): the activation

@@ -59,6 +59,14 @@ void moe_ref_expand_rows(const uint16_t* x, const int32_t* dest_of_src, int T, i
 void moe_ref_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, int T, int H, int k, int group,
                              uint8_t* q_out, float* scales);
 
+/* MXFP8 quantising expand: per token and block of 32 columns, e =
+ * max(floor(log2 amax) - 8, -127) (-127 for an all-zero block), scale byte
+ * (E8M0) = e + 127, codes = e4m3(x / 2^e) saturating; codes and scale bytes
+ * written to every expanded row of the token.  H must be a multiple of 32.
+ * q_out [rows, H] uint8 codes, scales [rows, H/32] uint8. */
+void moe_ref_expand_rows_mxfp8(const uint16_t* x, const int32_t* dest_of_src, int T, int H, int k,
+                               uint8_t* q_out, uint8_t* scales);
+
 /* The oracle's FP8 E4M3 (OCP, bias 7, max 448) conversions, exported for pinning. */
 uint8_t moe_ref_e4m3_from_f32(float v);
 double moe_ref_f64_from_e4m3(uint8_t c);

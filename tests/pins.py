@@ -527,6 +527,83 @@ def pin_expand_fp8(o) -> list:
     return fails
 
 
+def _bruteforce_expand_mxfp8(x_bits, dest, k, rows):
+    """Per block of 32: the smallest power-of-two scale 2^e with amax / 2^e < 512
+    found by halving and doubling (no logarithm), codes by torch's own E4M3
+    conversion of x / 2^e after the +-448 clamp."""
+    T, H = x_bits.shape
+    B = H // 32
+    xv = bf.bf16_to_float(x_bits).astype(np.float64)
+    q = np.zeros((rows, H), np.uint8)
+    sc = np.zeros((rows, B), np.uint8)
+    for t in range(T):
+        for b in range(B):
+            seg = xv[t, 32 * b:32 * (b + 1)]
+            amax = float(np.max(np.abs(seg)))
+            e = -127
+            if amax > 0:
+                e = 0
+                while amax / 2.0 ** e >= 512.0:
+                    e += 1
+                while amax / 2.0 ** e < 256.0 and e > -127:
+                    e -= 1
+            codes = _torch_e4m3((seg / 2.0 ** e).astype(np.float32))
+            for j in range(k):
+                d = dest[t * k + j]
+                q[d, 32 * b:32 * (b + 1)] = codes
+                sc[d, b] = e + 127
+    return q, sc
+
+
+def pin_expand_mxfp8(o) -> list:
+    fails = []
+    rng = _rng(12)
+    for (T, H, E, k) in ((5, 64, 8, 2), (4, 96, 6, 3), (3, 256, 4, 4), (6, 32, 5, 1)):
+        x = _rand_bf16(rng, (T, H), scale=3.0)
+        # magnitudes spread over many binades, one block per token
+        for t in range(T):
+            x[t, 32 * (t % (H // 32)):32 * (t % (H // 32) + 1)] = _rand_bf16(
+                rng, (32,), scale=float(10.0 ** rng.integers(-6, 5)))
+        x[0, :32] = 0                                      # an all-zero block
+        x[1, :32] = bf.bf16_round_exact_np(np.full(32, 1.875))  # saturates: 1.875 * 2^8 > 448
+        x[2, -32:] = bf.bf16_round_exact_np(np.full(32, 0.25))  # exact power of two
+        x[2, -31] = bf.bf16_round_exact_np(np.array([3e-6]))[0]  # tiny beside its block maximum: a subnormal code
+        r = o.route(rng.standard_normal((T, E)).astype(np.float32), k)
+        q, sc = o.expand_rows_mxfp8(x, r["dest_of_src"], k)
+        qb, scb = _bruteforce_expand_mxfp8(x, r["dest_of_src"], k, T * k)
+        if not np.array_equal(q, qb):
+            fails.append(f"mxfp8 expand codes differ from brute force T={T} H={H}")
+        if not np.array_equal(sc, scb):
+            fails.append(f"mxfp8 expand scale bytes differ from brute force T={T} H={H}")
+        # format properties, from the OCP MX definition: 2^(byte - 127) is a
+        # power-of-two scale with amax / scale in [256, 512); zero blocks get byte 0
+        xv = bf.bf16_to_float(x).astype(np.float64)
+        for s in range(T * k):
+            t, d = s // k, r["dest_of_src"][s]
+            for b in range(H // 32):
+                seg = xv[t, 32 * b:32 * (b + 1)]
+                amax = float(np.max(np.abs(seg)))
+                scale = 2.0 ** (int(sc[d, b]) - 127)
+                if amax == 0:
+                    if sc[d, b] != 0 or np.any(q[d, 32 * b:32 * (b + 1)] != 0):
+                        fails.append("mxfp8 expand: an all-zero block is not byte 0 with zero codes")
+                    continue
+                if not (256.0 <= amax / scale < 512.0):
+                    fails.append(f"mxfp8 expand: amax/scale = {amax / scale} outside [256, 512)")
+                    break
+                vals = np.array([o.lib.moe_ref_f64_from_e4m3(int(c)) for c in q[d, 32 * b:32 * (b + 1)]])
+                scaled = seg / scale
+                sat = np.abs(scaled) > 448.0
+                if np.any(np.abs(vals[sat]) != 448.0):
+                    fails.append("mxfp8 expand: a value beyond 448 after scaling does not saturate")
+                ok = ~sat
+                lim = np.maximum(np.abs(scaled[ok]) * 2.0 ** -4, 2.0 ** -10) * (1 + 1e-9)
+                if np.any(np.abs(vals[ok] - scaled[ok]) > lim):
+                    fails.append("mxfp8 expand: a code is more than half an E4M3 step from x / scale")
+                    break
+    return fails
+
+
 ALL_PINS = [
     pin_route_golden,
     pin_route_bruteforce,
@@ -535,6 +612,7 @@ ALL_PINS = [
     pin_expand,
     pin_e4m3_rounding,
     pin_expand_fp8,
+    pin_expand_mxfp8,
     pin_swiglu_layout_and_identities,
     pin_swiglu_expit_exhaustive,
     pin_combine_identity,

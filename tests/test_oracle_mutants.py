@@ -83,6 +83,14 @@ MUTANTS = [
     ("fp8_amax_first_only",
      "for (int c = g * group; c < (g + 1) * group; ++c) {\n                float v = fabsf(",
      "for (int c = g * group; c < g * group + 1; ++c) {\n                float v = fabsf("),
+    ("mx_emax_7", "e = ex - 1 - 8;", "e = ex - 1 - 7;"),
+    ("mx_ceil_log2", "e = ex - 1 - 8;", "e = ex - 8;"),
+    ("mx_e8m0_bias_128", "scales[(size_t)dst_row * B + b] = (uint8_t)(e + 127);",
+     "scales[(size_t)dst_row * B + b] = (uint8_t)(e + 128);"),
+    ("mx_scales_by_token", "scales[(size_t)dst_row * B + b] = (uint8_t)(e + 127);",
+     "scales[(size_t)t * B + b] = (uint8_t)(e + 127);"),
+    ("mx_zero_block_scale_one", "int e = -127;\n            if (amax > 0.0) {", "int e = 0;\n            if (amax > 0.0) {"),
+    ("mx_multiplies_by_scale", "moe_ref_e4m3_from_f32((float)ldexp(xv, -e));", "moe_ref_e4m3_from_f32((float)ldexp(xv, e));"),
     ("swiglu_gate_up_swapped",
      "double g = moe_ref_f64_from_bf16(h[(size_t)r * 2 * I + i]);\n"
      "            double u = moe_ref_f64_from_bf16(h[(size_t)r * 2 * I + I + i]);",
