@@ -4,7 +4,9 @@ One step = the whole path on one batch: moe_route_expand (route, then the
 expansion of the token rows) -> moe_swiglu -> moe_combine (the GEMM outputs
 are seeded stand-ins already in HBM).  With --pad the first call is
 moe_route_expand_padded; with --fp8-group it is moe_route_expand_fp8 (the
-route and the quantising expand).  The default workload is the Qwen3-30B-A3B-shaped prefill batch
+route and the quantising expand); with --mxfp8 it is moe_route, then
+moe_expand_rows_mxfp8 (E4M3 codes, one E8M0 scale byte per 32 columns).
+The default workload is the Qwen3-30B-A3B-shaped prefill batch
 (T=4096, H=2048, E=128, k=8, I=768).
 
 Inputs are resident in HBM before the timed region.  Steps rotate over
@@ -42,6 +44,7 @@ CSRC = os.path.join(ROOT, "moe_glue_amd", "csrc")
 # only while these are unchanged).
 _ROUTE_SOURCES = ("route.hip", "route_common.h", "fp8_common.h", "place_copy.h")
 KERNEL_SOURCES = {"route": _ROUTE_SOURCES, "expand": ("expand.hip",), "expand_fp8": ("quant.hip", "fp8_common.h"),
+                  "expand_mxfp8": ("quant.hip", "fp8_common.h"),
                   "swiglu": ("swiglu.hip",), "combine": ("combine.hip",),
                   "route_expand": _ROUTE_SOURCES + ("dispatch.hip", "expand.hip"),
                   "route_expand_padded": _ROUTE_SOURCES + ("expand.hip",),
@@ -56,7 +59,9 @@ def algorithmic_bytes(cfg, fp8_group: int = 0) -> dict:
     swiglu = R * 2 * I * 2 + R * I * 2
     combine = R * H * 2 + R * 4 + R * 4 + T * H * 2
     expand_fp8 = T * H * 2 + R * 4 + R * H + (R * (H // fp8_group) * 4 if fp8_group else 0)
+    expand_mxfp8 = T * H * 2 + R * 4 + R * H + R * (H // 32)
     return {"route": route, "expand": expand, "swiglu": swiglu, "combine": combine, "route_expand": route + expand,
+            "expand_mxfp8": expand_mxfp8,
             "route_expand_padded": route + expand, "expand_fp8": expand_fp8, "route_expand_fp8": route + expand_fp8}
 
 
@@ -134,7 +139,7 @@ class HipEvent:
 class Sets:
     """NSETS complete input/output sets on the device, with ctypes argument tuples."""
 
-    def __init__(self, inp, nsets, dev, pad_to=1, fp8_group=0):
+    def __init__(self, inp, nsets, dev, pad_to=1, fp8_group=0, mxfp8=False):
         import torch
         import moe_glue_amd as mg
 
@@ -168,6 +173,9 @@ class Sets:
             if fp8_group:
                 d["x_exp"] = torch.empty((P, H), dtype=torch.uint8, device=dev)
                 d["x_scales"] = torch.empty((P, H // fp8_group), dtype=torch.float32, device=dev)
+            if mxfp8:
+                d["x_exp"] = torch.empty((P, H), dtype=torch.uint8, device=dev)
+                d["x_scales"] = torch.empty((P, H // 32), dtype=torch.uint8, device=dev)
             d["act"] = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
             d["out"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
             p = lambda key: 0 if d[key] is None else d[key].data_ptr()  # noqa: E731
@@ -186,6 +194,8 @@ class Sets:
                 "expand": (p("x"), p("dest_of_src"), T, H, k, p("x_exp"), stream),
                 "expand_fp8": ((p("x"), p("dest_of_src"), T, H, k, fp8_group, p("x_exp"), p("x_scales"), stream)
                                if fp8_group else None),
+                "expand_mxfp8": ((p("x"), p("dest_of_src"), T, H, k, p("x_exp"), p("x_scales"), stream)
+                                 if mxfp8 else None),
                 "route_expand_fp8": ((p("logits"), p("bias"), T, E, k, pad_to, p("x"), H, fp8_group, p("topk_ids"),
                                       p("topk_weights"), p("expert_offsets"), p("expert_counts"), p("dest_of_src"),
                                       p("src_of_dest"), p("x_exp"), p("x_scales"), p("workspace"),
@@ -196,6 +206,7 @@ class Sets:
             self.sets.append(d)
         self.fns = {"route": self.lib.moe_route if pad_to == 1 else self.lib.moe_route_padded,
                     "expand": self.lib.moe_expand_rows, "expand_fp8": self.lib.moe_expand_rows_fp8,
+                    "expand_mxfp8": self.lib.moe_expand_rows_mxfp8,
                     "route_expand": self.lib.moe_route_expand,
                     "route_expand_padded": self.lib.moe_route_expand_padded,
                     "route_expand_fp8": self.lib.moe_route_expand_fp8, "swiglu": self.lib.moe_swiglu,
@@ -203,7 +214,9 @@ class Sets:
         # Route and expand run as one moe_route_expand(_padded, _fp8) call
         # (one launch for decode batches, destination-order expand for large
         # ones, the copy in the route's place launch in between).
-        if fp8_group:
+        if mxfp8:
+            self.calls = ["route", "expand_mxfp8", "swiglu", "combine"]
+        elif fp8_group:
             self.calls = ["route_expand_fp8", "swiglu", "combine"]
         elif pad_to == 1:
             self.calls = ["route_expand", "swiglu", "combine"]
@@ -383,6 +396,8 @@ def main(argv=None):
     ap.add_argument("--pad", type=int, default=1, help="pad expert segments to a multiple of this many rows")
     ap.add_argument("--fp8-group", type=int, default=0,
                     help="expand with FP8 E4M3 quantisation, one scale per this many columns (0: bf16 expand)")
+    ap.add_argument("--mxfp8", action="store_true",
+                    help="expand with MXFP8 quantisation (E4M3 codes, E8M0 scale per 32 columns) after the route")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip the HIP-graph replay timing (ms_per_step_graph)")
@@ -405,7 +420,10 @@ def main(argv=None):
     cfg = I.CONFIGS[args.config]
     inp = I.make_inputs(cfg, args.seed)
     nsets = args.sets if args.sets > 0 else default_sets(cfg, args.pad, args.fp8_group)
-    sets = Sets(inp, nsets, dev, args.pad, args.fp8_group)
+    if args.mxfp8 and (args.fp8_group or args.pad > 1):
+        print("bench.py: --mxfp8 runs unpadded without --fp8-group", file=sys.stderr)
+        return 2
+    sets = Sets(inp, nsets, dev, args.pad, args.fp8_group, args.mxfp8)
     achievable, _ = copy_probe_gbps(dev)
     floor_us = launch_floor_us(dev)
 
@@ -482,7 +500,8 @@ def main(argv=None):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}", "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
-                   "input_sets": nsets, "seed": args.seed, "pad_to": args.pad, "fp8_group": args.fp8_group},
+                   "input_sets": nsets, "seed": args.seed, "pad_to": args.pad, "fp8_group": args.fp8_group,
+                   "mxfp8": args.mxfp8},
         "path_GBps": round(sum(ab[n] for n in names) / (elapsed / args.steps) / 1e9, 1),
         "achievable_copy_GBps": round(achievable, 1),
         "launch_floor_us": floor_us,

@@ -12,6 +12,7 @@
  *   moe_route_padded route with expert segments padded to a row multiple
  *   moe_route_expand_padded  moe_route_padded + expand in one call
  *   moe_expand_rows_fp8  expand with FP8 (E4M3) quantisation per column group
+ *   moe_expand_rows_mxfp8 expand with MXFP8 quantisation (E8M0 scale per 32 columns)
  *   moe_route_expand_fp8 moe_route_padded + moe_expand_rows_fp8 in one call
  *
  * The problem statement these calls follow:
@@ -163,6 +164,26 @@ moe_status moe_expand_rows(const uint16_t* x, const int32_t* dest_of_src, int32_
  * MOE_ERR_UNSUPPORTED (group, sizes), MOE_ERR_HIP. */
 moe_status moe_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, int32_t T, int32_t H, int32_t k,
                                int32_t group, uint8_t* x_expanded, float* scales, void* stream);
+
+/* moe_expand_rows with MXFP8 quantisation (OCP microscaling).  "CuTeDSL at
+ * Perplexity", section "Blackwell support", names MXFP8 among the
+ * block-scaled formats and takes its absolute maximum over 32 elements; the
+ * scale encoding follows the OCP Microscaling formats definition, which is
+ * also the scale format of gfx950's scaled matrix instructions.  For each
+ * token t and block b of 32 consecutive columns:
+ *   amax = max |x[t, c]| over the block
+ *   e    = max(floor(log2 amax) - 8, -127)   (-127 for an all-zero block)
+ *   scales[d, b]        = e + 127            (E8M0 byte: the scale is 2^e)
+ *   x_expanded[d, c]    = E4M3(clamp(x[t, c] / 2^e, +-448)), nearest-even
+ * for every expanded row d = dest_of_src[t*k + j].  The division by a power
+ * of two is exact.
+ * x [T, H] bf16; x_expanded [rows, H] uint8 E4M3 codes; scales [rows, H/32]
+ * uint8 E8M0 bytes.  Rows not named in dest_of_src are not written.
+ * H must be a multiple of 32.  Alignment: x 16 bytes, x_expanded 8 bytes.
+ * T = 0 is a no-op.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN,
+ * MOE_ERR_UNSUPPORTED (sizes), MOE_ERR_HIP. */
+moe_status moe_expand_rows_mxfp8(const uint16_t* x, const int32_t* dest_of_src, int32_t T, int32_t H, int32_t k,
+                                 uint8_t* x_expanded, uint8_t* scales, void* stream);
 
 /* ------------------------------------------------ route + expand (dispatch) */
 

@@ -11,6 +11,7 @@ Four calls, each a thin wrapper over the C ABI of the HIP library
     route_expand(logits, k, x, bias=None)  route + expand, one launch for T <= 64
     route_padded(logits, k, pad_to)    route with expert segments padded to pad_to rows
     expand_rows_fp8(x, dest, k, group) expand with FP8 E4M3 quantisation per column group
+    expand_rows_mxfp8(x, dest, k)    expand with MXFP8 quantisation (E8M0 scale per 32 columns)
 
 Tensors are torch CUDA (HIP) tensors; bf16 tensors use torch.bfloat16.  Work
 is enqueued on torch's current stream and nothing synchronises.  Every call
@@ -23,7 +24,7 @@ from ._binding import (E_MAX, EXPORTED, K_MAX, LIB_PATH, MoEGlueArgumentError, M
                        load)
 
 __all__ = ["route", "route_workspace_bytes", "alloc_route_outputs", "route_padded", "padded_rows", "expand_rows",
-           "expand_rows_fp8",
+           "expand_rows_fp8", "expand_rows_mxfp8",
            "route_expand", "route_expand_padded", "route_expand_fp8", "swiglu", "combine",
            "copy_probe", "MoEGlueError", "MoEGlueArgumentError", "E_MAX", "K_MAX"]
 
@@ -218,6 +219,24 @@ def expand_rows_fp8(x, dest_of_src, k: int, group: int, rows: int | None = None,
     st = load().moe_expand_rows_fp8(_ptr(x), _ptr(dest_of_src), T, H, k, group, _ptr(out), _ptr(scales),
                                     _stream(x.device))
     check(st, "moe_expand_rows_fp8")
+    return out, scales
+
+
+def expand_rows_mxfp8(x, dest_of_src, k: int, rows: int | None = None, out=None, scales=None):
+    """MXFP8 quantising expand; returns (codes uint8 [rows, H], E8M0 scale bytes
+    uint8 [rows, H/32]).  See moe_expand_rows_mxfp8 in include/moe_glue.h."""
+    torch = _torch()
+    _need_gpu("x", x, torch.bfloat16, 2)
+    _need_gpu("dest_of_src", dest_of_src, torch.int32)
+    T, H = x.shape
+    n = T * k if rows is None else rows
+    if out is None:
+        out = torch.empty((n, H), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((n, max(1, H // 32)), dtype=torch.uint8, device=x.device)
+    st = load().moe_expand_rows_mxfp8(_ptr(x), _ptr(dest_of_src), T, H, k, _ptr(out), _ptr(scales),
+                                      _stream(x.device))
+    check(st, "moe_expand_rows_mxfp8")
     return out, scales
 
 

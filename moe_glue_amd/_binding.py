@@ -19,7 +19,7 @@ K_MAX = 16
 PAD_MAX = 4096
 
 EXPORTED = ("moe_route_workspace_bytes", "moe_route", "moe_route_padded_rows", "moe_route_padded",
-            "moe_expand_rows", "moe_expand_rows_fp8", "moe_route_expand", "moe_route_expand_padded",
+            "moe_expand_rows", "moe_expand_rows_fp8", "moe_expand_rows_mxfp8", "moe_route_expand", "moe_route_expand_padded",
             "moe_route_expand_fp8", "moe_swiglu", "moe_combine", "moe_copy_probe",
             "moe_status_string", "moe_last_error")
 
@@ -69,6 +69,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_expand_rows.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _vp]
     lib.moe_expand_rows_fp8.restype = ctypes.c_int
     lib.moe_expand_rows_fp8.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
+    lib.moe_expand_rows_mxfp8.restype = ctypes.c_int
+    lib.moe_expand_rows_mxfp8.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]
     lib.moe_route_expand.restype = ctypes.c_int
     lib.moe_route_expand.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      ctypes.c_size_t, _vp]

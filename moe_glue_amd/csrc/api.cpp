@@ -164,6 +164,20 @@ moe_status check_fp8_args(const char* fn, const uint16_t* x, const int32_t* dest
     return MOE_OK;
 }
 
+moe_status check_mxfp8_args(const char* fn, const uint16_t* x, const int32_t* dest_of_src, int32_t T, int32_t H,
+                            int32_t k, const uint8_t* x_expanded, const uint8_t* scales) {
+    moe_status s = check_rows(fn, T, H, "H");
+    if (s != MOE_OK) return s;
+    if (k < 1 || k > MOE_K_MAX) return fail(MOE_ERR_SHAPE, "%s: k=%d must be in [1, %d]", fn, k, MOE_K_MAX);
+    if ((int64_t)T * k >= INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "%s: T*k too large", fn);
+    if (H % 32 != 0) return fail(MOE_ERR_SHAPE, "%s: H=%d is not a multiple of the 32-column block", fn, H);
+    if (T == 0) return MOE_OK;
+    if (!x || !dest_of_src || !x_expanded || !scales) return fail(MOE_ERR_NULL, "%s: NULL tensor pointer", fn);
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(x_expanded) & 7u) != 0)
+        return fail(MOE_ERR_ALIGN, "%s: x must be 16-byte and codes 8-byte aligned", fn);
+    return MOE_OK;
+}
+
 moe_status check_pad(const char* fn, int32_t T, int32_t E, int32_t k, int32_t pad_to) {
     if (pad_to < 1) return fail(MOE_ERR_SHAPE, "%s: pad_to=%d must be >= 1", fn, pad_to);
     if (pad_to > MOE_PAD_MAX) return fail(MOE_ERR_UNSUPPORTED, "%s: pad_to=%d exceeds %d", fn, pad_to, MOE_PAD_MAX);
@@ -342,6 +356,16 @@ moe_status moe_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, in
     return from_hip(moe::launch_expand_rows_fp8(x, dest_of_src, T, H, k, group, x_expanded, scales,
                                                 static_cast<hipStream_t>(stream)),
                     "moe_expand_rows_fp8 launch");
+}
+
+moe_status moe_expand_rows_mxfp8(const uint16_t* x, const int32_t* dest_of_src, int32_t T, int32_t H, int32_t k,
+                                 uint8_t* x_expanded, uint8_t* scales, void* stream) {
+    moe_status s = check_mxfp8_args("moe_expand_rows_mxfp8", x, dest_of_src, T, H, k, x_expanded, scales);
+    if (s != MOE_OK) return s;
+    if (T == 0) return ok();
+    return from_hip(moe::launch_expand_rows_mxfp8(x, dest_of_src, T, H, k, x_expanded, scales,
+                                                  static_cast<hipStream_t>(stream)),
+                    "moe_expand_rows_mxfp8 launch");
 }
 
 moe_status moe_route_expand_fp8(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,

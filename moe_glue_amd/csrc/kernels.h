@@ -138,6 +138,9 @@ hipError_t launch_expand_grouped(const void* x, const int32_t* row_list, const R
                                  void* x_expanded, hipStream_t stream);
 hipError_t launch_expand_rows_fp8(const void* x, const int32_t* dest_of_src, int T, int H, int k, int group,
                                   void* q_out, float* scales, hipStream_t stream);
+// MXFP8: E4M3 codes with one E8M0 scale byte per block of 32 columns (H % 32 == 0).
+hipError_t launch_expand_rows_mxfp8(const void* x, const int32_t* dest_of_src, int T, int H, int k, void* q_out,
+                                    uint8_t* scales, hipStream_t stream);
 hipError_t launch_swiglu(const void* h, int R, int I, void* act, hipStream_t stream);
 hipError_t launch_combine(const void* y, const float* topk_weights, const int32_t* dest_of_src, int T, int H,
                           int k, void* out, hipStream_t stream);

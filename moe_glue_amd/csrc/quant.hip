@@ -10,6 +10,8 @@
 // the 8 codes (8 bytes) are stored to each of the token's k expanded rows, and
 // the group's first lane stores its scale k times.  HBM traffic: T*H*2 read,
 // R*H + R*(H/group)*4 written -- about 0.57x the bf16 expand at group 128.
+// The MXFP8 form below differs only in its scale: a power of two per block of
+// 32 columns, stored as one E8M0 byte.
 #include "device_common.h"
 #include "fp8_common.h"
 #include "kernels.h"
@@ -57,6 +59,56 @@ __global__ __launch_bounds__(kThreads) void expand_rows_fp8_kernel(const u32x4* 
     }
 }
 
+// MXFP8 (OCP microscaling; "CuTeDSL at Perplexity", Blackwell support, takes
+// the MXFP8 absolute maximum over 32 elements): a block of 32 columns is 4
+// consecutive lanes.  Its scale is the power of two 2^e, e = max(floor(log2
+// amax) - 8, -127), stored as the E8M0 byte e + 127; the codes are
+// E4M3(clamp(x * 2^-e, +-448)), and multiplying by a power of two is exact.
+// amax is a bf16 value widened to fp32, so for a normal amax floor(log2 amax)
+// is its exponent field minus 127; a zero or subnormal amax (field 0) takes
+// e = -127.  2^-e is built from its bits: 127 - e lies in [8, 254] for every
+// finite amax, a normal fp32.
+constexpr int kMxLanes = 4;  // 32 columns / 8 per lane
+
+template <bool ROW_PER_WAVE>
+__global__ __launch_bounds__(kThreads) void expand_rows_mxfp8_kernel(const u32x4* __restrict__ x,
+                                                                     const int32_t* __restrict__ dest_of_src,
+                                                                     uint32_t n, uint32_t H16, FastDiv div_h16, int k,
+                                                                     uint32_t B, u32x2* __restrict__ q_out,
+                                                                     uint8_t* __restrict__ scales) {
+    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    // every lane takes part in the block reduction; n is a multiple of 4, so
+    // no block straddles the end and lanes past it work on zeros
+    const bool live = i < n;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (live) v = load_stream(x + i);
+    float f[8];
+    unpack8(v, f);
+    const uint32_t amax_bits = group_reduce<kMxLanes, Op::Max>(abs_max_bits8(f));
+    if (!live) return;
+    const int ef = (int)(amax_bits >> 23);  // |x| bits: no sign
+    const int e = ef == 0 ? -127 : max(ef - 127 - 8, -127);
+    const float inv = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);
+    const uint8_t byte = (uint8_t)(e + 127);
+    const u32x2 codes = quantize8_e4m3(f, inv);
+    uint32_t t = fastdiv(i, div_h16);
+    if constexpr (ROW_PER_WAVE) t = uniform(t);
+    const uint32_t c = i - t * H16;
+    const int32_t* d = dest_of_src + (size_t)t * k;
+    int32_t dj[kKMax];
+#pragma unroll
+    for (int j = 0; j < kKMax; ++j) dj[j] = d[j < k ? j : k - 1];
+    const bool first_of_block = (threadIdx.x % kMxLanes) == 0;
+    const uint32_t b = c / kMxLanes;
+#pragma unroll
+    for (int j = 0; j < kKMax; ++j) {
+        if (j < k) {
+            __builtin_nontemporal_store(codes, q_out + (size_t)dj[j] * H16 + c);
+            if (first_of_block) scales[(size_t)dj[j] * B + b] = byte;
+        }
+    }
+}
+
 template <int GL>
 hipError_t launch_gl(const void* x, const int32_t* dest_of_src, int T, int H, int k, int group, void* q_out,
                      float* scales, hipStream_t stream) {
@@ -76,6 +128,23 @@ hipError_t launch_gl(const void* x, const int32_t* dest_of_src, int T, int H, in
 }
 
 }  // namespace
+
+hipError_t launch_expand_rows_mxfp8(const void* x, const int32_t* dest_of_src, int T, int H, int k, void* q_out,
+                                    uint8_t* scales, hipStream_t stream) {
+    const uint32_t H16 = (uint32_t)H / 8;
+    const uint32_t n = (uint32_t)T * H16;
+    const uint32_t blocks = (n + kThreads - 1) / kThreads;
+    const uint32_t B = (uint32_t)(H / 32);
+    const u32x4* xs = static_cast<const u32x4*>(x);
+    u32x2* q = static_cast<u32x2*>(q_out);
+    if (H16 % kWave == 0)
+        expand_rows_mxfp8_kernel<true><<<blocks, kThreads, 0, stream>>>(xs, dest_of_src, n, H16, make_fastdiv(H16), k,
+                                                                        B, q, scales);
+    else
+        expand_rows_mxfp8_kernel<false><<<blocks, kThreads, 0, stream>>>(xs, dest_of_src, n, H16, make_fastdiv(H16),
+                                                                         k, B, q, scales);
+    return hipGetLastError();
+}
 
 hipError_t launch_expand_rows_fp8(const void* x, const int32_t* dest_of_src, int T, int H, int k, int group,
                                   void* q_out, float* scales, hipStream_t stream) {

@@ -256,6 +256,23 @@ def test_expand_fp8_argument_errors(lib):
     assert call(T=0, x=None, d=None, q=None, sc=None) == "MOE_OK"
 
 
+def test_expand_mxfp8_argument_errors(lib):
+    def call(x=FAKE, d=FAKE, T=4, H=256, k=2, q=FAKE, sc=FAKE):
+        return status(lib, lib.moe_expand_rows_mxfp8(x, d, T, H, k, q, sc, None))
+
+    assert call(H=48) == "MOE_ERR_SHAPE"       # 16-byte rows, but not whole 32-column blocks
+    assert call(H=100) == "MOE_ERR_ALIGN"
+    assert call(k=0) == "MOE_ERR_SHAPE"
+    assert call(k=17) == "MOE_ERR_SHAPE"
+    assert call(sc=None) == "MOE_ERR_NULL"
+    assert call(q=None) == "MOE_ERR_NULL"
+    assert call(d=None) == "MOE_ERR_NULL"
+    assert call(q=FAKE + 4) == "MOE_ERR_ALIGN"
+    assert call(x=FAKE + 8) == "MOE_ERR_ALIGN"
+    assert call(T=-1) == "MOE_ERR_SHAPE"
+    assert call(T=0, x=None, d=None, q=None, sc=None) == "MOE_OK"
+
+
 def test_route_expand_fp8_argument_errors(lib):
     def call(T=4, E=8, k=2, pad=1, x=FAKE, H=256, group=128, q=FAKE, sc=FAKE, ws=None, wsb=0):
         return status(lib, lib.moe_route_expand_fp8(FAKE, None, T, E, k, pad, x, H, group, FAKE, FAKE, FAKE, None,

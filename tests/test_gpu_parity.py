@@ -474,6 +474,61 @@ def test_expand_fp8_qwen_workload_and_padded_layout(dev, oracle_lib):
     assert np.all(qh[~valid] == 0xAB), "fp8 expand wrote into padding rows"
 
 
+# ------------------------------------------------------------------ MXFP8 quantising expand
+def _mx_special_rows(x: np.ndarray, seed: int) -> np.ndarray:
+    """Blocks that exercise the MX scale: all zero, saturating (1.875 * 2^8 >
+    448), magnitudes spread over +-100 binades, and tiny negatives beside a
+    block maximum of 1 (their codes are -0)."""
+    import bruteforce as bf
+
+    x = x.copy()
+    T, H = x.shape
+    rng = np.random.default_rng(seed)
+    x[0, :32] = 0
+    x[-1, -32:] = np.uint16(0x3FF0)  # bf16 1.875
+    if T > 1:
+        v = rng.standard_normal(H) * np.repeat(2.0 ** rng.integers(-100, 100, H // 32), 32)
+        x[1] = bf.bf16_round_exact_np(v)
+    if T > 2:
+        v = -np.abs(rng.standard_normal(32)) * 1e-30
+        v[5] = 1.0
+        x[2, :32] = bf.bf16_round_exact_np(v)
+    return x
+
+
+@pytest.mark.parametrize("T,H,E,k", [(1, 32, 4, 1), (17, 256, 8, 2), (300, 2048, 128, 8), (77, 544, 17, 5),
+                                     (65, 4096, 64, 16), (33, 7168, 256, 8), (40, 96, 6, 3), (1023, 1408, 64, 6)])
+def test_expand_mxfp8_matches_oracle(dev, oracle_lib, T, H, E, k):
+    import torch
+    import moe_glue_amd as mg
+
+    _log(f"[expand_mxfp8] T={T} H={H} E={E} k={k}")
+    cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
+    inp = inputs.make_inputs(cfg, 13, parts=("x", "logits"))
+    x = _mx_special_rows(inp["x"], 13)
+    r = oracle_lib.route(inp["logits"], k)
+    q, sc = mg.expand_rows_mxfp8(G.to_dev(x, dev), G.to_dev(r["dest_of_src"], dev), k)
+    torch.cuda.synchronize()
+    qr, scr = oracle_lib.expand_rows_mxfp8(x, r["dest_of_src"], k)
+    compare.assert_equal(G.to_host(sc), scr, "mxfp8 scale bytes")
+    compare.assert_equal(G.to_host(q), qr, "mxfp8 codes")
+
+
+def test_expand_mxfp8_qwen_workload(dev, oracle_lib):
+    import torch
+    import moe_glue_amd as mg
+
+    cfg = inputs.CONFIGS["qwen3_30b_a3b"]
+    _log(f"[expand_mxfp8] {inputs.describe(cfg)}")
+    inp = inputs.make_inputs(cfg, 0, parts=("x", "logits"))
+    r = mg.route(G.to_dev(inp["logits"], dev), cfg.k)
+    q, sc = mg.expand_rows_mxfp8(G.to_dev(inp["x"], dev), r["dest_of_src"], cfg.k)
+    torch.cuda.synchronize()
+    qr, scr = oracle_lib.expand_rows_mxfp8(inp["x"], G.to_host(r["dest_of_src"]), cfg.k)
+    compare.assert_equal(G.to_host(sc), scr, "mxfp8 scale bytes")
+    compare.assert_equal(G.to_host(q), qr, "mxfp8 codes")
+
+
 # T, E, k, H, group, pad_to; order auto folds the quantising copy into the
 # route's place step for small batches, token never, fused whenever possible
 FP8_FUSED_CASES = [(1, 8, 2, 256, 8, 1), (40, 64, 6, 512, 128, 1), (300, 128, 8, 2048, 128, 1),
