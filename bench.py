@@ -4,8 +4,8 @@ One step = the whole path on one batch: moe_route_expand (route, then the
 expansion of the token rows) -> moe_swiglu -> moe_combine (the GEMM outputs
 are seeded stand-ins already in HBM).  With --pad the first call is
 moe_route_expand_padded; with --fp8-group it is moe_route_expand_fp8 (the
-route and the quantising expand); with --mxfp8 it is moe_route, then
-moe_expand_rows_mxfp8 (E4M3 codes, one E8M0 scale byte per 32 columns).
+route and the quantising expand); with --mxfp8 it is moe_route_expand_mxfp8
+(the same with E4M3 codes and one E8M0 scale byte per 32 columns).
 The default workload is the Qwen3-30B-A3B-shaped prefill batch
 (T=4096, H=2048, E=128, k=8, I=768).
 
@@ -48,7 +48,8 @@ KERNEL_SOURCES = {"route": _ROUTE_SOURCES, "expand": ("expand.hip",), "expand_fp
                   "swiglu": ("swiglu.hip",), "combine": ("combine.hip",),
                   "route_expand": _ROUTE_SOURCES + ("dispatch.hip", "expand.hip"),
                   "route_expand_padded": _ROUTE_SOURCES + ("expand.hip",),
-                  "route_expand_fp8": _ROUTE_SOURCES + ("quant.hip",)}
+                  "route_expand_fp8": _ROUTE_SOURCES + ("quant.hip",),
+                  "route_expand_mxfp8": _ROUTE_SOURCES + ("quant.hip",)}
 
 
 def algorithmic_bytes(cfg, fp8_group: int = 0) -> dict:
@@ -62,7 +63,8 @@ def algorithmic_bytes(cfg, fp8_group: int = 0) -> dict:
     expand_mxfp8 = T * H * 2 + R * 4 + R * H + R * (H // 32)
     return {"route": route, "expand": expand, "swiglu": swiglu, "combine": combine, "route_expand": route + expand,
             "expand_mxfp8": expand_mxfp8,
-            "route_expand_padded": route + expand, "expand_fp8": expand_fp8, "route_expand_fp8": route + expand_fp8}
+            "route_expand_padded": route + expand, "expand_fp8": expand_fp8, "route_expand_fp8": route + expand_fp8,
+            "route_expand_mxfp8": route + expand_mxfp8}
 
 
 def source_digest(kernel: str) -> str:
@@ -196,6 +198,10 @@ class Sets:
                                if fp8_group else None),
                 "expand_mxfp8": ((p("x"), p("dest_of_src"), T, H, k, p("x_exp"), p("x_scales"), stream)
                                  if mxfp8 else None),
+                "route_expand_mxfp8": ((p("logits"), p("bias"), T, E, k, pad_to, p("x"), H, p("topk_ids"),
+                                        p("topk_weights"), p("expert_offsets"), p("expert_counts"),
+                                        p("dest_of_src"), p("src_of_dest"), p("x_exp"), p("x_scales"),
+                                        p("workspace"), d["workspace"].numel(), stream) if mxfp8 else None),
                 "route_expand_fp8": ((p("logits"), p("bias"), T, E, k, pad_to, p("x"), H, fp8_group, p("topk_ids"),
                                       p("topk_weights"), p("expert_offsets"), p("expert_counts"), p("dest_of_src"),
                                       p("src_of_dest"), p("x_exp"), p("x_scales"), p("workspace"),
@@ -207,6 +213,7 @@ class Sets:
         self.fns = {"route": self.lib.moe_route if pad_to == 1 else self.lib.moe_route_padded,
                     "expand": self.lib.moe_expand_rows, "expand_fp8": self.lib.moe_expand_rows_fp8,
                     "expand_mxfp8": self.lib.moe_expand_rows_mxfp8,
+                    "route_expand_mxfp8": self.lib.moe_route_expand_mxfp8,
                     "route_expand": self.lib.moe_route_expand,
                     "route_expand_padded": self.lib.moe_route_expand_padded,
                     "route_expand_fp8": self.lib.moe_route_expand_fp8, "swiglu": self.lib.moe_swiglu,
@@ -215,7 +222,7 @@ class Sets:
         # (one launch for decode batches, destination-order expand for large
         # ones, the copy in the route's place launch in between).
         if mxfp8:
-            self.calls = ["route", "expand_mxfp8", "swiglu", "combine"]
+            self.calls = ["route_expand_mxfp8", "swiglu", "combine"]
         elif fp8_group:
             self.calls = ["route_expand_fp8", "swiglu", "combine"]
         elif pad_to == 1:
@@ -420,8 +427,8 @@ def main(argv=None):
     cfg = I.CONFIGS[args.config]
     inp = I.make_inputs(cfg, args.seed)
     nsets = args.sets if args.sets > 0 else default_sets(cfg, args.pad, args.fp8_group)
-    if args.mxfp8 and (args.fp8_group or args.pad > 1):
-        print("bench.py: --mxfp8 runs unpadded without --fp8-group", file=sys.stderr)
+    if args.mxfp8 and args.fp8_group:
+        print("bench.py: --mxfp8 and --fp8-group are two scale formats; choose one", file=sys.stderr)
         return 2
     sets = Sets(inp, nsets, dev, args.pad, args.fp8_group, args.mxfp8)
     achievable, _ = copy_probe_gbps(dev)
@@ -477,7 +484,8 @@ def main(argv=None):
                           "traffic": measured_traffic(n, cfg.name)}
     # the roofline kernel: the longest call that is a single kernel (route and
     # route_expand launch several)
-    single = [n for n in names if n not in ("route", "route_expand", "route_expand_padded", "route_expand_fp8")]
+    single = [n for n in names if n not in ("route", "route_expand", "route_expand_padded", "route_expand_fp8",
+                                            "route_expand_mxfp8")]
     dominant = max(single, key=lambda n: kernels[n]["us"]) if kernels else None
     roofline = None
     if kernels:

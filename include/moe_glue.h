@@ -14,6 +14,7 @@
  *   moe_expand_rows_fp8  expand with FP8 (E4M3) quantisation per column group
  *   moe_expand_rows_mxfp8 expand with MXFP8 quantisation (E8M0 scale per 32 columns)
  *   moe_route_expand_fp8 moe_route_padded + moe_expand_rows_fp8 in one call
+ *   moe_route_expand_mxfp8 moe_route_padded + moe_expand_rows_mxfp8 in one call
  *
  * The problem statement these calls follow:
  *   - "CuTeDSL at Perplexity" (Perplexity blog), section "Mixture of Experts
@@ -241,6 +242,19 @@ moe_status moe_route_expand_fp8(const float* logits, const float* bias, int32_t 
                                 float* topk_weights, int32_t* expert_offsets, int32_t* expert_counts,
                                 int32_t* dest_of_src, int32_t* src_of_dest, uint8_t* x_expanded, float* scales,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_route_padded followed by moe_expand_rows_mxfp8, in one call, as
+ * moe_route_expand_fp8 is for moe_expand_rows_fp8 (same launch choices;
+ * padding rows of x_expanded and scales are not written).  scales is
+ * [rows, H/32] E8M0 bytes.  The workspace must hold
+ * moe_route_workspace_bytes(T, E, k) bytes (16-byte aligned) whenever T > 64;
+ * for T <= 64 it may be NULL.  Layouts, limits, alignment and errors: the
+ * union of moe_route_padded's and moe_expand_rows_mxfp8's. */
+moe_status moe_route_expand_mxfp8(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                                  int32_t pad_to, const uint16_t* x, int32_t H, int32_t* topk_ids,
+                                  float* topk_weights, int32_t* expert_offsets, int32_t* expert_counts,
+                                  int32_t* dest_of_src, int32_t* src_of_dest, uint8_t* x_expanded, uint8_t* scales,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------- SwiGLU */
 

@@ -12,6 +12,7 @@ Four calls, each a thin wrapper over the C ABI of the HIP library
     route_padded(logits, k, pad_to)    route with expert segments padded to pad_to rows
     expand_rows_fp8(x, dest, k, group) expand with FP8 E4M3 quantisation per column group
     expand_rows_mxfp8(x, dest, k)    expand with MXFP8 quantisation (E8M0 scale per 32 columns)
+    route_expand_fp8 / route_expand_mxfp8  route + the quantising expand in one call
 
 Tensors are torch CUDA (HIP) tensors; bf16 tensors use torch.bfloat16.  Work
 is enqueued on torch's current stream and nothing synchronises.  Every call
@@ -25,7 +26,7 @@ from ._binding import (E_MAX, EXPORTED, K_MAX, LIB_PATH, MoEGlueArgumentError, M
 
 __all__ = ["route", "route_workspace_bytes", "alloc_route_outputs", "route_padded", "padded_rows", "expand_rows",
            "expand_rows_fp8", "expand_rows_mxfp8",
-           "route_expand", "route_expand_padded", "route_expand_fp8", "swiglu", "combine",
+           "route_expand", "route_expand_padded", "route_expand_fp8", "route_expand_mxfp8", "swiglu", "combine",
            "copy_probe", "MoEGlueError", "MoEGlueArgumentError", "E_MAX", "K_MAX"]
 
 
@@ -182,6 +183,38 @@ def route_expand_fp8(logits, k: int, x, group: int, pad_to: int = 1, bias=None, 
                                      _ptr(out["src_of_dest"]), _ptr(out["x_expanded"]), _ptr(out["scales"]),
                                      _ptr(ws), ws.numel() if ws is not None else 0, _stream(logits.device))
     check(st, "moe_route_expand_fp8")
+    return out
+
+
+def route_expand_mxfp8(logits, k: int, x, pad_to: int = 1, bias=None, out: dict | None = None) -> dict:
+    """route_padded() (route() for pad_to = 1) and expand_rows_mxfp8() in one
+    call; see moe_route_expand_mxfp8 in include/moe_glue.h.  Returns the route
+    dict plus "x_expanded" (uint8 E4M3 codes [rows, H]) and "scales" (uint8
+    E8M0 bytes [rows, H/32]); padding rows are not written."""
+    torch = _torch()
+    _need_gpu("logits", logits, torch.float32, 2)
+    _need_gpu("x", x, torch.bfloat16, 2)
+    T, E = logits.shape
+    if x.shape[0] != T:
+        raise MoEGlueArgumentError(2, f"x has {x.shape[0]} rows, logits has T={T}")
+    H = x.shape[1]
+    if bias is not None:
+        _need_gpu("bias", bias, torch.float32, 1)
+    P = max(1, padded_rows(T, E, k, pad_to)) if pad_to > 1 else max(1, T * k)
+    if out is None:
+        out = alloc_route_outputs(T, E, k, logits.device)
+        out["src_of_dest"] = torch.empty((P,), dtype=torch.int32, device=logits.device)
+    if out.get("x_expanded") is None:
+        out["x_expanded"] = torch.empty((P, H), dtype=torch.uint8, device=x.device)
+    if out.get("scales") is None:
+        out["scales"] = torch.empty((P, max(1, H // 32)), dtype=torch.uint8, device=x.device)
+    ws = out["workspace"]
+    st = load().moe_route_expand_mxfp8(_ptr(logits), _ptr(bias), T, E, k, pad_to, _ptr(x), H,
+                                       _ptr(out["topk_ids"]), _ptr(out["topk_weights"]), _ptr(out["expert_offsets"]),
+                                       _ptr(out.get("expert_counts")), _ptr(out["dest_of_src"]),
+                                       _ptr(out["src_of_dest"]), _ptr(out["x_expanded"]), _ptr(out["scales"]),
+                                       _ptr(ws), ws.numel() if ws is not None else 0, _stream(logits.device))
+    check(st, "moe_route_expand_mxfp8")
     return out
 
 

@@ -368,33 +368,38 @@ moe_status moe_expand_rows_mxfp8(const uint16_t* x, const int32_t* dest_of_src, 
                     "moe_expand_rows_mxfp8 launch");
 }
 
-moe_status moe_route_expand_fp8(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
-                                int32_t pad_to, const uint16_t* x, int32_t H, int32_t group, int32_t* topk_ids,
-                                float* topk_weights, int32_t* expert_offsets, int32_t* expert_counts,
-                                int32_t* dest_of_src, int32_t* src_of_dest, uint8_t* x_expanded, float* scales,
-                                void* workspace, size_t workspace_bytes, void* stream) {
-    const char* fn = "moe_route_expand_fp8";
-    moe_status s = check_route_args(fn, logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, dest_of_src,
-                                    src_of_dest);
-    if (s != MOE_OK) return s;
-    s = check_pad(fn, T, E, k, pad_to);
-    if (s != MOE_OK) return s;
-    s = check_fp8_args(fn, x, dest_of_src, T, H, k, group, x_expanded, scales);
-    if (s != MOE_OK) return s;
+}  // extern "C"
+
+namespace {
+
+// moe_route_expand_fp8 / moe_route_expand_mxfp8: the route (padded for
+// pad_to > 1), then the quantising expand with fp32 scales per `group`
+// columns or, with mx, E8M0 scales per 32 columns.  Arguments already checked
+// except the route workspace.
+moe_status route_expand_quant(const char* fn, const float* logits, const float* bias, int32_t T, int32_t E,
+                              int32_t k, int32_t pad_to, const uint16_t* x, int32_t H, int32_t group, bool mx,
+                              int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                              int32_t* expert_counts, int32_t* dest_of_src, int32_t* src_of_dest,
+                              uint8_t* x_expanded, void* scales, void* workspace, size_t workspace_bytes,
+                              void* stream) {
     const moe::RouteVariant requested = requested_route_variant();
     const hipStream_t st = static_cast<hipStream_t>(stream);
     moe::RouteArgs a{logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, expert_counts,
                      dest_of_src, src_of_dest, workspace, pad_to, /*row_list=*/nullptr, {}};
-    if (T <= moe::kRouteSmallDispatchMaxTokens && requested == moe::RouteVariant::Auto) {
+    const auto set_copy = [&]() {
         a.copy_x = x;
         a.copy_out = x_expanded;
         a.copy_H = H;
         a.copy_group = group;
         a.copy_scales = scales;
-        return from_hip(moe::launch_route_expand_small(a, st), "moe_route_expand_fp8 launch");
+        a.copy_mx = mx;
+    };
+    if (T <= moe::kRouteSmallDispatchMaxTokens && requested == moe::RouteVariant::Auto) {
+        set_copy();
+        return from_hip(moe::launch_route_expand_small(a, st), fn);
     }
     const moe::RouteVariant v = moe::route_pick_variant(T, E, requested);
-    s = check_route_workspace(fn, T, E, k, true, v, workspace, workspace_bytes);
+    moe_status s = check_route_workspace(fn, T, E, k, true, v, workspace, workspace_bytes);
     if (s != MOE_OK) return s;
     // The quantising copy folds into the two-launch route's place step when
     // one of its workgroups holds a whole row and the codes are small: measured
@@ -409,17 +414,54 @@ moe_status moe_route_expand_fp8(const float* logits, const float* bias, int32_t 
     const bool small = (int64_t)T * k * H <= kQuantisingFoldMaxBytes;
     const bool fold = v == moe::RouteVariant::TwoPass && T > 0 && H <= moe::route_quantising_place_max_h() &&
                       !forced_token && (small || forced_fold);
-    if (fold) {
-        a.copy_x = x;
-        a.copy_out = x_expanded;
-        a.copy_H = H;
-        a.copy_group = group;
-        a.copy_scales = scales;
-    }
-    s = from_hip(moe::launch_route(a, v, st), "moe_route_expand_fp8 launch (route)");
+    if (fold) set_copy();
+    s = from_hip(moe::launch_route(a, v, st), fn);
     if (s != MOE_OK || T == 0 || fold) return s;
-    return from_hip(moe::launch_expand_rows_fp8(x, dest_of_src, T, H, k, group, x_expanded, scales, st),
-                    "moe_route_expand_fp8 launch (expand)");
+    if (mx)
+        return from_hip(moe::launch_expand_rows_mxfp8(x, dest_of_src, T, H, k, x_expanded,
+                                                      static_cast<uint8_t*>(scales), st), fn);
+    return from_hip(moe::launch_expand_rows_fp8(x, dest_of_src, T, H, k, group, x_expanded,
+                                                static_cast<float*>(scales), st), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_route_expand_fp8(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                                int32_t pad_to, const uint16_t* x, int32_t H, int32_t group, int32_t* topk_ids,
+                                float* topk_weights, int32_t* expert_offsets, int32_t* expert_counts,
+                                int32_t* dest_of_src, int32_t* src_of_dest, uint8_t* x_expanded, float* scales,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "moe_route_expand_fp8";
+    moe_status s = check_route_args(fn, logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, dest_of_src,
+                                    src_of_dest);
+    if (s != MOE_OK) return s;
+    s = check_pad(fn, T, E, k, pad_to);
+    if (s != MOE_OK) return s;
+    s = check_fp8_args(fn, x, dest_of_src, T, H, k, group, x_expanded, scales);
+    if (s != MOE_OK) return s;
+    return route_expand_quant(fn, logits, bias, T, E, k, pad_to, x, H, group, false, topk_ids, topk_weights,
+                              expert_offsets, expert_counts, dest_of_src, src_of_dest, x_expanded, scales, workspace,
+                              workspace_bytes, stream);
+}
+
+moe_status moe_route_expand_mxfp8(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                                  int32_t pad_to, const uint16_t* x, int32_t H, int32_t* topk_ids,
+                                  float* topk_weights, int32_t* expert_offsets, int32_t* expert_counts,
+                                  int32_t* dest_of_src, int32_t* src_of_dest, uint8_t* x_expanded, uint8_t* scales,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "moe_route_expand_mxfp8";
+    moe_status s = check_route_args(fn, logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, dest_of_src,
+                                    src_of_dest);
+    if (s != MOE_OK) return s;
+    s = check_pad(fn, T, E, k, pad_to);
+    if (s != MOE_OK) return s;
+    s = check_mxfp8_args(fn, x, dest_of_src, T, H, k, x_expanded, scales);
+    if (s != MOE_OK) return s;
+    return route_expand_quant(fn, logits, bias, T, E, k, pad_to, x, H, 32, true, topk_ids, topk_weights,
+                              expert_offsets, expert_counts, dest_of_src, src_of_dest, x_expanded, scales, workspace,
+                              workspace_bytes, stream);
 }
 
 moe_status moe_swiglu(const uint16_t* h, int32_t R, int32_t I, uint16_t* act, void* stream) {

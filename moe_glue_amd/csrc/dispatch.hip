@@ -16,7 +16,8 @@
 // workgroups, each storing every ks-th of the k destination rows: at decode
 // sizes the column blocks alone would leave a handful of CUs issuing all the
 // stores, and routing once more per workgroup costs less than that.  The same
-// kernel serves the padded layout (pad_to) and the FP8 quantising copy.
+// kernel serves the padded layout (pad_to) and the FP8 and MXFP8 quantising
+// copies.
 #include "fp8_common.h"
 #include "place_copy.h"
 #include "route_common.h"
@@ -36,7 +37,7 @@ __global__ __launch_bounds__((SingleShape<G>::THREADS)) void route_expand_small_
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ expert_counts, int32_t* __restrict__ dest_of_src, int32_t* __restrict__ src_of_dest,
     const u32x4* __restrict__ x, uint32_t H16, FastDiv div_h16, int ks, void* __restrict__ out,
-    float* __restrict__ scales, uint32_t G_groups, int gl) {
+    void* __restrict__ scales, uint32_t G_groups, int gl, bool mx) {
     using S = SingleShape<G>;
     __shared__ int32_t ids_lds[kRouteSmallDispatchMaxTokens * kKMax];
     __shared__ unsigned long long masks[kEMax];
@@ -74,22 +75,23 @@ __global__ __launch_bounds__((SingleShape<G>::THREADS)) void route_expand_small_
             for (int j = js; j < k; j += ks) store_stream(x_exp + (size_t)s_dest[t * k + j] * H16 + c, v);
         }
     } else {
-        // E4M3 as moe_expand_rows_fp8: a scale group is gl consecutive lanes of
-        // one row (H/8 is a multiple of gl, so no group straddles the end of x)
+        // E4M3 as moe_expand_rows_fp8 (or, with mx, moe_expand_rows_mxfp8): a
+        // scale group is gl consecutive lanes of one row (H/8 is a multiple of
+        // gl, so no group straddles the end of x)
         float f[8];
         unpack8(v, f);
-        const float amax = __builtin_bit_cast(float, group_abs_max(abs_max_bits8(f), gl));
+        const uint32_t amax_bits = group_abs_max(abs_max_bits8(f), gl);
         if (i < n) {
             const uint32_t t = fastdiv(i, div_h16);
             const uint32_t c = i - t * H16;
-            const float scale = e4m3_scale(amax);
-            const u32x2 codes = quantize8_e4m3(f, e4m3_inverse_scale(amax));
+            const BlockScale bs = block_scale(amax_bits, mx);
+            const u32x2 codes = quantize8_e4m3(f, bs.inv);
             const bool first_of_group = (threadIdx.x % (uint32_t)gl) == 0;
             u32x2* q_out = static_cast<u32x2*>(out);
             for (int j = js; j < k; j += ks) {
                 const size_t d = (size_t)s_dest[t * k + j];
                 __builtin_nontemporal_store(codes, q_out + d * H16 + c);
-                if (first_of_group) scales[d * G_groups + c / (uint32_t)gl] = scale;
+                if (first_of_group) store_block_scale(scales, d * G_groups + c / (uint32_t)gl, bs, mx);
             }
         }
     }
@@ -109,11 +111,11 @@ hipError_t launch_gv(const RouteArgs& a, hipStream_t stream) {
         route_expand_small_kernel<G, V, kCopyFp8><<<blocks * ks, S::THREADS, 0, stream>>>(
             a.logits, a.bias, a.T, a.E, a.k, a.pad_to, a.topk_ids, a.topk_weights, a.expert_offsets, a.expert_counts,
             a.dest_of_src, a.src_of_dest, x, H16, make_fastdiv(H16), ks, a.copy_out, a.copy_scales,
-            (uint32_t)(a.copy_H / a.copy_group), a.copy_group / 8);
+            (uint32_t)(a.copy_H / a.copy_group), a.copy_group / 8, a.copy_mx);
     else
         route_expand_small_kernel<G, V, kCopyBf16><<<blocks * ks, S::THREADS, 0, stream>>>(
             a.logits, a.bias, a.T, a.E, a.k, a.pad_to, a.topk_ids, a.topk_weights, a.expert_offsets, a.expert_counts,
-            a.dest_of_src, a.src_of_dest, x, H16, make_fastdiv(H16), ks, a.copy_out, nullptr, 0, 1);
+            a.dest_of_src, a.src_of_dest, x, H16, make_fastdiv(H16), ks, a.copy_out, nullptr, 0, 1, false);
     return hipGetLastError();
 }
 

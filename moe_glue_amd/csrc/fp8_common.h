@@ -44,6 +44,49 @@ __device__ __forceinline__ uint32_t group_abs_max(uint32_t m, int gl) {
 __device__ __forceinline__ float e4m3_scale(float amax) { return amax / 448.0f; }
 __device__ __forceinline__ float e4m3_inverse_scale(float amax) { return amax > 0.0f ? 448.0f / amax : 0.0f; }
 
+// OCP microscaling (MX) block scale from the fp32 bits of the block's |x|
+// maximum, a bf16 value widened to fp32: e = max(floor(log2 amax) - 8, -127)
+// (8 is the exponent of E4M3's largest normal), -127 for a zero or
+// subnormal maximum; floor(log2 amax) of a normal amax is its exponent field
+// minus 127.  The E8M0 byte is e + 127, and 2^-e -- built from its bits,
+// 127 - e in [8, 254] for every finite maximum -- is a normal fp32, so
+// x * 2^-e is exact.
+__device__ __forceinline__ int mx_scale_exponent(uint32_t amax_bits) {
+    const int ef = (int)(amax_bits >> 23);
+    return ef == 0 ? -127 : max(ef - 127 - 8, -127);
+}
+__device__ __forceinline__ float mx_inverse_scale(int e) { return __builtin_bit_cast(float, (uint32_t)(127 - e) << 23); }
+
+// A block's scale in either format: fp32 amax/448 (scale) or MX (byte), and
+// the factor the codes are taken of.
+struct BlockScale {
+    float inv;
+    float scale;
+    uint8_t byte;
+};
+__device__ __forceinline__ BlockScale block_scale(uint32_t amax_bits, bool mx) {
+    BlockScale b;
+    if (mx) {
+        const int e = mx_scale_exponent(amax_bits);
+        b.inv = mx_inverse_scale(e);
+        b.scale = 0.0f;
+        b.byte = (uint8_t)(e + 127);
+    } else {
+        const float amax = __builtin_bit_cast(float, amax_bits);
+        b.inv = e4m3_inverse_scale(amax);
+        b.scale = e4m3_scale(amax);
+        b.byte = 0;
+    }
+    return b;
+}
+// Entry idx of a scale array: fp32 scales, or E8M0 bytes for MX.
+__device__ __forceinline__ void store_block_scale(void* scales, size_t idx, const BlockScale& b, bool mx) {
+    if (mx)
+        static_cast<uint8_t*>(scales)[idx] = b.byte;
+    else
+        static_cast<float*>(scales)[idx] = b.scale;
+}
+
 // The 8 codes of f[0..7] times inv, in memory order.
 __device__ __forceinline__ u32x2 quantize8_e4m3(const float (&f)[8], float inv) {
     u32x2 codes;

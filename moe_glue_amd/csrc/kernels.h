@@ -80,13 +80,15 @@ struct RouteArgs {
     // When set (two-launch variant only, not with row_list): the place step
     // also copies x [T, copy_H] bf16 to copy_out in token order (the expand;
     // with copy_group > 0 quantised to E4M3 codes plus copy_scales, one scale
-    // per copy_group columns), keeping the slot ranks in the workspace's
+    // per copy_group columns: fp32 amax/448, or with copy_mx an E8M0 byte per
+    // 32 columns), keeping the slot ranks in the workspace's
     // row-list area meanwhile.
     const void* copy_x;
     void* copy_out;
     int copy_H;
     int copy_group;
-    float* copy_scales;
+    void* copy_scales;  // float [rows, H/copy_group], or uint8_t E8M0 [rows, H/32] with copy_mx
+    bool copy_mx;
 };
 
 // Keys per lane (8 above 32 experts, else 4) and lanes that cooperate on one token.
@@ -126,7 +128,7 @@ hipError_t launch_route(const RouteArgs& a, RouteVariant variant, hipStream_t st
 // Route + expand in one launch for T <= kRouteSmallDispatchMaxTokens: every
 // workgroup recomputes the routing in LDS and copies its share of the rows.
 constexpr int kRouteSmallDispatchMaxTokens = 64;
-// The copy is RouteArgs::copy_* (bf16, or E4M3 with copy_group > 0); segments
+// The copy is RouteArgs::copy_* (bf16, or E4M3 with copy_group > 0, MX scales with copy_mx); segments
 // padded to pad_to rows.
 hipError_t launch_route_expand_small(const RouteArgs& a, hipStream_t stream);
 

@@ -26,7 +26,8 @@ constexpr int kPlaceCopyThreads = 1024;  // lanes per workgroup of the place ste
 struct PlaceCopy {
     const u32x4* x;
     void* out;        // u32x4 rows (bf16) or u32x2 rows (E4M3 codes)
-    float* scales;    // kCopyFp8: [rows, G]
+    void* scales;     // kCopyFp8: [rows, G] fp32, or E8M0 bytes with mx
+    bool mx;          // kCopyFp8: OCP microscaling scales (G = H/32, gl = 4)
     uint32_t H16;
     uint32_t G;       // kCopyFp8: scale groups per row
     int gl;           // kCopyFp8: lanes per scale group (group / 8)

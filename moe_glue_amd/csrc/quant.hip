@@ -61,13 +61,9 @@ __global__ __launch_bounds__(kThreads) void expand_rows_fp8_kernel(const u32x4* 
 
 // MXFP8 (OCP microscaling; "CuTeDSL at Perplexity", Blackwell support, takes
 // the MXFP8 absolute maximum over 32 elements): a block of 32 columns is 4
-// consecutive lanes.  Its scale is the power of two 2^e, e = max(floor(log2
-// amax) - 8, -127), stored as the E8M0 byte e + 127; the codes are
+// consecutive lanes.  Its scale is the power of two 2^e of fp8_common.h's
+// mx_scale_exponent, stored as the E8M0 byte e + 127; the codes are
 // E4M3(clamp(x * 2^-e, +-448)), and multiplying by a power of two is exact.
-// amax is a bf16 value widened to fp32, so for a normal amax floor(log2 amax)
-// is its exponent field minus 127; a zero or subnormal amax (field 0) takes
-// e = -127.  2^-e is built from its bits: 127 - e lies in [8, 254] for every
-// finite amax, a normal fp32.
 constexpr int kMxLanes = 4;  // 32 columns / 8 per lane
 
 template <bool ROW_PER_WAVE>
@@ -86,9 +82,8 @@ __global__ __launch_bounds__(kThreads) void expand_rows_mxfp8_kernel(const u32x4
     unpack8(v, f);
     const uint32_t amax_bits = group_reduce<kMxLanes, Op::Max>(abs_max_bits8(f));
     if (!live) return;
-    const int ef = (int)(amax_bits >> 23);  // |x| bits: no sign
-    const int e = ef == 0 ? -127 : max(ef - 127 - 8, -127);
-    const float inv = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);
+    const int e = mx_scale_exponent(amax_bits);
+    const float inv = mx_inverse_scale(e);
     const uint8_t byte = (uint8_t)(e + 127);
     const u32x2 codes = quantize8_e4m3(f, inv);
     uint32_t t = fastdiv(i, div_h16);

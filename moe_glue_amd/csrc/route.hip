@@ -463,16 +463,16 @@ __device__ __forceinline__ void scan_place(
             const bool present = copy_item<COPY>(cp, chunk, threadIdx.x + m * kFusedThreads, ntok, tl, col);
             float f[8];
             unpack8(xv[m], f);
-            const float amax = __builtin_bit_cast(float, group_abs_max(abs_max_bits8(f), cp.gl));
+            const uint32_t amax_bits = group_abs_max(abs_max_bits8(f), cp.gl);
             if (present) {
-                const float scale = e4m3_scale(amax);
-                const u32x2 codes = quantize8_e4m3(f, e4m3_inverse_scale(amax));
+                const BlockScale bs = block_scale(amax_bits, cp.mx);
+                const u32x2 codes = quantize8_e4m3(f, bs.inv);
                 const bool first_of_group = (threadIdx.x % (uint32_t)cp.gl) == 0;
                 const uint32_t g = col / (uint32_t)cp.gl;
                 for (int j = 0; j < k; ++j) {
                     const size_t d = (size_t)s_dest[tl * k + j];
                     __builtin_nontemporal_store(codes, q_out + d * H16 + col);
-                    if (first_of_group) cp.scales[d * cp.G + g] = scale;
+                    if (first_of_group) store_block_scale(cp.scales, d * cp.G + g, bs, cp.mx);
                 }
             }
         }
@@ -513,6 +513,7 @@ void launch_scan_place(bool list, int nwg, const u32x4* rows8, int nb, int tok_p
         cp.x = static_cast<const u32x4*>(a.copy_x);
         cp.out = a.copy_out;
         cp.scales = a.copy_scales;
+        cp.mx = a.copy_mx;
         if (mode == kCopyFp8) {
             route_place_copy_kernel<QP, kCopyFp8><<<nwg * cp.chunks, kFusedThreads, 0, stream>>>(
                 rows8, nb, tok_per_row, a.T, a.E, a.k, a.pad_to, a.topk_ids, ranks, a.dest_of_src, a.src_of_dest,

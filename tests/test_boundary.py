@@ -273,6 +273,24 @@ def test_expand_mxfp8_argument_errors(lib):
     assert call(T=0, x=None, d=None, q=None, sc=None) == "MOE_OK"
 
 
+def test_route_expand_mxfp8_argument_errors(lib):
+    def call(T=4, E=8, k=2, pad=1, x=FAKE, H=256, q=FAKE, sc=FAKE, ws=None, wsb=0):
+        return status(lib, lib.moe_route_expand_mxfp8(FAKE, None, T, E, k, pad, x, H, FAKE, FAKE, FAKE, None,
+                                                      FAKE, FAKE, q, sc, ws, wsb, None))
+
+    assert call(pad=0) == "MOE_ERR_SHAPE"
+    assert call(k=9) == "MOE_ERR_SHAPE"
+    assert call(H=48) == "MOE_ERR_SHAPE"
+    assert call(H=100) == "MOE_ERR_ALIGN"
+    assert call(x=None) == "MOE_ERR_NULL"
+    assert call(sc=None) == "MOE_ERR_NULL"
+    assert call(q=FAKE + 4) == "MOE_ERR_ALIGN"
+    assert call(T=65) == "MOE_ERR_WORKSPACE"
+    need = lib.moe_route_workspace_bytes(4096, 128, 8)
+    assert call(T=4096, E=128, k=8, H=2048, ws=FAKE, wsb=need - 1) == "MOE_ERR_WORKSPACE"
+    assert b"moe_route_expand_mxfp8" in lib.moe_last_error()
+
+
 def test_route_expand_fp8_argument_errors(lib):
     def call(T=4, E=8, k=2, pad=1, x=FAKE, H=256, group=128, q=FAKE, sc=FAKE, ws=None, wsb=0):
         return status(lib, lib.moe_route_expand_fp8(FAKE, None, T, E, k, pad, x, H, group, FAKE, FAKE, FAKE, None,

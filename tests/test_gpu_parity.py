@@ -575,6 +575,46 @@ def test_route_expand_fp8_matches_oracle(dev, oracle_lib, monkeypatch, order, T,
     assert np.all(sch[~valid] == -7.0) and np.all(got["scales"][n:] == -7.0), "scales written into padding rows"
 
 
+MX_FUSED_CASES = [(T, E, k, H, M) for (T, E, k, H, group, M) in FP8_FUSED_CASES if H % 32 == 0]
+
+
+@pytest.mark.parametrize("order", ["auto", "token", "fused"])
+@pytest.mark.parametrize("T,E,k,H,M", MX_FUSED_CASES)
+def test_route_expand_mxfp8_matches_oracle(dev, oracle_lib, monkeypatch, order, T, E, k, H, M):
+    """moe_route_expand_mxfp8 = route (padded for M > 1) then the MXFP8
+    expand; padding rows of the codes and scale bytes stay untouched."""
+    import torch
+    import moe_glue_amd as mg
+
+    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", order)
+    _log(f"[route_expand_mxfp8] T={T} E={E} k={k} H={H} pad_to={M} order={order}")
+    cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8, bias_std=0.5 if E % 2 == 0 else 0.0)
+    inp = inputs.make_inputs(cfg, 10, parts=("x", "logits"))
+    x = _mx_special_rows(inp["x"], 10) if T > 0 else inp["x"]
+    bias = None if inp["bias"] is None else G.to_dev(inp["bias"], dev)
+    P = mg.padded_rows(T, E, k, M) if M > 1 else T * k
+    out = mg.alloc_route_outputs(T, E, k, dev)
+    out["src_of_dest"] = torch.empty((max(P, 1),), dtype=torch.int32, device=dev)
+    out["x_expanded"] = torch.full((max(P, 1), H), 0xAB, dtype=torch.uint8, device=dev)
+    out["scales"] = torch.full((max(P, 1), H // 32), 0xCD, dtype=torch.uint8, device=dev)
+    r = mg.route_expand_mxfp8(G.to_dev(inp["logits"], dev), k, G.to_dev(x, dev), M, bias, out=out)
+    torch.cuda.synchronize()
+    got = G.route_host(r)
+    ref = (oracle_lib.route_padded(inp["logits"], k, M, inp["bias"]) if M > 1
+           else oracle_lib.route(inp["logits"], k, inp["bias"]))
+    n = int(ref["expert_offsets"][E])
+    got["src_of_dest"] = got["src_of_dest"][:n]
+    compare.assert_route_equal({key: v for key, v in got.items() if key not in ("x_expanded", "scales")}, ref,
+                               f"route_expand_mxfp8 T={T} E={E} k={k} M={M}")
+    qr, scr = oracle_lib.expand_rows_mxfp8(x, ref["dest_of_src"], k, rows=n)
+    valid = ref["src_of_dest"] >= 0
+    qh, sch = got["x_expanded"][:n], got["scales"][:n]
+    compare.assert_equal(qh[valid], qr[valid], "mxfp8 codes (valid rows)")
+    compare.assert_equal(sch[valid], scr[valid], "mxfp8 scale bytes (valid rows)")
+    assert np.all(qh[~valid] == 0xAB) and np.all(got["x_expanded"][n:] == 0xAB), "codes written into padding rows"
+    assert np.all(sch[~valid] == 0xCD) and np.all(got["scales"][n:] == 0xCD), "scales written into padding rows"
+
+
 @pytest.mark.parametrize("T,E,k,H,I,variant,order", [(32, 128, 8, 2048, 768, "auto", "auto"),
                                                      (700, 64, 6, 256, 64, "two", "grouped"),
                                                      (300, 128, 8, 512, 32, "three", "token"),
