@@ -97,8 +97,8 @@ hipError_t launch_u(const void* x, const int32_t* dest_of_src, int T, int H, int
 // row pair (or row), so the slices cover its whole source whenever
 // H/8 <= 1024 k (at rows <= 512 vectors they cover it 2k times over); past
 // that only a part is warmed, which costs time, not correctness.  Loads
-// outside the group are skipped.  Measured at the Qwen3-30B-A3B shape with x in HBM:
-// 27.0 -> 23.0 us (4 vectors per lane; 24.4 with 1, 23.1 with 2).
+// outside the group are skipped.  Measured at the Qwen3-30B-A3B shape with x
+// in HBM: 27.0 -> 23.0 us (4 vectors per lane; 24.4 with 1, 23.1 with 2).
 constexpr int kGroupedThreads = 256;
 constexpr int kGroupedItems = 512;  // 16-byte vectors per workgroup: small windows
 constexpr int kGroupedPrefetch = 4;  // source vectors per lane touched up front
@@ -126,7 +126,6 @@ __device__ __forceinline__ void copy_group_rows(const u32x4* __restrict__ x, con
             if (i0 + u * kGroupedThreads < items) store_stream(x_exp + (size_t)ent[u].x * H16 + col[u], v[u]);
     }
 }
-
 
 template <int U>
 __global__ __launch_bounds__(kGroupedThreads) void expand_grouped_kernel(const u32x4* __restrict__ x,
