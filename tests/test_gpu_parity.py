@@ -615,6 +615,44 @@ def test_route_expand_mxfp8_matches_oracle(dev, oracle_lib, monkeypatch, order, 
     assert np.all(sch[~valid] == 0xCD) and np.all(got["scales"][n:] == 0xCD), "scales written into padding rows"
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp8"])
+@pytest.mark.parametrize("variant", ["single", "two", "three"])
+@pytest.mark.parametrize("T,E,k,H,M", [(48, 128, 8, 2048, 1), (48, 64, 6, 512, 16), (700, 128, 8, 1024, 1),
+                                       (700, 17, 5, 256, 8)])
+def test_route_expand_quantised_every_route_variant(dev, oracle_lib, monkeypatch, fmt, variant, T, E, k, H, M):
+    """The combined quantising calls with the route variant forced: the
+    single-workgroup route followed by the separate quantising expand, and
+    the two- and three-launch routes (folded copy or separate expand)."""
+    import torch
+    import moe_glue_amd as mg
+
+    if variant == "single" and T > 256:
+        pytest.skip("single-workgroup route covers T <= 256")
+    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
+    _log(f"[route_expand_{fmt}] T={T} E={E} k={k} H={H} pad_to={M} variant={variant}")
+    cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
+    inp = inputs.make_inputs(cfg, 11, parts=("x", "logits"))
+    x = _mx_special_rows(inp["x"], 11)
+    if fmt == "fp8":
+        r = mg.route_expand_fp8(G.to_dev(inp["logits"], dev), k, G.to_dev(x, dev), 32, M)
+    else:
+        r = mg.route_expand_mxfp8(G.to_dev(inp["logits"], dev), k, G.to_dev(x, dev), M)
+    torch.cuda.synchronize()
+    got = G.route_host(r)
+    ref = oracle_lib.route_padded(inp["logits"], k, M) if M > 1 else oracle_lib.route(inp["logits"], k)
+    n = int(ref["expert_offsets"][E])
+    got["src_of_dest"] = got["src_of_dest"][:n]
+    compare.assert_route_equal({key: v for key, v in got.items() if key not in ("x_expanded", "scales")}, ref,
+                               f"route_expand_{fmt} T={T} variant={variant}")
+    if fmt == "fp8":
+        qr, scr = oracle_lib.expand_rows_fp8(x, ref["dest_of_src"], k, 32, rows=n)
+    else:
+        qr, scr = oracle_lib.expand_rows_mxfp8(x, ref["dest_of_src"], k, rows=n)
+    valid = ref["src_of_dest"] >= 0
+    compare.assert_equal(got["x_expanded"][:n][valid], qr[valid], f"{fmt} codes (valid rows)")
+    compare.assert_equal(got["scales"][:n][valid], scr[valid], f"{fmt} scales (valid rows)")
+
+
 @pytest.mark.parametrize("T,E,k,H,I,variant,order", [(32, 128, 8, 2048, 768, "auto", "auto"),
                                                      (700, 64, 6, 256, 64, "two", "grouped"),
                                                      (300, 128, 8, 512, 32, "three", "token"),
