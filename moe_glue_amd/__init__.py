@@ -58,6 +58,48 @@ def _need_gpu(name: str, t, dtype=None, ndim=None) -> None:
         raise MoEGlueArgumentError(2, f"{name} must have {ndim} dims (got shape {tuple(t.shape)})")
 
 
+def _check_bias(bias, E: int) -> None:
+    """bias: None, or fp32 [E] on the GPU (the kernels read bias[e] for every e < E)."""
+    if bias is None:
+        return
+    torch = _torch()
+    _need_gpu("bias", bias, torch.float32, 1)
+    if bias.shape[0] != E:
+        raise MoEGlueArgumentError(2, f"bias has {bias.shape[0]} entries, logits has E={E}")
+
+
+def _check_vec(name: str, t, dtype, n: int, at_least: bool = False) -> None:
+    """t: a GPU tensor of `dtype` with exactly n (or at least n) elements."""
+    _need_gpu(name, t, dtype)
+    if (t.numel() < n) if at_least else (t.numel() != n):
+        raise MoEGlueArgumentError(2, f"{name} has {t.numel()} entries, expected {'at least ' if at_least else ''}{n}")
+
+
+def _check_route_out(out: dict, T: int, E: int, k: int, rows: int) -> None:
+    """Caller-supplied route outputs: ids/weights/dest_of_src [T*k], offsets
+    [E+1], counts [E] (or absent), src_of_dest at least `rows` entries (the
+    padded row bound for a padded layout).  The workspace size is checked by
+    the library itself, which receives its byte count."""
+    torch = _torch()
+    _check_vec("topk_ids", out.get("topk_ids"), torch.int32, T * k)
+    _check_vec("topk_weights", out.get("topk_weights"), torch.float32, T * k)
+    _check_vec("expert_offsets", out.get("expert_offsets"), torch.int32, E + 1)
+    if out.get("expert_counts") is not None:
+        _check_vec("expert_counts", out["expert_counts"], torch.int32, E)
+    _check_vec("dest_of_src", out.get("dest_of_src"), torch.int32, T * k)
+    _check_vec("src_of_dest", out.get("src_of_dest"), torch.int32, rows, at_least=True)
+    ws = out.get("workspace")
+    if ws is not None:
+        _need_gpu("workspace", ws)
+
+
+def _check_rows_out(name: str, t, rows: int, width: int, dtype) -> None:
+    """t: a 2-D GPU tensor of `dtype`, [>= rows, width]."""
+    _need_gpu(name, t, dtype, 2)
+    if t.shape[0] < rows or t.shape[1] != width:
+        raise MoEGlueArgumentError(2, f"{name} is {list(t.shape)}, expected [>= {rows}, {width}]")
+
+
 def route_workspace_bytes(T: int, E: int, k: int) -> int:
     return int(load().moe_route_workspace_bytes(T, E, k))
 
@@ -82,12 +124,10 @@ def route(logits, k: int, bias=None, out: dict | None = None) -> dict:
     torch = _torch()
     _need_gpu("logits", logits, torch.float32, 2)
     T, E = logits.shape
-    if bias is not None:
-        _need_gpu("bias", bias, torch.float32, 1)
-        if bias.shape[0] != E:
-            raise MoEGlueArgumentError(2, f"bias has {bias.shape[0]} entries, logits has E={E}")
+    _check_bias(bias, E)
     if out is None:
         out = alloc_route_outputs(T, E, k, logits.device)
+    _check_route_out(out, T, E, k, T * k)
     ws = out["workspace"]
     lib = load()
     st = lib.moe_route(_ptr(logits), _ptr(bias), T, E, k, _ptr(out["topk_ids"]), _ptr(out["topk_weights"]),
@@ -110,12 +150,12 @@ def route_padded(logits, k: int, pad_to: int, bias=None, out: dict | None = None
     torch = _torch()
     _need_gpu("logits", logits, torch.float32, 2)
     T, E = logits.shape
-    if bias is not None:
-        _need_gpu("bias", bias, torch.float32, 1)
+    _check_bias(bias, E)
     if out is None:
         out = alloc_route_outputs(T, E, k, logits.device)
         out["src_of_dest"] = torch.empty((max(1, padded_rows(T, E, k, pad_to)),), dtype=torch.int32,
                                          device=logits.device)
+    _check_route_out(out, T, E, k, padded_rows(T, E, k, pad_to))
     ws = out["workspace"]
     st = load().moe_route_padded(_ptr(logits), _ptr(bias), T, E, k, pad_to, _ptr(out["topk_ids"]),
                                  _ptr(out["topk_weights"]), _ptr(out["expert_offsets"]),
@@ -136,14 +176,15 @@ def route_expand_padded(logits, k: int, pad_to: int, x, bias=None, out: dict | N
     if x.shape[0] != T:
         raise MoEGlueArgumentError(2, f"x has {x.shape[0]} rows, logits has T={T}")
     H = x.shape[1]
-    if bias is not None:
-        _need_gpu("bias", bias, torch.float32, 1)
+    _check_bias(bias, E)
     P = max(1, padded_rows(T, E, k, pad_to))
     if out is None:
         out = alloc_route_outputs(T, E, k, logits.device)
         out["src_of_dest"] = torch.empty((P,), dtype=torch.int32, device=logits.device)
     if out.get("x_expanded") is None:
         out["x_expanded"] = torch.empty((P, H), dtype=torch.bfloat16, device=x.device)
+    _check_route_out(out, T, E, k, padded_rows(T, E, k, pad_to))
+    _check_rows_out("x_expanded", out["x_expanded"], padded_rows(T, E, k, pad_to), H, torch.bfloat16)
     ws = out["workspace"]
     st = load().moe_route_expand_padded(_ptr(logits), _ptr(bias), T, E, k, pad_to, _ptr(x), H, _ptr(out["topk_ids"]),
                                         _ptr(out["topk_weights"]), _ptr(out["expert_offsets"]),
@@ -166,8 +207,7 @@ def route_expand_fp8(logits, k: int, x, group: int, pad_to: int = 1, bias=None, 
     if x.shape[0] != T:
         raise MoEGlueArgumentError(2, f"x has {x.shape[0]} rows, logits has T={T}")
     H = x.shape[1]
-    if bias is not None:
-        _need_gpu("bias", bias, torch.float32, 1)
+    _check_bias(bias, E)
     P = max(1, padded_rows(T, E, k, pad_to)) if pad_to > 1 else max(1, T * k)
     if out is None:
         out = alloc_route_outputs(T, E, k, logits.device)
@@ -176,6 +216,11 @@ def route_expand_fp8(logits, k: int, x, group: int, pad_to: int = 1, bias=None, 
         out["x_expanded"] = torch.empty((P, H), dtype=torch.uint8, device=x.device)
     if out.get("scales") is None:
         out["scales"] = torch.empty((P, max(1, H // group)), dtype=torch.float32, device=x.device)
+    rows = padded_rows(T, E, k, pad_to) if pad_to > 1 else T * k
+    _check_route_out(out, T, E, k, rows)
+    _check_rows_out("x_expanded", out["x_expanded"], rows, H, torch.uint8)
+    _check_rows_out("scales", out["scales"], rows, H // group if group > 0 and H % group == 0 else -1,
+                    torch.float32)
     ws = out["workspace"]
     st = load().moe_route_expand_fp8(_ptr(logits), _ptr(bias), T, E, k, pad_to, _ptr(x), H, group,
                                      _ptr(out["topk_ids"]), _ptr(out["topk_weights"]), _ptr(out["expert_offsets"]),
@@ -198,8 +243,7 @@ def route_expand_mxfp8(logits, k: int, x, pad_to: int = 1, bias=None, out: dict 
     if x.shape[0] != T:
         raise MoEGlueArgumentError(2, f"x has {x.shape[0]} rows, logits has T={T}")
     H = x.shape[1]
-    if bias is not None:
-        _need_gpu("bias", bias, torch.float32, 1)
+    _check_bias(bias, E)
     P = max(1, padded_rows(T, E, k, pad_to)) if pad_to > 1 else max(1, T * k)
     if out is None:
         out = alloc_route_outputs(T, E, k, logits.device)
@@ -208,6 +252,10 @@ def route_expand_mxfp8(logits, k: int, x, pad_to: int = 1, bias=None, out: dict 
         out["x_expanded"] = torch.empty((P, H), dtype=torch.uint8, device=x.device)
     if out.get("scales") is None:
         out["scales"] = torch.empty((P, max(1, H // 32)), dtype=torch.uint8, device=x.device)
+    rows = padded_rows(T, E, k, pad_to) if pad_to > 1 else T * k
+    _check_route_out(out, T, E, k, rows)
+    _check_rows_out("x_expanded", out["x_expanded"], rows, H, torch.uint8)
+    _check_rows_out("scales", out["scales"], rows, H // 32 if H % 32 == 0 else -1, torch.uint8)
     ws = out["workspace"]
     st = load().moe_route_expand_mxfp8(_ptr(logits), _ptr(bias), T, E, k, pad_to, _ptr(x), H,
                                        _ptr(out["topk_ids"]), _ptr(out["topk_weights"]), _ptr(out["expert_offsets"]),
@@ -244,11 +292,17 @@ def expand_rows_fp8(x, dest_of_src, k: int, group: int, rows: int | None = None,
     _need_gpu("x", x, torch.bfloat16, 2)
     _need_gpu("dest_of_src", dest_of_src, torch.int32)
     T, H = x.shape
+    if dest_of_src.numel() != T * k:
+        raise MoEGlueArgumentError(2, f"dest_of_src has {dest_of_src.numel()} entries, expected T*k={T * k}")
     n = T * k if rows is None else rows
+    if n < T * k:
+        raise MoEGlueArgumentError(2, f"rows={n} is below T*k={T * k}")
     if out is None:
         out = torch.empty((n, H), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((n, max(1, H // group)), dtype=torch.float32, device=x.device)
+    _check_rows_out("out", out, n, H, torch.uint8)
+    _check_rows_out("scales", scales, n, H // group if group > 0 and H % group == 0 else -1, torch.float32)
     st = load().moe_expand_rows_fp8(_ptr(x), _ptr(dest_of_src), T, H, k, group, _ptr(out), _ptr(scales),
                                     _stream(x.device))
     check(st, "moe_expand_rows_fp8")
@@ -262,11 +316,17 @@ def expand_rows_mxfp8(x, dest_of_src, k: int, rows: int | None = None, out=None,
     _need_gpu("x", x, torch.bfloat16, 2)
     _need_gpu("dest_of_src", dest_of_src, torch.int32)
     T, H = x.shape
+    if dest_of_src.numel() != T * k:
+        raise MoEGlueArgumentError(2, f"dest_of_src has {dest_of_src.numel()} entries, expected T*k={T * k}")
     n = T * k if rows is None else rows
+    if n < T * k:
+        raise MoEGlueArgumentError(2, f"rows={n} is below T*k={T * k}")
     if out is None:
         out = torch.empty((n, H), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((n, max(1, H // 32)), dtype=torch.uint8, device=x.device)
+    _check_rows_out("out", out, n, H, torch.uint8)
+    _check_rows_out("scales", scales, n, H // 32 if H % 32 == 0 else -1, torch.uint8)
     st = load().moe_expand_rows_mxfp8(_ptr(x), _ptr(dest_of_src), T, H, k, _ptr(out), _ptr(scales),
                                       _stream(x.device))
     check(st, "moe_expand_rows_mxfp8")
@@ -284,14 +344,13 @@ def route_expand(logits, k: int, x, bias=None, out: dict | None = None) -> dict:
     if x.shape[0] != T:
         raise MoEGlueArgumentError(2, f"x has {x.shape[0]} rows, logits has T={T}")
     H = x.shape[1]
-    if bias is not None:
-        _need_gpu("bias", bias, torch.float32, 1)
-        if bias.shape[0] != E:
-            raise MoEGlueArgumentError(2, f"bias has {bias.shape[0]} entries, logits has E={E}")
+    _check_bias(bias, E)
     if out is None:
         out = alloc_route_outputs(T, E, k, logits.device)
     if out.get("x_expanded") is None:
         out["x_expanded"] = torch.empty((T * k, H), dtype=torch.bfloat16, device=x.device)
+    _check_route_out(out, T, E, k, T * k)
+    _check_rows_out("x_expanded", out["x_expanded"], T * k, H, torch.bfloat16)
     ws = out["workspace"]
     st = load().moe_route_expand(_ptr(logits), _ptr(bias), T, E, k, _ptr(x), H, _ptr(out["topk_ids"]),
                                  _ptr(out["topk_weights"]), _ptr(out["expert_offsets"]),

@@ -309,3 +309,153 @@ def test_route_expand_fp8_argument_errors(lib):
     need = lib.moe_route_workspace_bytes(4096, 128, 8)
     assert call(T=4096, E=128, k=8, H=2048, ws=FAKE, wsb=need - 1) == "MOE_ERR_WORKSPACE"
     assert b"moe_route_expand_fp8" in lib.moe_last_error()
+
+
+class FakeGpu:
+    """Stands in for a contiguous GPU tensor of a given shape and dtype, so the
+    binding's checks can run on the CPU.  Its data pointer is never wanted: a
+    check that fails raises before any pointer is read, and data_ptr() raises
+    to make sure no call with a fake address reaches the library."""
+
+    def __init__(self, shape, dtype):
+        import torch
+
+        self._t = torch.empty(shape, dtype=dtype)
+        self.dtype = dtype
+        self.shape = self._t.shape
+        self.is_cuda = True
+        self.device = torch.device("cuda", 0)
+
+    def is_contiguous(self):
+        return True
+
+    def dim(self):
+        return self._t.dim()
+
+    def numel(self):
+        return self._t.numel()
+
+    def element_size(self):
+        return self._t.element_size()
+
+    def data_ptr(self):
+        raise AssertionError("the binding reached a library call with a fake tensor")
+
+
+def fake_route_out(T, E, k, src_rows=None, counts=True):
+    import torch
+
+    out = {"topk_ids": FakeGpu((T, k), torch.int32), "topk_weights": FakeGpu((T, k), torch.float32),
+           "expert_offsets": FakeGpu((E + 1,), torch.int32),
+           "expert_counts": FakeGpu((E,), torch.int32) if counts else None,
+           "dest_of_src": FakeGpu((T * k,), torch.int32),
+           "src_of_dest": FakeGpu((T * k if src_rows is None else src_rows,), torch.int32),
+           "workspace": FakeGpu((1 << 16,), torch.uint8)}
+    return out
+
+
+@pytest.mark.parametrize("call", ["route", "route_padded", "route_expand", "route_expand_padded", "route_expand_fp8",
+                                  "route_expand_mxfp8"])
+def test_binding_rejects_bias_of_wrong_length(lib, call):
+    """Every route wrapper checks that bias has E entries before any launch
+    (the kernels read bias[e] for every e < E)."""
+    import torch
+    import moe_glue_amd as mg
+
+    T, E, k, H = 70, 16, 4, 64
+    logits = FakeGpu((T, E), torch.float32)
+    x = FakeGpu((T, H), torch.bfloat16)
+    rows = mg.padded_rows(T, E, k, 8)
+    for bad in (E - 1, E + 1):
+        bias = FakeGpu((bad,), torch.float32)
+        out = fake_route_out(T, E, k, rows)
+        out["x_expanded"] = FakeGpu((rows, H), torch.uint8 if call.endswith("fp8") else torch.bfloat16)
+        out["scales"] = FakeGpu((rows, H // 32), torch.uint8 if call.endswith("mxfp8") else torch.float32)
+        with pytest.raises(ValueError, match="bias has"):
+            if call == "route":
+                mg.route(logits, k, bias, out=out)
+            elif call == "route_padded":
+                mg.route_padded(logits, k, 8, bias, out=out)
+            elif call == "route_expand":
+                mg.route_expand(logits, k, x, bias, out=out)
+            elif call == "route_expand_padded":
+                mg.route_expand_padded(logits, k, 8, x, bias, out=out)
+            elif call == "route_expand_fp8":
+                mg.route_expand_fp8(logits, k, x, 32, 8, bias, out=out)
+            else:
+                mg.route_expand_mxfp8(logits, k, x, 8, bias, out=out)
+
+
+def test_binding_rejects_short_route_outputs(lib):
+    """Caller-supplied route outputs are size-checked: an unpadded src_of_dest
+    handed to a padded route, short id/weight/map arrays, short offsets."""
+    import torch
+    import moe_glue_amd as mg
+
+    T, E, k = 70, 16, 4
+    logits = FakeGpu((T, E), torch.float32)
+    with pytest.raises(ValueError, match="src_of_dest"):
+        mg.route_padded(logits, k, 8, out=fake_route_out(T, E, k))  # T*k entries, padded rows needed
+    for key, shape, dtype in (("topk_ids", (T * k - 1,), torch.int32), ("topk_weights", (T, k - 1), torch.float32),
+                              ("expert_offsets", (E,), torch.int32), ("expert_counts", (E - 1,), torch.int32),
+                              ("dest_of_src", (T * k + 1,), torch.int32), ("src_of_dest", (T * k - 1,), torch.int32),
+                              ("topk_ids", (T, k), torch.int64)):
+        out = fake_route_out(T, E, k)
+        out[key] = FakeGpu(shape, dtype)
+        with pytest.raises(ValueError, match=key):
+            mg.route(logits, k, out=out)
+
+
+def test_binding_rejects_short_expanded_rows(lib):
+    """x_expanded (and scales) of the combined calls must hold every expanded row."""
+    import torch
+    import moe_glue_amd as mg
+
+    T, E, k, H = 70, 16, 4, 64
+    logits = FakeGpu((T, E), torch.float32)
+    x = FakeGpu((T, H), torch.bfloat16)
+    out = fake_route_out(T, E, k)
+    out["x_expanded"] = FakeGpu((T * k - 1, H), torch.bfloat16)
+    with pytest.raises(ValueError, match="x_expanded"):
+        mg.route_expand(logits, k, x, out=out)
+    out = fake_route_out(T, E, k)
+    out["x_expanded"] = FakeGpu((T * k, H), torch.uint8)
+    out["scales"] = FakeGpu((T * k, H // 16 + 1), torch.float32)
+    with pytest.raises(ValueError, match="scales"):
+        mg.route_expand_fp8(logits, k, x, 16, out=out)
+    out = fake_route_out(T, E, k)
+    out["x_expanded"] = FakeGpu((T * k, H), torch.uint8)
+    out["scales"] = FakeGpu((T * k - 1, H // 32), torch.uint8)
+    with pytest.raises(ValueError, match="scales"):
+        mg.route_expand_mxfp8(logits, k, x, out=out)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp8"])
+def test_binding_quantising_expand_checks_sizes(lib, fmt):
+    """expand_rows_fp8 / _mxfp8: dest_of_src must have T*k entries, the code
+    rows and scales must hold every expanded row, with the right widths."""
+    import torch
+    import moe_glue_amd as mg
+
+    T, H, k, group = 10, 64, 3, 32
+    x = FakeGpu((T, H), torch.bfloat16)
+    sdt = torch.float32 if fmt == "fp8" else torch.uint8
+
+    def call(dest, out=None, scales=None, rows=None):
+        if fmt == "fp8":
+            return mg.expand_rows_fp8(x, dest, k, group, rows=rows, out=out, scales=scales)
+        return mg.expand_rows_mxfp8(x, dest, k, rows=rows, out=out, scales=scales)
+
+    good = FakeGpu((T * k,), torch.int32)
+    with pytest.raises(ValueError, match="dest_of_src"):
+        call(FakeGpu((T * k - 1,), torch.int32), FakeGpu((T * k, H), torch.uint8), FakeGpu((T * k, H // 32), sdt))
+    with pytest.raises(ValueError, match="out"):
+        call(good, FakeGpu((T * k - 1, H), torch.uint8), FakeGpu((T * k, H // 32), sdt))
+    with pytest.raises(ValueError, match="out"):
+        call(good, FakeGpu((T * k, H + 8), torch.uint8), FakeGpu((T * k, H // 32), sdt))
+    with pytest.raises(ValueError, match="scales"):
+        call(good, FakeGpu((T * k, H), torch.uint8), FakeGpu((T * k - 1, H // 32), sdt))
+    with pytest.raises(ValueError, match="scales"):
+        call(good, FakeGpu((T * k, H), torch.uint8), FakeGpu((T * k, H // 32 + 1), sdt))
+    with pytest.raises(ValueError, match="rows"):
+        call(good, FakeGpu((T * k, H), torch.uint8), FakeGpu((T * k, H // 32), sdt), rows=T * k - 1)
