@@ -36,7 +36,8 @@
  *   - The caller allocates and owns every buffer, including the route
  *     workspace.  The library never allocates or frees device memory and
  *     keeps no state between calls, so calls on different streams do not
- *     interfere unless their buffers overlap.
+ *     interfere unless their buffers overlap.  (The one exception is
+ *     moe_route_expand_noalloc, whose workspace is a built-in device array.)
  *   - Inputs must not alias outputs.
  *   - Argument errors are detected on the host BEFORE any HIP call: the call
  *     returns a non-OK status, records a message (moe_last_error) and
@@ -255,6 +256,26 @@ moe_status moe_route_expand_mxfp8(const float* logits, const float* bias, int32_
                                   float* topk_weights, int32_t* expert_offsets, int32_t* expert_counts,
                                   int32_t* dest_of_src, int32_t* src_of_dest, uint8_t* x_expanded, uint8_t* scales,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_route_expand for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results, launches and errors as
+ * moe_route_expand, without the workspace: the library keeps one built-in
+ * device scratch array of MOE_NOALLOC_SCRATCH_BYTES per GPU (it exists on
+ * each GPU the library runs on until the process ends; its device address is
+ * looked up on the first call on each device).  The call allocates nothing.
+ * Calls whose moe_route_workspace_bytes(T, E, k) exceeds the scratch return
+ * MOE_ERR_UNSUPPORTED before any HIP call.  Every call on one GPU shares that
+ * GPU's scratch: calls that can overlap on the device (on different streams,
+ * or captured into graphs that run concurrently) race and give wrong results;
+ * calls on one stream are safe.  The scratch needs no clearing between calls
+ * (the route reads only what the same call wrote). */
+#define MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
+size_t moe_noalloc_scratch_bytes(void);
+moe_status moe_route_expand_noalloc(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                                    const uint16_t* x, int32_t H, int32_t* topk_ids, float* topk_weights,
+                                    int32_t* expert_offsets, int32_t* expert_counts, int32_t* dest_of_src,
+                                    int32_t* src_of_dest, uint16_t* x_expanded, void* stream);
 
 /* ----------------------------------------------------------------- SwiGLU */
 

@@ -9,6 +9,8 @@ Four calls, each a thin wrapper over the C ABI of the HIP library
     swiglu(h)                          doActivation: silu(gate) * up
     combine(y, topk_weights, dest_of_src)  weighted sum back to token order
     route_expand(logits, k, x, bias=None)  route + expand, one launch for T <= 64
+    route_expand_noalloc(logits, k, x, out=...)  the same with the library's built-in
+                                       workspace (allocates nothing given `out`)
     route_padded(logits, k, pad_to)    route with expert segments padded to pad_to rows
     expand_rows_fp8(x, dest, k, group) expand with FP8 E4M3 quantisation per column group
     expand_rows_mxfp8(x, dest, k)    expand with MXFP8 quantisation (E8M0 scale per 32 columns)
@@ -26,7 +28,7 @@ from ._binding import (E_MAX, EXPORTED, K_MAX, LIB_PATH, MoEGlueArgumentError, M
 
 __all__ = ["route", "route_workspace_bytes", "alloc_route_outputs", "route_padded", "padded_rows", "expand_rows",
            "expand_rows_fp8", "expand_rows_mxfp8",
-           "route_expand", "route_expand_padded", "route_expand_fp8", "route_expand_mxfp8", "swiglu", "combine",
+           "route_expand", "route_expand_noalloc", "noalloc_scratch_bytes", "route_expand_padded", "route_expand_fp8", "route_expand_mxfp8", "swiglu", "combine",
            "copy_probe", "MoEGlueError", "MoEGlueArgumentError", "E_MAX", "K_MAX"]
 
 
@@ -358,6 +360,38 @@ def route_expand(logits, k: int, x, bias=None, out: dict | None = None) -> dict:
                                  _ptr(out["x_expanded"]), _ptr(ws), ws.numel() if ws is not None else 0,
                                  _stream(logits.device))
     check(st, "moe_route_expand")
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the library's built-in scratch behind route_expand_noalloc()."""
+    return int(load().moe_noalloc_scratch_bytes())
+
+
+def route_expand_noalloc(logits, k: int, x, bias=None, out: dict | None = None) -> dict:
+    """route_expand() with the library's built-in device scratch as the route
+    workspace; see moe_route_expand_noalloc in include/moe_glue.h.  With `out`
+    (the route dict without "workspace", plus "x_expanded") nothing is
+    allocated.  Calls that can overlap on one GPU share the scratch and race."""
+    torch = _torch()
+    _need_gpu("logits", logits, torch.float32, 2)
+    _need_gpu("x", x, torch.bfloat16, 2)
+    T, E = logits.shape
+    if x.shape[0] != T:
+        raise MoEGlueArgumentError(2, f"x has {x.shape[0]} rows, logits has T={T}")
+    H = x.shape[1]
+    _check_bias(bias, E)
+    if out is None:
+        out = alloc_route_outputs(T, E, k, logits.device)
+        del out["workspace"]
+        out["x_expanded"] = torch.empty((T * k, H), dtype=torch.bfloat16, device=x.device)
+    _check_route_out(out, T, E, k, T * k)
+    _check_rows_out("x_expanded", out.get("x_expanded"), T * k, H, torch.bfloat16)
+    st = load().moe_route_expand_noalloc(_ptr(logits), _ptr(bias), T, E, k, _ptr(x), H, _ptr(out["topk_ids"]),
+                                         _ptr(out["topk_weights"]), _ptr(out["expert_offsets"]),
+                                         _ptr(out.get("expert_counts")), _ptr(out["dest_of_src"]),
+                                         _ptr(out["src_of_dest"]), _ptr(out["x_expanded"]), _stream(logits.device))
+    check(st, "moe_route_expand_noalloc")
     return out
 
 

@@ -20,7 +20,8 @@ PAD_MAX = 4096
 
 EXPORTED = ("moe_route_workspace_bytes", "moe_route", "moe_route_padded_rows", "moe_route_padded",
             "moe_expand_rows", "moe_expand_rows_fp8", "moe_expand_rows_mxfp8", "moe_route_expand", "moe_route_expand_padded",
-            "moe_route_expand_fp8", "moe_route_expand_mxfp8", "moe_swiglu", "moe_combine", "moe_copy_probe",
+            "moe_route_expand_fp8", "moe_route_expand_mxfp8", "moe_noalloc_scratch_bytes", "moe_route_expand_noalloc",
+            "moe_swiglu", "moe_combine", "moe_copy_probe",
             "moe_status_string", "moe_last_error")
 
 _vp = ctypes.c_void_p
@@ -83,6 +84,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_route_expand_mxfp8.restype = ctypes.c_int
     lib.moe_route_expand_mxfp8.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp,
                                            _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.moe_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.moe_noalloc_scratch_bytes.argtypes = []
+    lib.moe_route_expand_noalloc.restype = ctypes.c_int
+    lib.moe_route_expand_noalloc.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                             _vp, _vp]
     lib.moe_swiglu.restype = ctypes.c_int
     lib.moe_swiglu.argtypes = [_vp, _i32, _i32, _vp, _vp]
     lib.moe_combine.restype = ctypes.c_int

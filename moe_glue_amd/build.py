@@ -20,7 +20,7 @@ LIB = os.path.join(LIBDIR, "libmoe_glue.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "expand.hip", "quant.hip", "swiglu.hip", "combine.hip",
-           "probe.hip"]
+           "probe.hip", "noalloc.hip"]
 HEADERS = ["device_common.h", "kernels.h", "route_common.h", "fp8_common.h", "place_copy.h"]
 ARCH = "gfx950"
 

@@ -203,6 +203,50 @@ moe_status route_impl(const char* fn, const float* logits, const float* bias, in
     return from_hip(moe::launch_route(a, v, static_cast<hipStream_t>(stream)), fn);
 }
 
+// moe_route_expand, for the caller's workspace or the built-in scratch.
+moe_status route_expand_impl(const char* fn, const float* logits, const float* bias, int32_t T, int32_t E,
+                             int32_t k, const uint16_t* x, int32_t H, int32_t* topk_ids, float* topk_weights,
+                             int32_t* expert_offsets, int32_t* expert_counts, int32_t* dest_of_src,
+                             int32_t* src_of_dest, uint16_t* x_expanded, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    moe_status s = check_route_args(fn, logits, bias, T, E, k, topk_ids, topk_weights,
+                                    expert_offsets, dest_of_src, src_of_dest);
+    if (s != MOE_OK) return s;
+    s = check_expand_args(fn, x, dest_of_src, T, H, k, x_expanded);
+    if (s != MOE_OK) return s;
+    const moe::RouteVariant requested = requested_route_variant();
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    moe::RouteArgs a{logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, expert_counts,
+                     dest_of_src, src_of_dest, workspace, /*pad_to=*/1, /*row_list=*/nullptr, {}};
+    if (T <= moe::kRouteSmallDispatchMaxTokens && requested == moe::RouteVariant::Auto) {
+        a.copy_x = x;
+        a.copy_out = x_expanded;
+        a.copy_H = H;
+        return from_hip(moe::launch_route_expand_small(a, st), fn);
+    }
+    const moe::RouteVariant v = moe::route_pick_variant(T, E, requested);
+    s = check_route_workspace(fn, T, E, k, true, v, workspace, workspace_bytes);
+    if (s != MOE_OK) return s;
+    // the multi-workgroup route either lists the rows per token group for the
+    // destination-order expand, or copies them itself in token order
+    const ExpandOrder order = expand_order(T, k, v);
+    if (order == ExpandOrder::Grouped) {
+        a.row_list = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + moe::route_histogram_bytes(T, E));
+        a.groups = moe::route_row_groups(T, E, H);
+    } else if (order == ExpandOrder::Fused) {
+        a.copy_x = x;
+        a.copy_out = x_expanded;
+        a.copy_H = H;
+    }
+    s = from_hip(moe::launch_route(a, v, st), fn);
+    if (s != MOE_OK || T == 0 || order == ExpandOrder::Fused) return s;
+    if (order == ExpandOrder::Grouped)
+        return from_hip(moe::launch_expand_grouped(x, a.row_list, a.groups, H, k, x_expanded, st),
+                        fn);
+    return from_hip(moe::launch_expand_rows(x, dest_of_src, T, H, k, x_expanded, st),
+                    fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -263,42 +307,34 @@ moe_status moe_route_expand(const float* logits, const float* bias, int32_t T, i
                             int32_t* expert_offsets, int32_t* expert_counts, int32_t* dest_of_src,
                             int32_t* src_of_dest, uint16_t* x_expanded, void* workspace, size_t workspace_bytes,
                             void* stream) {
-    moe_status s = check_route_args("moe_route_expand", logits, bias, T, E, k, topk_ids, topk_weights,
-                                    expert_offsets, dest_of_src, src_of_dest);
+    return route_expand_impl("moe_route_expand", logits, bias, T, E, k, x, H, topk_ids, topk_weights,
+                             expert_offsets, expert_counts, dest_of_src, src_of_dest, x_expanded, workspace,
+                             workspace_bytes, stream);
+}
+
+size_t moe_noalloc_scratch_bytes(void) { return moe::kNoAllocScratchBytes; }
+
+moe_status moe_route_expand_noalloc(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                                    const uint16_t* x, int32_t H, int32_t* topk_ids, float* topk_weights,
+                                    int32_t* expert_offsets, int32_t* expert_counts, int32_t* dest_of_src,
+                                    int32_t* src_of_dest, uint16_t* x_expanded, void* stream) {
+    const char* fn = "moe_route_expand_noalloc";
+    // every argument check and the size limit before the first HIP call
+    moe_status s = check_route_args(fn, logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, dest_of_src,
+                                    src_of_dest);
     if (s != MOE_OK) return s;
-    s = check_expand_args("moe_route_expand", x, dest_of_src, T, H, k, x_expanded);
+    s = check_expand_args(fn, x, dest_of_src, T, H, k, x_expanded);
     if (s != MOE_OK) return s;
-    const moe::RouteVariant requested = requested_route_variant();
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    moe::RouteArgs a{logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, expert_counts,
-                     dest_of_src, src_of_dest, workspace, /*pad_to=*/1, /*row_list=*/nullptr, {}};
-    if (T <= moe::kRouteSmallDispatchMaxTokens && requested == moe::RouteVariant::Auto) {
-        a.copy_x = x;
-        a.copy_out = x_expanded;
-        a.copy_H = H;
-        return from_hip(moe::launch_route_expand_small(a, st), "moe_route_expand launch");
-    }
-    const moe::RouteVariant v = moe::route_pick_variant(T, E, requested);
-    s = check_route_workspace("moe_route_expand", T, E, k, true, v, workspace, workspace_bytes);
+    const size_t need = moe::route_workspace_bytes(T, E, k);
+    if (need > moe::kNoAllocScratchBytes)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: T=%d E=%d k=%d needs %zu bytes of workspace; the built-in scratch "
+                    "holds %zu (use moe_route_expand with a caller workspace)", fn, T, E, k, need,
+                    moe::kNoAllocScratchBytes);
+    void* ws = nullptr;
+    s = from_hip(moe::noalloc_scratch(stream, &ws), "moe_route_expand_noalloc: scratch address");
     if (s != MOE_OK) return s;
-    // the multi-workgroup route either lists the rows per token group for the
-    // destination-order expand, or copies them itself in token order
-    const ExpandOrder order = expand_order(T, k, v);
-    if (order == ExpandOrder::Grouped) {
-        a.row_list = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + moe::route_histogram_bytes(T, E));
-        a.groups = moe::route_row_groups(T, E, H);
-    } else if (order == ExpandOrder::Fused) {
-        a.copy_x = x;
-        a.copy_out = x_expanded;
-        a.copy_H = H;
-    }
-    s = from_hip(moe::launch_route(a, v, st), "moe_route_expand launch (route)");
-    if (s != MOE_OK || T == 0 || order == ExpandOrder::Fused) return s;
-    if (order == ExpandOrder::Grouped)
-        return from_hip(moe::launch_expand_grouped(x, a.row_list, a.groups, H, k, x_expanded, st),
-                        "moe_route_expand launch (expand)");
-    return from_hip(moe::launch_expand_rows(x, dest_of_src, T, H, k, x_expanded, st),
-                    "moe_route_expand launch (expand)");
+    return route_expand_impl(fn, logits, bias, T, E, k, x, H, topk_ids, topk_weights, expert_offsets, expert_counts,
+                             dest_of_src, src_of_dest, x_expanded, ws, moe::kNoAllocScratchBytes, stream);
 }
 
 moe_status moe_route_expand_padded(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,

@@ -8,6 +8,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "moe_glue.h"
+
 namespace moe {
 
 // ---------------------------------------------------------------- route
@@ -147,5 +149,12 @@ hipError_t launch_swiglu(const void* h, int R, int I, void* act, hipStream_t str
 hipError_t launch_combine(const void* y, const float* topk_weights, const int32_t* dest_of_src, int T, int H,
                           int k, void* out, hipStream_t stream);
 hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+// ------------------------------------------------------- built-in scratch
+// Bytes of the file-scope device array behind moe_route_expand_noalloc.
+constexpr size_t kNoAllocScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+// Device address of that array on the device `stream` runs on (the current
+// device for the null stream), looked up on the first call per device.
+hipError_t noalloc_scratch(void* stream, void** out);
 
 }  // namespace moe

@@ -459,3 +459,23 @@ def test_binding_quantising_expand_checks_sizes(lib, fmt):
         call(good, FakeGpu((T * k, H), torch.uint8), FakeGpu((T * k, H // 32 + 1), sdt))
     with pytest.raises(ValueError, match="rows"):
         call(good, FakeGpu((T * k, H), torch.uint8), FakeGpu((T * k, H // 32), sdt), rows=T * k - 1)
+
+
+def test_route_expand_noalloc_argument_errors(lib):
+    """moe_route_expand_noalloc checks its arguments, then the scratch limit,
+    before its first HIP call (the scratch address lookup)."""
+    def call(T=4, E=8, k=2, x=FAKE, H=256, ids=FAKE, xe=FAKE):
+        return status(lib, lib.moe_route_expand_noalloc(FAKE, None, T, E, k, x, H, ids, FAKE, FAKE, None, FAKE,
+                                                        FAKE, xe, None))
+
+    cap = lib.moe_noalloc_scratch_bytes()
+    assert cap == 4 << 20
+    assert call(k=9) == "MOE_ERR_SHAPE"
+    assert call(ids=None) == "MOE_ERR_NULL"
+    assert call(x=None) == "MOE_ERR_NULL"
+    assert call(H=12) == "MOE_ERR_ALIGN"
+    assert lib.moe_route_workspace_bytes(65536, 128, 8) > cap
+    assert call(T=65536, E=128, k=8, H=64) == "MOE_ERR_UNSUPPORTED"
+    assert b"scratch" in lib.moe_last_error()
+    assert lib.moe_route_workspace_bytes(4096, 128, 8) <= cap  # the Qwen3-30B-A3B-shaped batch fits
+    assert lib.moe_route_workspace_bytes(8192, 256, 8) <= cap  # and the DeepSeek-V3-shaped one
