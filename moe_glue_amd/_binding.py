@@ -23,6 +23,10 @@ EXPORTED = ("moe_route_workspace_bytes", "moe_route", "moe_route_padded_rows", "
             "moe_route_expand_fp8", "moe_route_expand_mxfp8", "moe_noalloc_scratch_bytes", "moe_route_expand_noalloc",
             "moe_swiglu", "moe_combine", "moe_copy_probe",
             "moe_status_string", "moe_last_error")
+# include/moe_glue_testing.h
+TESTING_EXPORTED = ("moe_testing_force",)
+ROUTE_VARIANTS = {"auto": 0, "single": 1, "two": 2, "three": 3}
+EXPAND_ORDERS = {"auto": 0, "token": 1, "fused": 2, "grouped": 3, "placed": 4}
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -99,6 +103,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_last_error.restype = ctypes.c_char_p
     lib.moe_last_error.argtypes = []
+    lib.moe_testing_force.restype = ctypes.c_int
+    lib.moe_testing_force.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     _lib = lib
     return lib
 
@@ -111,3 +117,12 @@ def check(status: int, fn: str) -> None:
     detail = lib.moe_last_error().decode()
     cls = MoEGlueError if status == MOE_ERR_HIP else MoEGlueArgumentError
     raise cls(status, f"{fn}: {name}: {detail}")
+
+
+def testing_force(route: str = "auto", order: str = "auto", workgroups_per_group: int = 0) -> None:
+    """Test and measurement hook (include/moe_glue_testing.h): force the route
+    variant and the expand order process-wide; "auto" everywhere restores the
+    library's own choice."""
+    rc = load().moe_testing_force(ROUTE_VARIANTS[route], EXPAND_ORDERS[order], int(workgroups_per_group))
+    if rc != 0:
+        raise ValueError(f"moe_testing_force rejected ({route}, {order}, {workgroups_per_group})")

@@ -20,7 +20,7 @@ LIB = os.path.join(LIBDIR, "libmoe_glue.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "expand.hip", "quant.hip", "swiglu.hip", "combine.hip",
-           "probe.hip", "noalloc.hip"]
+           "probe.hip", "noalloc.hip", "place_expand.hip"]
 HEADERS = ["device_common.h", "kernels.h", "route_common.h", "fp8_common.h", "place_copy.h"]
 ARCH = "gfx950"
 
@@ -75,7 +75,7 @@ def is_stale() -> bool:
     if not os.path.exists(LIB):
         return True
     t = os.path.getmtime(LIB)
-    files = [os.path.join(CSRC, f) for f in SOURCES + HEADERS] + [os.path.join(INCLUDE, "moe_glue.h")]
+    files = [os.path.join(CSRC, f) for f in SOURCES + HEADERS] + [os.path.join(INCLUDE, "moe_glue.h"), os.path.join(INCLUDE, "moe_glue_testing.h")]
     return any(os.path.getmtime(f) > t for f in files)
 
 

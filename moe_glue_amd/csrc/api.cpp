@@ -7,10 +7,10 @@
 
 #include <cstdarg>
 #include <cstdio>
-#include <cstdlib>
-#include <cstring>
+#include <atomic>
 
 #include "kernels.h"
+#include "moe_glue_testing.h"
 
 namespace {
 
@@ -37,49 +37,76 @@ moe_status from_hip(hipError_t e, const char* what) {
     return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Route variant override for tests and measurements:
-// MOE_GLUE_ROUTE_VARIANT = auto | single | two | three (anything else: auto).
+// Variant forcing for tests and measurements (moe_testing_force in
+// include/moe_glue_testing.h): process-wide, read once per call.
+std::atomic<int> g_force_route{0};  // 0 auto, 1 single, 2 two, 3 three
+std::atomic<int> g_force_order{0};  // ExpandOrder + 1, 0 auto
+std::atomic<int> g_force_wpg{0};    // workgroups per token group of the placing expand, 0 auto
+
 moe::RouteVariant requested_route_variant() {
-    const char* v = std::getenv("MOE_GLUE_ROUTE_VARIANT");
-    if (v == nullptr) return moe::RouteVariant::Auto;
-    if (std::strcmp(v, "single") == 0) return moe::RouteVariant::SingleWorkgroup;
-    if (std::strcmp(v, "two") == 0) return moe::RouteVariant::TwoPass;
-    if (std::strcmp(v, "three") == 0) return moe::RouteVariant::ThreePass;
-    return moe::RouteVariant::Auto;
+    switch (g_force_route.load(std::memory_order_relaxed)) {
+        case 1: return moe::RouteVariant::SingleWorkgroup;
+        case 2: return moe::RouteVariant::TwoPass;
+        case 3: return moe::RouteVariant::ThreePass;
+        default: return moe::RouteVariant::Auto;
+    }
 }
 
 // Expand of moe_route_expand above the one-launch size:
-//   Grouped  destination order from the route's row list (expand.hip); the
-//            route then also builds the row list (about 2 us more on the
-//            histogram path).  Token order scatters every token's k rows
-//            over k expert segments, a cost per expanded row; the list's cost
-//            is fixed.  Measured on this part with x coming from HBM (enough
-//            rotating input sets that no copy of x stays in the Infinity
-//            Cache), moe_route_expand per call against the copy in the place
-//            launch: at 16384 expanded rows the grouped call is 1.6-1.7 us
-//            behind (H = 2048 and 7168), from 24576 rows ahead at every width
-//            measured (H = 2048, 4096, 7168; by 1.2 us at the Qwen3-30B-A3B
-//            shape, 13 us at DeepSeek-V3);
+//   Placed   the two-launch route's second launch is the expand itself
+//            (place_expand.hip): each workgroup places and copies a share of
+//            one token group's rows in destination order.  One launch and
+//            one round trip through memory fewer than Grouped;
+//   Grouped  destination order from a row list the route's place launch
+//            writes (expand.hip): the form for batches outside Placed's
+//            limits (three-launch route, E > 256, group sizes);
 //   Fused    token order, copied by the route's scan+place launch itself
-//            (two-launch route only), one launch less;
+//            (two-launch route only), one launch less than Token;
 //   Token    token order, a launch of its own after the route.
-// Override for tests and measurements:
-// MOE_GLUE_EXPAND_ORDER = token | fused | grouped | auto (anything else: auto).
+// Destination order pays from about 24576 expanded rows: token order
+// scatters every token's k rows over k expert segments, a cost per expanded
+// row; the destination-order forms' cost is mostly fixed.  Measured on this
+// part with x coming from HBM (enough rotating input sets that no copy of x
+// stays in the Infinity Cache), moe_route_expand per call with the row-list
+// order against the copy in the place launch: at 16384 expanded rows the
+// grouped call is 1.6-1.7 us behind (H = 2048 and 7168), from 24576 rows ahead
+// at every width measured (H = 2048, 4096, 7168).
 constexpr int64_t kGroupedExpandMinRows = 24576;
 
-enum class ExpandOrder { Token, Fused, Grouped };
+enum class ExpandOrder { Token = 0, Fused = 1, Grouped = 2, Placed = 3 };
 
 constexpr int64_t kQuantisingFoldMaxBytes = 20ll << 20;  // E4M3 codes of moe_route_expand_fp8
 
-ExpandOrder expand_order(int32_t T, int32_t k, moe::RouteVariant v) {
-    const char* e = std::getenv("MOE_GLUE_EXPAND_ORDER");
+int forced_order() { return g_force_order.load(std::memory_order_relaxed); }
+
+// Placed runs every workgroup of the grid at once, each XCD on two token
+// groups, so it pays while their source rows stay within the XCDs' L2 and the
+// histogram each workgroup sums stays small.  Measured per moe_route_expand
+// call against the row-list order (T x H, E, k; x from HBM): 3072 x 2048 -1.4,
+// 4096 x 2048 (the Qwen3-30B-A3B shape) -0.9, 4096 x 4096 (64, 6) -2.6,
+// 6144 x 2048 -1.9, 4096 x 3072 +1.0, 8192 x 2048 +1.9, 8192 x 7168 (256, 8)
+// +38 us.
+constexpr int kPlacedMaxTokens = 6144;
+constexpr int64_t kPlacedMaxSourceBytes = 32ll << 20;
+
+ExpandOrder expand_order(int32_t T, int32_t E, int32_t k, int32_t H, moe::RouteVariant v,
+                         moe::PlaceExpandShape* shape) {
     const bool two = v == moe::RouteVariant::TwoPass;
     if (v == moe::RouteVariant::SingleWorkgroup || T == 0) return ExpandOrder::Token;
-    if (e != nullptr && std::strcmp(e, "token") == 0) return ExpandOrder::Token;
-    if (e != nullptr && std::strcmp(e, "grouped") == 0) return ExpandOrder::Grouped;
-    if (e != nullptr && std::strcmp(e, "fused") == 0) return two ? ExpandOrder::Fused : ExpandOrder::Token;
-    if ((int64_t)T * k >= kGroupedExpandMinRows) return ExpandOrder::Grouped;
-    return two ? ExpandOrder::Fused : ExpandOrder::Token;
+    switch (forced_order()) {
+        case 1: return ExpandOrder::Token;
+        case 2: return two ? ExpandOrder::Fused : ExpandOrder::Token;
+        case 3: return ExpandOrder::Grouped;
+        case 4: break;
+        default:
+            if ((int64_t)T * k < kGroupedExpandMinRows) return two ? ExpandOrder::Fused : ExpandOrder::Token;
+            if (T > kPlacedMaxTokens || (int64_t)T * H * 2 > kPlacedMaxSourceBytes) return ExpandOrder::Grouped;
+    }
+    if (two) {
+        *shape = moe::place_expand_shape(T, E, k, H, g_force_wpg.load(std::memory_order_relaxed));
+        if (shape->ok) return ExpandOrder::Placed;
+    }
+    return ExpandOrder::Grouped;
 }
 
 moe_status check_route_sizes(int32_t T, int32_t E, int32_t k) {
@@ -203,21 +230,24 @@ moe_status route_impl(const char* fn, const float* logits, const float* bias, in
     return from_hip(moe::launch_route(a, v, static_cast<hipStream_t>(stream)), fn);
 }
 
-// moe_route_expand, for the caller's workspace or the built-in scratch.
+// moe_route_expand (pad_to = 1) and moe_route_expand_padded, for the
+// caller's workspace or the built-in scratch.
 moe_status route_expand_impl(const char* fn, const float* logits, const float* bias, int32_t T, int32_t E,
-                             int32_t k, const uint16_t* x, int32_t H, int32_t* topk_ids, float* topk_weights,
-                             int32_t* expert_offsets, int32_t* expert_counts, int32_t* dest_of_src,
-                             int32_t* src_of_dest, uint16_t* x_expanded, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+                             int32_t k, int32_t pad_to, const uint16_t* x, int32_t H, int32_t* topk_ids,
+                             float* topk_weights, int32_t* expert_offsets, int32_t* expert_counts,
+                             int32_t* dest_of_src, int32_t* src_of_dest, uint16_t* x_expanded, void* workspace,
+                             size_t workspace_bytes, void* stream) {
     moe_status s = check_route_args(fn, logits, bias, T, E, k, topk_ids, topk_weights,
                                     expert_offsets, dest_of_src, src_of_dest);
+    if (s != MOE_OK) return s;
+    s = check_pad(fn, T, E, k, pad_to);
     if (s != MOE_OK) return s;
     s = check_expand_args(fn, x, dest_of_src, T, H, k, x_expanded);
     if (s != MOE_OK) return s;
     const moe::RouteVariant requested = requested_route_variant();
     const hipStream_t st = static_cast<hipStream_t>(stream);
     moe::RouteArgs a{logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, expert_counts,
-                     dest_of_src, src_of_dest, workspace, /*pad_to=*/1, /*row_list=*/nullptr, {}};
+                     dest_of_src, src_of_dest, workspace, pad_to, /*row_list=*/nullptr, {}};
     if (T <= moe::kRouteSmallDispatchMaxTokens && requested == moe::RouteVariant::Auto) {
         a.copy_x = x;
         a.copy_out = x_expanded;
@@ -227,9 +257,21 @@ moe_status route_expand_impl(const char* fn, const float* logits, const float* b
     const moe::RouteVariant v = moe::route_pick_variant(T, E, requested);
     s = check_route_workspace(fn, T, E, k, true, v, workspace, workspace_bytes);
     if (s != MOE_OK) return s;
-    // the multi-workgroup route either lists the rows per token group for the
-    // destination-order expand, or copies them itself in token order
-    const ExpandOrder order = expand_order(T, k, v);
+    moe::PlaceExpandShape shape{};
+    const ExpandOrder order = expand_order(T, E, k, H, v, &shape);
+    if (order == ExpandOrder::Placed) {
+        // top-k with count-byte rows, then placement and copy in one launch
+        int nb = 0;
+        s = from_hip(moe::launch_route_topk_bytes(a, &nb, st), fn);
+        if (s != MOE_OK) return s;
+        moe::PlaceExpandArgs pa{workspace, nb, T, E, k, H, pad_to, topk_ids, shape.groups, x, x_expanded,
+                                dest_of_src, src_of_dest, expert_offsets, expert_counts};
+        return from_hip(moe::launch_place_expand(pa, shape, st), fn);
+    }
+    // otherwise the multi-workgroup route either lists the rows per token
+    // group for the destination-order expand, or copies them itself in token
+    // order; the row list holds the real rows only, so padding rows stay
+    // untouched exactly as moe_expand_rows leaves them
     if (order == ExpandOrder::Grouped) {
         a.row_list = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + moe::route_histogram_bytes(T, E));
         a.groups = moe::route_row_groups(T, E, H);
@@ -241,10 +283,8 @@ moe_status route_expand_impl(const char* fn, const float* logits, const float* b
     s = from_hip(moe::launch_route(a, v, st), fn);
     if (s != MOE_OK || T == 0 || order == ExpandOrder::Fused) return s;
     if (order == ExpandOrder::Grouped)
-        return from_hip(moe::launch_expand_grouped(x, a.row_list, a.groups, H, k, x_expanded, st),
-                        fn);
-    return from_hip(moe::launch_expand_rows(x, dest_of_src, T, H, k, x_expanded, st),
-                    fn);
+        return from_hip(moe::launch_expand_grouped(x, a.row_list, a.groups, H, k, x_expanded, st), fn);
+    return from_hip(moe::launch_expand_rows(x, dest_of_src, T, H, k, x_expanded, st), fn);
 }
 
 }  // namespace
@@ -307,7 +347,7 @@ moe_status moe_route_expand(const float* logits, const float* bias, int32_t T, i
                             int32_t* expert_offsets, int32_t* expert_counts, int32_t* dest_of_src,
                             int32_t* src_of_dest, uint16_t* x_expanded, void* workspace, size_t workspace_bytes,
                             void* stream) {
-    return route_expand_impl("moe_route_expand", logits, bias, T, E, k, x, H, topk_ids, topk_weights,
+    return route_expand_impl("moe_route_expand", logits, bias, T, E, k, 1, x, H, topk_ids, topk_weights,
                              expert_offsets, expert_counts, dest_of_src, src_of_dest, x_expanded, workspace,
                              workspace_bytes, stream);
 }
@@ -333,8 +373,9 @@ moe_status moe_route_expand_noalloc(const float* logits, const float* bias, int3
     void* ws = nullptr;
     s = from_hip(moe::noalloc_scratch(stream, &ws), "moe_route_expand_noalloc: scratch address");
     if (s != MOE_OK) return s;
-    return route_expand_impl(fn, logits, bias, T, E, k, x, H, topk_ids, topk_weights, expert_offsets, expert_counts,
-                             dest_of_src, src_of_dest, x_expanded, ws, moe::kNoAllocScratchBytes, stream);
+    return route_expand_impl(fn, logits, bias, T, E, k, 1, x, H, topk_ids, topk_weights, expert_offsets,
+                             expert_counts, dest_of_src, src_of_dest, x_expanded, ws, moe::kNoAllocScratchBytes,
+                             stream);
 }
 
 moe_status moe_route_expand_padded(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
@@ -342,46 +383,9 @@ moe_status moe_route_expand_padded(const float* logits, const float* bias, int32
                                    float* topk_weights, int32_t* expert_offsets, int32_t* expert_counts,
                                    int32_t* dest_of_src, int32_t* src_of_dest, uint16_t* x_expanded,
                                    void* workspace, size_t workspace_bytes, void* stream) {
-    const char* fn = "moe_route_expand_padded";
-    moe_status s = check_route_args(fn, logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, dest_of_src,
-                                    src_of_dest);
-    if (s != MOE_OK) return s;
-    s = check_pad(fn, T, E, k, pad_to);
-    if (s != MOE_OK) return s;
-    s = check_expand_args(fn, x, dest_of_src, T, H, k, x_expanded);
-    if (s != MOE_OK) return s;
-    const moe::RouteVariant requested = requested_route_variant();
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    moe::RouteArgs a{logits, bias, T, E, k, topk_ids, topk_weights, expert_offsets, expert_counts,
-                     dest_of_src, src_of_dest, workspace, pad_to, /*row_list=*/nullptr, {}};
-    if (T <= moe::kRouteSmallDispatchMaxTokens && requested == moe::RouteVariant::Auto) {
-        a.copy_x = x;
-        a.copy_out = x_expanded;
-        a.copy_H = H;
-        return from_hip(moe::launch_route_expand_small(a, st), "moe_route_expand_padded launch");
-    }
-    const moe::RouteVariant v = moe::route_pick_variant(T, E, requested);
-    s = check_route_workspace(fn, T, E, k, true, v, workspace, workspace_bytes);
-    if (s != MOE_OK) return s;
-    // the row list holds the real rows only, so the grouped copy leaves the
-    // padding rows untouched exactly as moe_expand_rows does; so does the
-    // token-order copy of the place step
-    const ExpandOrder order = expand_order(T, k, v);
-    if (order == ExpandOrder::Grouped) {
-        a.row_list = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + moe::route_histogram_bytes(T, E));
-        a.groups = moe::route_row_groups(T, E, H);
-    } else if (order == ExpandOrder::Fused) {
-        a.copy_x = x;
-        a.copy_out = x_expanded;
-        a.copy_H = H;
-    }
-    s = from_hip(moe::launch_route(a, v, st), "moe_route_expand_padded launch (route)");
-    if (s != MOE_OK || T == 0 || order == ExpandOrder::Fused) return s;
-    if (order == ExpandOrder::Grouped)
-        return from_hip(moe::launch_expand_grouped(x, a.row_list, a.groups, H, k, x_expanded, st),
-                        "moe_route_expand_padded launch (expand)");
-    return from_hip(moe::launch_expand_rows(x, dest_of_src, T, H, k, x_expanded, st),
-                    "moe_route_expand_padded launch (expand)");
+    return route_expand_impl("moe_route_expand_padded", logits, bias, T, E, k, pad_to, x, H, topk_ids, topk_weights,
+                             expert_offsets, expert_counts, dest_of_src, src_of_dest, x_expanded, workspace,
+                             workspace_bytes, stream);
 }
 
 moe_status moe_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, int32_t T, int32_t H, int32_t k,
@@ -442,11 +446,10 @@ moe_status route_expand_quant(const char* fn, const float* logits, const float* 
     // at H = 2048, k = 8, group 128, folding saves 2-3 us up to 16 MB of codes
     // (T = 1000) but costs 3 us at 33 MB and 9 us at 67 MB (the copy then runs
     // well below the separate quantising expand's rate).
-    // MOE_GLUE_EXPAND_ORDER = token keeps the separate expand, = fused folds
-    // whenever possible (tests and measurements).
-    const char* e = std::getenv("MOE_GLUE_EXPAND_ORDER");
-    const bool forced_token = e != nullptr && std::strcmp(e, "token") == 0;
-    const bool forced_fold = e != nullptr && std::strcmp(e, "fused") == 0;
+    // A forced token order keeps the separate expand, a forced fused order
+    // folds whenever possible (tests and measurements).
+    const bool forced_token = forced_order() == 1;
+    const bool forced_fold = forced_order() == 2;
     const bool small = (int64_t)T * k * H <= kQuantisingFoldMaxBytes;
     const bool fold = v == moe::RouteVariant::TwoPass && T > 0 && H <= moe::route_quantising_place_max_h() &&
                       !forced_token && (small || forced_fold);
@@ -523,6 +526,16 @@ moe_status moe_combine(const uint16_t* y, const float* topk_weights, const int32
     if (!aligned4(topk_weights)) return fail(MOE_ERR_ALIGN, "moe_combine: topk_weights must be 4-byte aligned");
     return from_hip(moe::launch_combine(y, topk_weights, dest_of_src, T, H, k, out, static_cast<hipStream_t>(stream)),
                     "moe_combine launch");
+}
+
+int moe_testing_force(int route_variant, int expand_order, int workgroups_per_group) {
+    if (route_variant < 0 || route_variant > 3 || expand_order < 0 || expand_order > 4 || workgroups_per_group < 0 ||
+        workgroups_per_group > 4096)
+        return -1;
+    g_force_route.store(route_variant, std::memory_order_relaxed);
+    g_force_order.store(expand_order, std::memory_order_relaxed);
+    g_force_wpg.store(workgroups_per_group, std::memory_order_relaxed);
+    return 0;
 }
 
 moe_status moe_copy_probe(const void* src, void* dst, size_t bytes, void* stream) {

@@ -134,6 +134,56 @@ constexpr int kRouteSmallDispatchMaxTokens = 64;
 // padded to pad_to rows.
 hipError_t launch_route_expand_small(const RouteArgs& a, hipStream_t stream);
 
+// The prefill route + expand in two launches (place_expand.hip): the top-k
+// launch writes ids, weights and count-byte rows (no ranks); the second
+// launch places and copies each token group's rows in destination order.
+constexpr int kPeSlotsPerLane = 4;     // group slots <= 4 * 1024
+constexpr int kPeMaskWordsMax = 2048;  // E * ceil(group tokens / 64) bitmap words
+constexpr int kPeRowsMax = 512;        // rows one workgroup copies
+struct PlaceExpandShape {
+    bool ok;          // false: the shape is outside this path (use the row-list path)
+    RowGroups groups;
+    uint32_t S;       // workgroups per group
+    uint32_t Rc;      // rows per chunk (one pass of a workgroup)
+    uint32_t grid;
+};
+struct PlaceExpandArgs {
+    const void* rows8;  // count-byte rows of the top-k launch (workspace)
+    int nb;             // top-k rows
+    int T, E, k, H, pad_to;
+    const int32_t* topk_ids;
+    RowGroups groups;
+    const void* x;
+    void* x_expanded;
+    int32_t* dest_of_src;
+    int32_t* src_of_dest;
+    int32_t* expert_offsets;
+    int32_t* expert_counts;
+};
+// Position of the (r+1)-th set bit of m (r < popcount(m)), by halving.
+__host__ __device__ inline int select_bit(unsigned long long m, int r) {
+    int pos = 0;
+#pragma unroll
+    for (int width = 32; width >= 1; width /= 2) {
+        const unsigned long long low = m & ((1ull << width) - 1ull);
+        const int c = __builtin_popcountll(low);
+        if (r >= c) {
+            r -= c;
+            m >>= width;
+            pos += width;
+        } else {
+            m = low;
+        }
+    }
+    return pos;
+}
+// The shape for (T, E, k, H); workgroups_per_group = 0 picks the default.
+PlaceExpandShape place_expand_shape(int T, int E, int k, int H, int workgroups_per_group);
+hipError_t launch_place_expand(const PlaceExpandArgs& a, const PlaceExpandShape& sh, hipStream_t stream);
+// The top-k launch of that path: ids, weights and count-byte rows (workspace
+// front part) of every 16-token block; returns the number of rows in *nb.
+hipError_t launch_route_topk_bytes(const RouteArgs& a, int* nb, hipStream_t stream);
+
 // ---------------------------------------------------- streaming row kernels
 hipError_t launch_expand_rows(const void* x, const int32_t* dest_of_src, int T, int H, int k, void* x_expanded,
                               hipStream_t stream);

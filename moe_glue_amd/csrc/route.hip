@@ -72,11 +72,12 @@ __global__ __launch_bounds__((SingleShape<G>::THREADS)) void route_single_kernel
 
 // ------------------------------------------------------------- multi workgroup
 // 1. Workgroup b owns tokens [b*TOK, b*TOK + TOK).  Writes the top-k, each
-// slot's rank inside the workgroup (into dest_of_src, finished later) and the
+// slot's rank inside the workgroup (into dest_of_src, finished later; not
+// with RANKS = false, whose second launch ranks the slots itself) and the
 // workgroup's histogram as workspace row b: Epad int32 (three-launch form) or
 // one count byte per expert in route_byte_row_vectors(E) 16-byte vectors
 // (two-launch form; a count is at most TOK <= 64), zero padded.
-template <int G, int V, bool BYTES>
+template <int G, int V, bool BYTES, bool RANKS = true>
 __global__ __launch_bounds__((TopkShape<G>::THREADS)) void route_topk_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights, int32_t* __restrict__ dest_of_src,
@@ -94,8 +95,9 @@ __global__ __launch_bounds__((TopkShape<G>::THREADS)) void route_topk_kernel(
     topk_token<G, V>(logits, bias, T, E, k, tok0 + grp, grp, threadIdx.x % G, topk_ids, topk_weights, ids_lds);
     __syncthreads();
     mark_masks<S::THREADS>(ids_lds, ntok, k, Epad, masks, nullptr);
-    for (int s = threadIdx.x; s < ntok * k; s += S::THREADS)
-        dest_of_src[(size_t)tok0 * k + s] = slot_rank(masks, Epad, s / k, ids_lds[s]);
+    if constexpr (RANKS)
+        for (int s = threadIdx.x; s < ntok * k; s += S::THREADS)
+            dest_of_src[(size_t)tok0 * k + s] = slot_rank(masks, Epad, s / k, ids_lds[s]);
     if constexpr (BYTES) {
         const int words = route_byte_row_vectors(E) * 4;  // 4 experts per word
         for (int i = threadIdx.x; i < words; i += S::THREADS) {
@@ -259,23 +261,6 @@ constexpr int kFusedRows = kPlaceRows;
 constexpr int kFusedSlots = kFusedRows * kChunk * kKMax / kFusedThreads;
 constexpr int kFusedWaves = kFusedThreads / kWave;
 constexpr int kMaxRowVectors = kEMax / 16;
-
-// Sum of v over the lanes of the wave that sit a multiple of QP apart (QP a
-// power of two <= 32): DPP rotations inside each 16-lane row, then the
-// permlane swaps across rows.
-template <int QP>
-__device__ __forceinline__ uint32_t add_lanes(uint32_t v) {
-    if constexpr (QP <= 1) v += dpp<0x121>(v);  // row_ror:1
-    if constexpr (QP <= 2) v += dpp<0x122>(v);  // row_ror:2
-    if constexpr (QP <= 4) v += dpp<0x124>(v);  // row_ror:4
-    if constexpr (QP <= 8) v += dpp<0x128>(v);  // row_ror:8
-    if constexpr (QP <= 16) {
-        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-        v = p[0] + p[1];
-    }
-    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return p[0] + p[1];
-}
 
 // With a COPY mode the same launch also expands the unit's token rows in
 // token order (kCopyBf16: plain copy; kCopyFp8: quantised to E4M3 with one
@@ -590,6 +575,16 @@ hipError_t launch_route_gv(const RouteArgs& a, RouteVariant v, hipStream_t strea
     return hipGetLastError();
 }
 
+template <int G, int V>
+hipError_t launch_topk_bytes_gv(const RouteArgs& a, int* nb_out, hipStream_t stream) {
+    using S = TopkShape<G>;
+    const int nb = (a.T + S::TOK - 1) / S::TOK;
+    *nb_out = nb;
+    route_topk_kernel<G, V, true, false><<<nb, S::THREADS, 0, stream>>>(
+        a.logits, a.bias, a.T, a.E, a.k, a.topk_ids, a.topk_weights, nullptr, static_cast<int32_t*>(a.workspace));
+    return hipGetLastError();
+}
+
 }  // namespace
 
 int route_keys_per_lane(int E) { return E > 32 ? 8 : 4; }
@@ -653,6 +648,19 @@ hipError_t launch_route(const RouteArgs& a, RouteVariant variant, hipStream_t st
         case 16 * 16 + 8: return launch_route_gv<16, 8>(a, v, stream);
         case 32 * 16 + 8: return launch_route_gv<32, 8>(a, v, stream);
         default: return launch_route_gv<64, 8>(a, v, stream);
+    }
+}
+
+hipError_t launch_route_topk_bytes(const RouteArgs& a, int* nb, hipStream_t stream) {
+    switch (route_lanes_per_token(a.E) * 16 + route_keys_per_lane(a.E)) {
+        case 1 * 16 + 4: return launch_topk_bytes_gv<1, 4>(a, nb, stream);
+        case 2 * 16 + 4: return launch_topk_bytes_gv<2, 4>(a, nb, stream);
+        case 4 * 16 + 4: return launch_topk_bytes_gv<4, 4>(a, nb, stream);
+        case 8 * 16 + 4: return launch_topk_bytes_gv<8, 4>(a, nb, stream);
+        case 8 * 16 + 8: return launch_topk_bytes_gv<8, 8>(a, nb, stream);
+        case 16 * 16 + 8: return launch_topk_bytes_gv<16, 8>(a, nb, stream);
+        case 32 * 16 + 8: return launch_topk_bytes_gv<32, 8>(a, nb, stream);
+        default: return launch_topk_bytes_gv<64, 8>(a, nb, stream);
     }
 }
 

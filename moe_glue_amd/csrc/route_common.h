@@ -207,6 +207,23 @@ __device__ __forceinline__ void mark_padding(const int32_t* s_cnt, const int32_t
     }
 }
 
+// Sum of v over the lanes of the wave that sit a multiple of QP apart (QP a
+// power of two <= 32): DPP rotations inside each 16-lane row, then the
+// permlane swaps across rows.
+template <int QP>
+__device__ __forceinline__ uint32_t add_lanes(uint32_t v) {
+    if constexpr (QP <= 1) v += dpp<0x121>(v);  // row_ror:1
+    if constexpr (QP <= 2) v += dpp<0x122>(v);  // row_ror:2
+    if constexpr (QP <= 4) v += dpp<0x124>(v);  // row_ror:4
+    if constexpr (QP <= 8) v += dpp<0x128>(v);  // row_ror:8
+    if constexpr (QP <= 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = p[0] + p[1];
+    }
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return p[0] + p[1];
+}
+
 // Launch shapes.
 // Multi-workgroup top-k: one token per group of G lanes, one pass, TOK tokens
 // per workgroup: 16 (THREADS = 16*G = 64..1024) for G >= 4, one wave below.

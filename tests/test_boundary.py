@@ -10,6 +10,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_glue.h")
+TESTING_HEADER = os.path.join(ROOT, "include", "moe_glue_testing.h")
 
 
 @pytest.fixture(scope="module")
@@ -22,10 +23,14 @@ def lib():
     return _binding.load()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_include_holds_only_the_two_headers():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["moe_glue.h", "moe_glue_testing.h"]
 
 
 def test_header_declares_the_four_calls():
@@ -36,14 +41,23 @@ def test_header_declares_the_four_calls():
 
 
 def test_library_exports_every_declared_symbol(lib):
-    for name in declared_functions():
-        assert hasattr(lib, name), f"{name} declared in include/moe_glue.h but not exported"
+    for header in (HEADER, TESTING_HEADER):
+        for name in declared_functions(header):
+            assert hasattr(lib, name), f"{name} declared in {os.path.basename(header)} but not exported"
 
 
 def test_binding_names_match_header():
     from moe_glue_amd import _binding
 
     assert set(_binding.EXPORTED) == set(declared_functions())
+    assert set(_binding.TESTING_EXPORTED) == set(declared_functions(TESTING_HEADER))
+
+
+def test_testing_hook_rejects_out_of_range_values(lib):
+    assert lib.moe_testing_force(4, 0, 0) == -1
+    assert lib.moe_testing_force(0, 5, 0) == -1
+    assert lib.moe_testing_force(0, 0, -1) == -1
+    assert lib.moe_testing_force(0, 0, 0) == 0
 
 
 FAKE = 0x10000  # a 16-byte-aligned non-NULL address: never dereferenced, since validation fails first
@@ -69,8 +83,8 @@ def test_route_argument_errors(lib):
     assert status(lib, lib.moe_route(*args(4, 8, 2, logits=FAKE + 2))) == "MOE_ERR_ALIGN"
 
 
-def test_route_workspace_errors(lib, monkeypatch):
-    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", "three")
+def test_route_workspace_errors(lib, force):
+    force.route("three")
     T, E, k = 4096, 128, 8
     need = lib.moe_route_workspace_bytes(T, E, k)
     hist = (4096 // 16 + 1) * 128 * 4  # 16-token histogram rows + one row of totals
@@ -175,6 +189,22 @@ def test_row_groups_host(tmp_path):
                     "-Xclang", "-packed-fp32-ops", "-I", csrc, "-I", os.path.join(ROOT, "include"), src,
                     os.path.join(csrc, "route.hip"), "-o", str(exe)], check=True, capture_output=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout + out.stderr
+
+
+def test_place_expand_indexing_host(tmp_path):
+    """The placing destination-order expand's index arithmetic for random
+    routings and forced workgroups per group: every index in bounds, every
+    destination placed and copied once, at the stable counting-sort position
+    (tests/host/place_expand_check.cpp)."""
+    exe = tmp_path / "place_expand_check"
+    src = os.path.join(ROOT, "tests", "host", "place_expand_check.cpp")
+    csrc = os.path.join(ROOT, "moe_glue_amd", "csrc")
+    subprocess.run(["hipcc", "-O2", "-std=c++17", "-x", "hip", "--offload-arch=gfx950", "-Xclang", "-target-feature",
+                    "-Xclang", "-packed-fp32-ops", "-I", csrc, "-I", os.path.join(ROOT, "include"), src,
+                    os.path.join(csrc, "route.hip"), os.path.join(csrc, "place_expand.hip"), "-o", str(exe)],
+                   check=True, capture_output=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
     assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout + out.stderr
 
 

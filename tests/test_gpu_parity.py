@@ -52,13 +52,13 @@ def test_workload_full_size(dev, oracle_lib, name):
     check_path(got, ref, cfg, name)
 
 
-@pytest.mark.parametrize("order", ["auto", "grouped", "fused"])
+@pytest.mark.parametrize("order", ["auto", "placed", "grouped", "fused"])
 @pytest.mark.parametrize("name", inputs.CONFIG_ORDER)
-def test_workload_full_size_route_expand(dev, oracle_lib, monkeypatch, name, order):
+def test_workload_full_size_route_expand(dev, oracle_lib, force, name, order):
     """Route + expand as one moe_route_expand call at full size (the form the
     benchmark times): the one-launch dispatch for decode, the grouped
     destination-order expand or the token-major one above it."""
-    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", order)
+    force.order(order)
     cfg = inputs.CONFIGS[name]
     _log(f"[parity] route_expand {inputs.describe(cfg)} seed=0 order={order}")
     inp = inputs.make_inputs(cfg, 0, parts=("x", "logits"))
@@ -102,10 +102,10 @@ ROUTE_SHAPES = [  # (T, E, k): every lanes-per-token width, odd E, limits
 
 @pytest.mark.parametrize("variant", ["auto", "single", "two", "three"])
 @pytest.mark.parametrize("T,E,k", ROUTE_SHAPES)
-def test_route_shapes_and_variants(dev, oracle_lib, monkeypatch, variant, T, E, k):
+def test_route_shapes_and_variants(dev, oracle_lib, force, variant, T, E, k):
     if variant == "single" and T > 256:
         pytest.skip("single-workgroup route covers T <= 256")
-    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
+    force.route(variant)
     _log(f"[route] T={T} E={E} k={k} variant={variant}")
     rng = np.random.default_rng([T, E, k])
     logits = rng.standard_normal((T, E)).astype(np.float32)
@@ -116,8 +116,8 @@ def test_route_shapes_and_variants(dev, oracle_lib, monkeypatch, variant, T, E, 
 
 @pytest.mark.parametrize("variant", ["single", "two", "three"])
 @pytest.mark.parametrize("kind", ["quantized", "signed_zero", "constant", "wide"])
-def test_route_ties_and_special_rows(dev, oracle_lib, monkeypatch, variant, kind):
-    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
+def test_route_ties_and_special_rows(dev, oracle_lib, force, variant, kind):
+    force.route(variant)
     T, E, k = 200, 64, 6
     _log(f"[route] {kind} rows T={T} E={E} k={k} variant={variant}")
     logits = {"quantized": lambda: inputs.quantized_logits(T, E, 3),
@@ -141,13 +141,13 @@ def test_route_empty_batch(dev, oracle_lib):
     assert G.to_host(out["expert_counts"]).tolist() == [0] * 16
 
 
-def test_route_variants_bit_identical_and_deterministic(dev, monkeypatch):
+def test_route_variants_bit_identical_and_deterministic(dev, force):
     T, E, k = 256, 128, 8
     _log("[route] determinism and variants")
     logits = inputs.quantized_logits(T, E, 9)
     results = []
     for variant in ("single", "two", "three", "two", "three", "single"):
-        monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
+        force.route(variant)
         results.append(_route_gpu(dev, logits, k))
     for r in results[1:]:
         for key in results[0]:
@@ -252,12 +252,12 @@ def test_swiglu_shapes(dev, oracle_lib, R, I):
                                      (5000, 3, 3, 8), (4096, 128, 8, 2048), (9000, 300, 4, 64),
                                      (40, 16, 4, 32768), (300, 16, 4, 32768), (150, 64, 6, 4104),
                                      (90, 128, 8, 8800)])
-@pytest.mark.parametrize("order", ["auto", "grouped", "token", "fused"])
-def test_route_expand_matches_oracle(dev, oracle_lib, monkeypatch, order, T, E, k, H):
+@pytest.mark.parametrize("order", ["auto", "placed", "grouped", "token", "fused"])
+def test_route_expand_matches_oracle(dev, oracle_lib, force, order, T, E, k, H):
     import torch
     import moe_glue_amd as mg
 
-    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", order)
+    force.order(order)
     _log(f"[route_expand] T={T} E={E} k={k} H={H} order={order}")
     cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8, bias_std=0.5 if E % 2 == 0 else 0.0)
     inp = inputs.make_inputs(cfg, 6, parts=("x", "logits"))
@@ -270,17 +270,17 @@ def test_route_expand_matches_oracle(dev, oracle_lib, monkeypatch, order, T, E, 
     compare.assert_equal(got["x_expanded"], oracle_lib.expand_rows(inp["x"], ref["dest_of_src"], k), "x_expanded")
 
 
-@pytest.mark.parametrize("order", ["grouped", "fused"])
+@pytest.mark.parametrize("order", ["placed", "grouped", "fused"])
 @pytest.mark.parametrize("variant", ["two", "three"])
-def test_route_expand_workspace_needs_no_initialisation(dev, oracle_lib, monkeypatch, variant, order):
+def test_route_expand_workspace_needs_no_initialisation(dev, oracle_lib, force, variant, order):
     """The workspace (histogram rows, row list or slot ranks) may hold
     anything: fill it with 0xFF bytes, then with zeros, and get the same
     results both times."""
     import torch
     import moe_glue_amd as mg
 
-    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
-    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", order)
+    force.route(variant)
+    force.order(order)
     T, E, k, H = 1500, 96, 6, 256
     _log(f"[route_expand] garbage workspace T={T} E={E} k={k} variant={variant} order={order}")
     cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
@@ -299,10 +299,10 @@ def test_route_expand_workspace_needs_no_initialisation(dev, oracle_lib, monkeyp
                              "x_expanded")
 
 
-@pytest.mark.parametrize("order", ["grouped", "fused"])
+@pytest.mark.parametrize("order", ["placed", "grouped", "fused"])
 @pytest.mark.parametrize("variant", ["auto", "two", "three"])
 @pytest.mark.parametrize("T,E,k,H", [(70000, 64, 2, 64), (65535, 8, 2, 16), (20000, 512, 16, 8)])
-def test_route_expand_large_batches(dev, oracle_lib, monkeypatch, variant, T, E, k, H, order):
+def test_route_expand_large_batches(dev, oracle_lib, force, variant, T, E, k, H, order):
     """Batches past the two-launch route's 2^16-token limit (a forced two-launch
     request falls back to three launches), many token groups, E = 512 with
     k = 16; grouped destination order, or the copy fused into the place step
@@ -310,8 +310,8 @@ def test_route_expand_large_batches(dev, oracle_lib, monkeypatch, variant, T, E,
     import torch
     import moe_glue_amd as mg
 
-    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
-    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", order)
+    force.route(variant)
+    force.order(order)
     _log(f"[route_expand] large T={T} E={E} k={k} H={H} variant={variant} order={order}")
     cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
     inp = inputs.make_inputs(cfg, 13, parts=("x", "logits"))
@@ -323,22 +323,61 @@ def test_route_expand_large_batches(dev, oracle_lib, monkeypatch, variant, T, E,
     compare.assert_equal(got["x_expanded"], oracle_lib.expand_rows(inp["x"], ref["dest_of_src"], k), "x_expanded")
 
 
+@pytest.mark.parametrize("wpg", [1, 2, 7, 64, 300])
+@pytest.mark.parametrize("T,E,k,H,M", [(4096, 128, 8, 2048, 1), (1500, 96, 6, 256, 1), (3000, 64, 6, 8, 1),
+                                       (777, 256, 8, 16392, 1), (5000, 16, 4, 520, 1), (2500, 128, 8, 1024, 128),
+                                       (4100, 200, 6, 264, 7)])
+def test_route_expand_placed_slicing(dev, oracle_lib, force, wpg, T, E, k, H, M):
+    """The placing destination-order expand with the number of workgroups per
+    token group forced (1 to more than the group has row chunks), rows of one
+    16-byte vector up to more than one pass of a workgroup, E not a multiple
+    of 16, padded segments: the maps and every copied row match the oracle,
+    padding rows stay untouched."""
+    import torch
+    import moe_glue_amd as mg
+
+    force.order("placed")
+    force.workgroups_per_group(wpg)
+    _log(f"[placed] T={T} E={E} k={k} H={H} pad_to={M} workgroups/group={wpg}")
+    cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8, bias_std=0.5)
+    inp = inputs.make_inputs(cfg, 17, parts=("x", "logits"))
+    ref = oracle_lib.route_padded(inp["logits"], k, M, inp["bias"])
+    P = int(ref["expert_offsets"][E])
+    rows = mg.padded_rows(T, E, k, M) if M > 1 else T * k
+    out = mg.alloc_route_outputs(T, E, k, dev)
+    out["src_of_dest"] = torch.empty((rows,), dtype=torch.int32, device=dev)
+    out["x_expanded"] = torch.full((rows, H), 0x7F7F, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    out["workspace"].fill_(0xEE)
+    bias = G.to_dev(inp["bias"], dev)
+    r = mg.route_expand_padded(G.to_dev(inp["logits"], dev), k, M, G.to_dev(inp["x"], dev), bias, out=out)
+    torch.cuda.synchronize()
+    got = G.route_host(r)
+    got["src_of_dest"] = got["src_of_dest"][:P]
+    xe = got.pop("x_expanded")[:P]
+    compare.assert_route_equal(got, ref, f"placed T={T} E={E} k={k} M={M} wpg={wpg}")
+    want = oracle_lib.expand_rows(inp["x"], ref["dest_of_src"], k, rows=P)
+    pad_rows = ref["src_of_dest"] < 0
+    compare.assert_equal(xe[~pad_rows], want[~pad_rows], "placed x_expanded (real rows)")
+    assert np.all(xe[pad_rows] == 0x7F7F), "placed: a padding row was written"
+
+
+@pytest.mark.parametrize("order", ["grouped", "placed"])
 @pytest.mark.parametrize("variant", ["single", "two", "three"])
 @pytest.mark.parametrize("T", [48, 700])
-def test_route_expand_equals_separate_calls(dev, monkeypatch, variant, T):
+def test_route_expand_equals_separate_calls(dev, force, variant, T, order):
     import torch
     import moe_glue_amd as mg
 
     if variant == "single" and T > 256:
         pytest.skip("single-workgroup route covers T <= 256")
-    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", "grouped")
+    force.order(order)
     E, k, H = 128, 8, 2048
     _log(f"[route_expand] T={T} auto vs forced variant {variant}")
     cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
     inp = inputs.make_inputs(cfg, 8, parts=("x", "logits"))
     logits, x = G.to_dev(inp["logits"], dev), G.to_dev(inp["x"], dev)
     fused = G.route_host(mg.route_expand(logits, k, x))
-    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
+    force.route(variant)
     r = mg.route_expand(logits, k, x)
     torch.cuda.synchronize()
     sep = G.route_host(r)
@@ -353,12 +392,12 @@ PADDED_CASES = [(1, 8, 2, 4), (33, 8, 2, 16), (100, 17, 5, 8), (300, 128, 8, 128
 
 @pytest.mark.parametrize("variant", ["auto", "single", "two", "three"])
 @pytest.mark.parametrize("T,E,k,M", PADDED_CASES)
-def test_route_padded_matches_oracle(dev, oracle_lib, monkeypatch, variant, T, E, k, M):
+def test_route_padded_matches_oracle(dev, oracle_lib, force, variant, T, E, k, M):
     import moe_glue_amd as mg
 
     if variant == "single" and T > 256:
         pytest.skip("single-workgroup route covers T <= 256")
-    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
+    force.route(variant)
     _log(f"[route_padded] T={T} E={E} k={k} pad_to={M} variant={variant}")
     rng = np.random.default_rng([T, E, k, M])
     logits = rng.standard_normal((T, E)).astype(np.float32)
@@ -397,17 +436,17 @@ def test_expand_combine_on_padded_layout(dev, oracle_lib, T, E, k, M, H):
                               "combine on padded y")
 
 
-@pytest.mark.parametrize("order", ["auto", "grouped", "token", "fused"])
+@pytest.mark.parametrize("order", ["auto", "placed", "grouped", "token", "fused"])
 @pytest.mark.parametrize("T,E,k,M,H", [(20, 8, 2, 16, 256), (64, 512, 16, 32, 264), (32, 128, 8, 128, 2048),
                                        (1, 3, 2, 5, 8), (300, 128, 8, 128, 2048), (77, 17, 5, 16, 520),
                                        (1023, 64, 6, 64, 4096), (4096, 128, 8, 128, 2048), (2000, 256, 8, 3, 264)])
-def test_route_expand_padded_matches_oracle(dev, oracle_lib, monkeypatch, order, T, E, k, M, H):
+def test_route_expand_padded_matches_oracle(dev, oracle_lib, force, order, T, E, k, M, H):
     """moe_route_expand_padded: the padded maps, every real row copied, the
     padding rows untouched (sentinel), in every expand order."""
     import torch
     import moe_glue_amd as mg
 
-    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", order)
+    force.order(order)
     _log(f"[route_expand_padded] T={T} E={E} k={k} pad_to={M} H={H} order={order}")
     cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8, bias_std=0.5 if E % 2 == 0 else 0.0)
     inp = inputs.make_inputs(cfg, 14, parts=("x", "logits"))
@@ -541,13 +580,13 @@ FP8_FUSED_CASES = [(1, 8, 2, 256, 8, 1), (40, 64, 6, 512, 128, 1), (300, 128, 8,
 
 @pytest.mark.parametrize("order", ["auto", "token", "fused"])
 @pytest.mark.parametrize("T,E,k,H,group,M", FP8_FUSED_CASES)
-def test_route_expand_fp8_matches_oracle(dev, oracle_lib, monkeypatch, order, T, E, k, H, group, M):
+def test_route_expand_fp8_matches_oracle(dev, oracle_lib, force, order, T, E, k, H, group, M):
     """moe_route_expand_fp8 = route (padded for M > 1) then the quantising
     expand; padding rows of the codes and scales stay untouched."""
     import torch
     import moe_glue_amd as mg
 
-    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", order)
+    force.order(order)
     _log(f"[route_expand_fp8] T={T} E={E} k={k} H={H} group={group} pad_to={M} order={order}")
     cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8, bias_std=0.5 if E % 2 == 0 else 0.0)
     inp = inputs.make_inputs(cfg, 9, parts=("x", "logits"))
@@ -580,13 +619,13 @@ MX_FUSED_CASES = [(T, E, k, H, M) for (T, E, k, H, group, M) in FP8_FUSED_CASES 
 
 @pytest.mark.parametrize("order", ["auto", "token", "fused"])
 @pytest.mark.parametrize("T,E,k,H,M", MX_FUSED_CASES)
-def test_route_expand_mxfp8_matches_oracle(dev, oracle_lib, monkeypatch, order, T, E, k, H, M):
+def test_route_expand_mxfp8_matches_oracle(dev, oracle_lib, force, order, T, E, k, H, M):
     """moe_route_expand_mxfp8 = route (padded for M > 1) then the MXFP8
     expand; padding rows of the codes and scale bytes stay untouched."""
     import torch
     import moe_glue_amd as mg
 
-    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", order)
+    force.order(order)
     _log(f"[route_expand_mxfp8] T={T} E={E} k={k} H={H} pad_to={M} order={order}")
     cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8, bias_std=0.5 if E % 2 == 0 else 0.0)
     inp = inputs.make_inputs(cfg, 10, parts=("x", "logits"))
@@ -619,7 +658,7 @@ def test_route_expand_mxfp8_matches_oracle(dev, oracle_lib, monkeypatch, order, 
 @pytest.mark.parametrize("variant", ["single", "two", "three"])
 @pytest.mark.parametrize("T,E,k,H,M", [(48, 128, 8, 2048, 1), (48, 64, 6, 512, 16), (700, 128, 8, 1024, 1),
                                        (700, 17, 5, 256, 8)])
-def test_route_expand_quantised_every_route_variant(dev, oracle_lib, monkeypatch, fmt, variant, T, E, k, H, M):
+def test_route_expand_quantised_every_route_variant(dev, oracle_lib, force, fmt, variant, T, E, k, H, M):
     """The combined quantising calls with the route variant forced: the
     single-workgroup route followed by the separate quantising expand, and
     the two- and three-launch routes (folded copy or separate expand)."""
@@ -628,7 +667,7 @@ def test_route_expand_quantised_every_route_variant(dev, oracle_lib, monkeypatch
 
     if variant == "single" and T > 256:
         pytest.skip("single-workgroup route covers T <= 256")
-    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
+    force.route(variant)
     _log(f"[route_expand_{fmt}] T={T} E={E} k={k} H={H} pad_to={M} variant={variant}")
     cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
     inp = inputs.make_inputs(cfg, 11, parts=("x", "logits"))
@@ -654,18 +693,20 @@ def test_route_expand_quantised_every_route_variant(dev, oracle_lib, monkeypatch
 
 
 @pytest.mark.parametrize("T,E,k,H,I,variant,order", [(32, 128, 8, 2048, 768, "auto", "auto"),
+                                                     (4096, 128, 8, 2048, 768, "auto", "auto"),
+                                                     (700, 64, 6, 256, 64, "two", "placed"),
                                                      (700, 64, 6, 256, 64, "two", "grouped"),
                                                      (300, 128, 8, 512, 32, "three", "token"),
                                                      (1023, 64, 6, 4096, 1408, "auto", "fused")])
-def test_graph_replay_matches_eager(dev, monkeypatch, T, E, k, H, I, variant, order):
+def test_graph_replay_matches_eager(dev, force, T, E, k, H, I, variant, order):
     """route_expand, swiglu and combine captured in one HIP graph: every replay
     (outputs overwritten with garbage by eager work in between) gives exactly
     the eager results."""
     import torch
     import moe_glue_amd as mg
 
-    monkeypatch.setenv("MOE_GLUE_ROUTE_VARIANT", variant)
-    monkeypatch.setenv("MOE_GLUE_EXPAND_ORDER", order)
+    force.route(variant)
+    force.order(order)
     _log(f"[graph] T={T} E={E} k={k} H={H} I={I} variant={variant} order={order}")
     cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=I)
     inp = inputs.make_inputs(cfg, 21, parts=("x", "logits", "h", "y"))
