@@ -241,7 +241,10 @@ double moe_ref_f64_from_e4m3(uint8_t c) {
  *   q[c]  = e4m3(fp32(x[t, c] * inv))   saturating, nearest-even
  * and every expanded row dest_of_src[t*k + j] receives the token's codes
  * (q_out [rows, H]) and scales (scales [rows, H/group]).  The divisions and
- * the product are single fp32 operations, the precision the kernel decides in. */
+ * the product are single fp32 operations, the precision the kernel decides in,
+ * taken without fp32's exponent limits: for amax below 2^-64, 448/amax would
+ * overflow, so x and amax are first multiplied by 2^64 (exact for such small
+ * values), which gives the significands an unlimited exponent range would. */
 void moe_ref_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, int T, int H, int k, int group,
                              uint8_t* q_out, float* scales) {
     const int G = H / group;
@@ -253,12 +256,13 @@ void moe_ref_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, int 
                 if (v > amax) amax = v;
             }
             const float scale = amax / 448.0f;
-            const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+            const float pre = amax < 0x1p-64f ? 0x1p64f : 1.0f;
+            const float inv = amax > 0.0f ? 448.0f / (amax * pre) : 0.0f;
             for (int j = 0; j < k; ++j) {
                 const int64_t dst_row = dest_of_src[(size_t)t * k + j];
                 scales[(size_t)dst_row * G + g] = scale;
                 for (int c = g * group; c < (g + 1) * group; ++c) {
-                    const float xv = (float)moe_ref_f64_from_bf16(x[(size_t)t * H + c]);
+                    const float xv = (float)moe_ref_f64_from_bf16(x[(size_t)t * H + c]) * pre;
                     q_out[(size_t)dst_row * H + c] = moe_ref_e4m3_from_f32(xv * inv);
                 }
             }

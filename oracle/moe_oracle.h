@@ -53,8 +53,10 @@ void moe_ref_expand_rows(const uint16_t* x, const int32_t* dest_of_src, int T, i
                          uint16_t* x_exp);
 
 /* FP8 quantising expand: per token and group of `group` columns, scale =
- * fp32(amax/448), codes = e4m3(fp32(x * fp32(448/amax))) saturating; codes
- * and scales written to every expanded row of the token.
+ * fp32(amax/448), codes = e4m3(fp32(x * fp32(448/amax))) saturating, the two
+ * fp32 roundings taken without exponent limits (x and amax scaled by 2^64
+ * when amax < 2^-64); codes and scales written to every expanded row of the
+ * token.
  * q_out [rows, H] uint8 codes, scales [rows, H/group] fp32. */
 void moe_ref_expand_rows_fp8(const uint16_t* x, const int32_t* dest_of_src, int T, int H, int k, int group,
                              uint8_t* q_out, float* scales);

@@ -477,19 +477,31 @@ def pin_e4m3_rounding(o) -> list:
     return fails
 
 
+def _round_sig24(v: np.ndarray) -> np.ndarray:
+    """v (float64) rounded to a 24-bit significand, nearest-even, with no
+    exponent limits: the significand from frexp goes through float32 (in
+    [0.5, 1) it is always normal), the exponent is put back in float64."""
+    m, e = np.frexp(np.asarray(v, np.float64))
+    return np.ldexp(m.astype(np.float32).astype(np.float64), e)
+
+
 def _bruteforce_expand_fp8(x_bits, dest, k, group, rows):
+    """The FP8 reading with fp32 roundings and no exponent limits: inv =
+    448/amax to 24 bits, the product x * inv to 24 bits (exact in float64
+    before that rounding), clamped, then torch's own E4M3 conversion."""
     T, H = x_bits.shape
     G = H // group
-    xv = bf.bf16_to_float(x_bits).astype(np.float32)
+    xv = bf.bf16_to_float(x_bits).astype(np.float64)
     q = np.zeros((rows, H), np.uint8)
     sc = np.zeros((rows, G), np.float32)
     for t in range(T):
         for g in range(G):
             seg = xv[t, g * group:(g + 1) * group]
-            amax = np.float32(np.max(np.abs(seg)))
-            scale = np.float32(amax / np.float32(448.0))
-            inv = np.float32(np.float32(448.0) / amax) if amax > 0 else np.float32(0.0)
-            codes = _torch_e4m3((seg * inv).astype(np.float32))
+            amax = np.max(np.abs(seg))
+            scale = np.float32(np.float32(amax) / np.float32(448.0))
+            inv = _round_sig24(448.0 / amax) if amax > 0 else 0.0
+            prod = np.clip(_round_sig24(seg * inv), -448.0, 448.0)
+            codes = _torch_e4m3(prod.astype(np.float32))
             for j in range(k):
                 d = dest[t * k + j]
                 q[d, g * group:(g + 1) * group] = codes
@@ -497,11 +509,28 @@ def _bruteforce_expand_fp8(x_bits, dest, k, group, rows):
     return q, sc
 
 
+def _tiny_groups(x_bits, group):
+    """Rows 1 and 2 of x: groups whose maximum is tiny -- row 1 alternates
+    groups of about 1e-37 (below 448/FLT_MAX, where 448/amax overflows fp32)
+    and of about 1e-25 (below 2^-64, no overflow), row 2 holds bf16
+    subnormals (magnitudes 2^-133 and up), signs mixed."""
+    T, H = x_bits.shape
+    rng = np.random.default_rng(99)
+    if T > 1:
+        mag = np.where((np.arange(H) // group) % 2 == 0, 1e-37, 1e-25)
+        x_bits[1] = bf.bf16_round_exact_np(rng.standard_normal(H) * mag)
+    if T > 2:
+        sub = rng.integers(1, 0x80, H).astype(np.uint16)  # subnormal magnitudes, 1..127 quanta of 2^-133
+        x_bits[2] = sub | (rng.integers(0, 2, H).astype(np.uint16) << 15)
+    return x_bits
+
+
 def pin_expand_fp8(o) -> list:
     fails = []
     rng = _rng(10)
     for (T, H, E, k, group) in ((5, 32, 8, 2, 8), (4, 64, 6, 3, 16), (3, 128, 4, 4, 128), (6, 48, 5, 1, 16)):
         x = _rand_bf16(rng, (T, H), scale=3.0)
+        x = _tiny_groups(x, group)
         x[0, :group] = 0  # an all-zero group
         r = o.route(rng.standard_normal((T, E)).astype(np.float32), k)
         q, sc = o.expand_rows_fp8(x, r["dest_of_src"], k, group)

@@ -80,6 +80,9 @@ MUTANTS = [
     ("fp8_divide_by_scale", "q_out[(size_t)dst_row * H + c] = moe_ref_e4m3_from_f32(xv * inv);",
      "q_out[(size_t)dst_row * H + c] = moe_ref_e4m3_from_f32(xv / scale);"),
     ("fp8_scales_by_token", "scales[(size_t)dst_row * G + g] = scale;", "scales[(size_t)t * G + g] = scale;"),
+    ("fp8_no_prescale", "const float pre = amax < 0x1p-64f ? 0x1p64f : 1.0f;", "const float pre = 1.0f;"),
+    ("fp8_prescale_inverse_only", "const float xv = (float)moe_ref_f64_from_bf16(x[(size_t)t * H + c]) * pre;",
+     "const float xv = (float)moe_ref_f64_from_bf16(x[(size_t)t * H + c]);"),
     ("fp8_amax_first_only",
      "for (int c = g * group; c < (g + 1) * group; ++c) {\n                float v = fabsf(",
      "for (int c = g * group; c < g * group + 1; ++c) {\n                float v = fabsf("),
