@@ -156,6 +156,9 @@ moe_status moe_expand_rows(const uint16_t* x, const int32_t* dest_of_src, int32_
  *   scale = fp32(amax / 448)
  *   inv   = fp32(448 / amax)  (0 when amax = 0)
  *   code  = E4M3(clamp(fp32(x[t, c] * inv), -448, 448)), nearest-even
+ * where inv and the product are fp32 roundings without fp32's exponent
+ * limits (for amax < 2^-64, x and amax are scaled by 2^64 first, exactly;
+ * scale is then an fp32 subnormal)
  * (OCP FP8 E4M3: bias 7, largest finite 448), and every expanded row
  * dest_of_src[t*k + j] receives the token's codes and scales:
  *   x_expanded uint8 [rows, H] codes, scales fp32 [rows, H/group],
@@ -297,7 +300,10 @@ moe_status moe_swiglu(const uint16_t* h, int32_t R, int32_t I, uint16_t* act, vo
  * accumulated in fp32 in j order, rounded once to nearest even.
  * y bf16 [T*k, H]; topk_weights fp32 [T,k]; dest_of_src int32 [T*k];
  * out bf16 [T, H].  H % 8 == 0 and y, out 16-byte aligned, else MOE_ERR_ALIGN.
- * dest_of_src entries must lie in [0, T*k) (not checked).
+ * dest_of_src entries must be rows of y (not checked): in [0, T*k) for the
+ * layout of moe_route, in [0, expert_offsets[E]) -- at most
+ * moe_route_padded_rows(T, E, k, pad_to) -- for that of moe_route_padded,
+ * whose padding rows combine never reads.
  * T = 0 is a no-op.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN,
  * MOE_ERR_UNSUPPORTED (T*H/8 >= 2^31), MOE_ERR_HIP. */
 moe_status moe_combine(const uint16_t* y, const float* topk_weights, const int32_t* dest_of_src,

@@ -85,7 +85,7 @@ __global__ __launch_bounds__((SingleShape<G>::THREADS)) void route_expand_small_
             const uint32_t t = fastdiv(i, div_h16);
             const uint32_t c = i - t * H16;
             const BlockScale bs = block_scale(amax_bits, mx);
-            const u32x2 codes = quantize8_e4m3(f, bs.inv);
+            const u32x2 codes = quantize8_e4m3(f, bs.inv, bs.pre);
             const bool first_of_group = (threadIdx.x % (uint32_t)gl) == 0;
             u32x2* q_out = static_cast<u32x2*>(out);
             for (int j = js; j < k; j += ks) {

@@ -40,7 +40,8 @@ __global__ __launch_bounds__(kThreads) void expand_rows_fp8_kernel(const u32x4* 
     if (!live) return;
     const float amax = __builtin_bit_cast(float, amax_bits);
     const float scale = e4m3_scale(amax);
-    const u32x2 codes = quantize8_e4m3(f, e4m3_inverse_scale(amax));
+    const float pre = e4m3_prescale(amax_bits);
+    const u32x2 codes = quantize8_e4m3(f, e4m3_inverse_scale(amax, pre), pre);
     uint32_t t = fastdiv(i, div_h16);
     if constexpr (ROW_PER_WAVE) t = uniform(t);
     const uint32_t c = i - t * H16;

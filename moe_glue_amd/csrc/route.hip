@@ -451,7 +451,7 @@ __device__ __forceinline__ void scan_place(
             const uint32_t amax_bits = group_abs_max(abs_max_bits8(f), cp.gl);
             if (present) {
                 const BlockScale bs = block_scale(amax_bits, cp.mx);
-                const u32x2 codes = quantize8_e4m3(f, bs.inv);
+                const u32x2 codes = quantize8_e4m3(f, bs.inv, bs.pre);
                 const bool first_of_group = (threadIdx.x % (uint32_t)cp.gl) == 0;
                 const uint32_t g = col / (uint32_t)cp.gl;
                 for (int j = 0; j < k; ++j) {

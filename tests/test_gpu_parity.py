@@ -614,6 +614,65 @@ def test_route_expand_fp8_matches_oracle(dev, oracle_lib, force, order, T, E, k,
     assert np.all(sch[~valid] == -7.0) and np.all(got["scales"][n:] == -7.0), "scales written into padding rows"
 
 
+def _with_tiny_groups(x, group, seed):
+    """x with tiny groups planted in several tokens: maxima of about 1e-37
+    (448/amax overflows fp32), about 1e-25 (below 2^-64, no overflow) and
+    bf16 subnormals (2^-133 and up), signs mixed; other groups untouched."""
+    import bruteforce as bf
+
+    x = x.copy()
+    T, H = x.shape
+    rng = np.random.default_rng(seed)
+    for t in range(0, T, max(1, T // 7)):
+        kind = t % 3
+        g0 = (t // 3) % max(1, H // group) * group
+        if kind == 0:
+            x[t, g0:g0 + group] = bf.bf16_round_exact_np(rng.standard_normal(group) * 1e-37)
+        elif kind == 1:
+            x[t, g0:g0 + group] = bf.bf16_round_exact_np(rng.standard_normal(group) * 1e-25)
+        else:
+            x[t, g0:g0 + group] = rng.integers(1, 0x80, group).astype(np.uint16) | \
+                (rng.integers(0, 2, group).astype(np.uint16) << 15)
+    return x
+
+
+@pytest.mark.parametrize("path", ["expand", "dispatch", "folded", "separate"])
+@pytest.mark.parametrize("group", [8, 32, 128])
+def test_fp8_tiny_groups(dev, oracle_lib, force, path, group):
+    """FP8 groups whose maximum is tiny (448/amax overflows fp32, or amax is a
+    bf16 subnormal): codes and scales as the oracle's exponent-unlimited
+    reading gives them, through the quantising expand, the one-launch
+    dispatch (T <= 64), the copy folded into the route's place launch and
+    the route followed by the separate quantising expand."""
+    import torch
+    import moe_glue_amd as mg
+
+    T = 48 if path == "dispatch" else 300
+    E, k, H = 64, 6, 1024
+    _log(f"[fp8 tiny groups] path={path} T={T} group={group}")
+    cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
+    inp = inputs.make_inputs(cfg, 31, parts=("x", "logits"))
+    x = _with_tiny_groups(inp["x"], group, 5)
+    ref = oracle_lib.route(inp["logits"], k)
+    qr, scr = oracle_lib.expand_rows_fp8(x, ref["dest_of_src"], k, group)
+    if path == "expand":
+        q, sc = mg.expand_rows_fp8(G.to_dev(x, dev), G.to_dev(ref["dest_of_src"], dev), k, group)
+        torch.cuda.synchronize()
+        q, sc = G.to_host(q), G.to_host(sc)
+    else:
+        force.order({"dispatch": "auto", "folded": "fused", "separate": "token"}[path])
+        if path != "dispatch":
+            force.route("two")
+        r = mg.route_expand_fp8(G.to_dev(inp["logits"], dev), k, G.to_dev(x, dev), group)
+        torch.cuda.synchronize()
+        got = G.route_host(r)
+        compare.assert_route_equal({key: v for key, v in got.items() if key not in ("x_expanded", "scales")}, ref,
+                                   f"fp8 tiny groups route ({path})")
+        q, sc = got["x_expanded"], got["scales"]
+    compare.assert_equal(sc, scr, f"fp8 tiny-group scales ({path})")
+    compare.assert_equal(q, qr, f"fp8 tiny-group codes ({path})")
+
+
 MX_FUSED_CASES = [(T, E, k, H, M) for (T, E, k, H, group, M) in FP8_FUSED_CASES if H % 32 == 0]
 
 
