@@ -8,16 +8,23 @@
 // this part a cooperative launch and its grid barrier cost far more than a
 // launch, and a plain launch gives no co-residency guarantee for spinning on a
 // flag.  So no workgroup waits for another: for a small batch (T <= 64) the
-// routing is cheap enough that every workgroup recomputes all of it in LDS
-// (top-k, bitmaps, scan, destinations), then copies its own share of the
-// rows.  Workgroup 0 also writes the routing outputs.  Each workgroup issues
-// the loads of its rows first, so their latency hides behind the routing.
-// A block of columns (one 16-byte vector per lane) is shared by `ks`
-// workgroups, each storing every ks-th of the k destination rows: at decode
-// sizes the column blocks alone would leave a handful of CUs issuing all the
-// stores, and routing once more per workgroup costs less than that.  The same
-// kernel serves the padded layout (pad_to) and the FP8 and MXFP8 quantising
-// copies.
+// routing is cheap enough that every workgroup recomputes all of it in LDS,
+// then copies its own share of the rows.  Workgroup 0 also writes the routing
+// outputs.  Each workgroup issues the loads of its rows first, so their
+// latency hides behind the routing.  A block of columns (one 16-byte vector
+// per lane) is shared by `ks` workgroups, each storing every ks-th of the k
+// destination rows: at decode sizes the column blocks alone would leave a
+// handful of CUs issuing all the stores, and routing once more per workgroup
+// costs less than that.  The same kernel serves the padded layout (pad_to) and
+// the FP8 and MXFP8 quantising copies.
+//
+// The routing is shaped for latency, since each workgroup runs it once on a
+// cold instruction cache and nothing else hides it: the top-k rounds stay a
+// rolled loop; each token's picks set its bit in the pick's 64-bit LDS bitmap
+// (T <= 64: one word per expert), so counts are popcounts and a slot's rank
+// is the popcount of the bits below its token; every wave scans the counts
+// itself into its own offset table and every lane forms the destinations of
+// its own rows.  Two barriers: after the clearing and after the top-k.
 #include "fp8_common.h"
 #include "place_copy.h"
 #include "route_common.h"
@@ -30,6 +37,7 @@ namespace {
 using namespace route_detail;
 
 constexpr uint32_t kSmallDispatchWorkgroups = 64;
+static_assert(kRouteSmallDispatchMaxTokens <= 64, "one bitmap word per expert");
 
 template <int G, int V, int MODE>
 __global__ __launch_bounds__((SingleShape<G>::THREADS)) void route_expand_small_kernel(
@@ -37,13 +45,15 @@ __global__ __launch_bounds__((SingleShape<G>::THREADS)) void route_expand_small_
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ expert_counts, int32_t* __restrict__ dest_of_src, int32_t* __restrict__ src_of_dest,
     const u32x4* __restrict__ x, uint32_t H16, FastDiv div_h16, int ks, void* __restrict__ out,
-    void* __restrict__ scales, uint32_t G_groups, int gl, bool mx) {
+    void* __restrict__ scales, uint32_t G_groups, int gl_q, bool mx) {
     using S = SingleShape<G>;
-    __shared__ int32_t ids_lds[kRouteSmallDispatchMaxTokens * kKMax];
-    __shared__ unsigned long long masks[kEMax];
-    __shared__ int32_t s_cnt[kEMax];
-    __shared__ int32_t s_off[kEMax + 1];
-    __shared__ int32_t s_dest[kRouteSmallDispatchMaxTokens * kKMax];
+    constexpr int NW = S::THREADS / kWave;
+    __shared__ int32_t s_ids[kRouteSmallDispatchMaxTokens * kKMax];  // [t][r]: expert of rank r
+    __shared__ unsigned long long s_mask[kEMax];                     // bit t: token t picked expert e
+    __shared__ int32_t s_off[NW][kEMax + 1];                         // each wave's offset table
+
+    const int lane = (int)(threadIdx.x % kWave);
+    const int wave = (int)(threadIdx.x / kWave);
 
     // this workgroup's item of x (one 16-byte vector per lane), loaded first
     const uint32_t n = (uint32_t)T * H16;
@@ -53,46 +63,97 @@ __global__ __launch_bounds__((SingleShape<G>::THREADS)) void route_expand_small_
     if (i < n) v = load_stream(x + i);
 
     const bool writer = blockIdx.x == 0;
-    route_small<G, V>(logits, bias, T, E, k, pad, writer, topk_ids, topk_weights, expert_offsets, expert_counts,
-                      ids_lds, masks, s_cnt, s_off);
-    mark_padding<S::THREADS>(s_cnt, s_off, E, pad, blockIdx.x, gridDim.x, src_of_dest);  // experts dealt out
-    const int Epad = (E + 3) & ~3;
-    for (int s = threadIdx.x; s < T * k; s += S::THREADS) {
-        const int e = ids_lds[s];
-        const int d = s_off[e] + slot_rank(masks, Epad, s / k, e);
-        s_dest[s] = d;
-        if (writer) {
-            dest_of_src[s] = d;
-            src_of_dest[d] = s;
-        }
+    const int grp = (int)threadIdx.x / G;
+    const int gl = (int)threadIdx.x % G;
+    const int wave_first = wave * (kWave / G);  // first token slot of this wave in a pass
+
+    for (int e = (int)threadIdx.x; e < E; e += S::THREADS) s_mask[e] = 0ull;
+    __syncthreads();  // bitmaps clear
+
+    for (int t0 = 0; t0 < T; t0 += S::TOK_PER_PASS) {
+        if (t0 + wave_first >= T) continue;  // wave-uniform: the lane exchange stays whole-wave
+        const int t = t0 + grp;
+        // ids of token t into s_ids[t][r] (and, from workgroup 0, topk_ids and topk_weights)
+        topk_token<G, V>(logits, bias, T, E, k, t, t, gl, writer ? topk_ids : nullptr, topk_weights, s_ids);
+        // its picks into the bitmaps: lane gl set ranks gl + G*j (written by this lane)
+        if (t < T)
+            for (int r = gl; r < k; r += G) atomicOr(&s_mask[s_ids[t * k + r]], 1ull << t);
     }
-    __syncthreads();
+    __syncthreads();  // every pick in the bitmaps
+
+    // this wave's offset table: exclusive scan of the padded counts (lane
+    // owns `per` consecutive experts, their bitmaps read in one go)
+    int32_t* off = s_off[wave];
+    {
+        constexpr int PER_MAX = kEMax / kWave;
+        const int per = (E + kWave - 1) / kWave;
+        const int base = lane * per;
+        const int own = max(0, min(per, E - base));
+        int len[PER_MAX];
+#pragma unroll
+        for (int q = 0; q < PER_MAX; ++q) len[q] = q < own ? __popcll(s_mask[base + q]) : 0;
+        if (pad > 1)  // uniform
+#pragma unroll
+            for (int q = 0; q < PER_MAX; ++q) len[q] = (len[q] + pad - 1) / pad * pad;
+        int local = 0;
+#pragma unroll
+        for (int q = 0; q < PER_MAX; ++q) local += len[q];
+        const int incl = wave_inclusive_sum(local);
+        int run = incl - local;
+#pragma unroll
+        for (int q = 0; q < PER_MAX; ++q) {
+            if (q < own) off[base + q] = run;
+            run += len[q];
+        }
+        if (lane == kWave - 1) off[E] = incl;
+    }
+    // destination of slot (t, j): the expert's offset plus the tokens below t that picked it
+    auto dest = [&](int t, int j) {
+        const int e = s_ids[t * k + j];
+        return off[e] + __popcll(s_mask[e] & ((1ull << t) - 1ull));
+    };
+
     if constexpr (MODE == kCopyBf16) {
         if (i < n) {
             const uint32_t t = fastdiv(i, div_h16);
             const uint32_t c = i - t * H16;
             u32x4* x_exp = static_cast<u32x4*>(out);
-            for (int j = js; j < k; j += ks) store_stream(x_exp + (size_t)s_dest[t * k + j] * H16 + c, v);
+            for (int j = js; j < k; j += ks) store_stream(x_exp + (size_t)dest((int)t, j) * H16 + c, v);
         }
     } else {
         // E4M3 as moe_expand_rows_fp8 (or, with mx, moe_expand_rows_mxfp8): a
-        // scale group is gl consecutive lanes of one row (H/8 is a multiple of
-        // gl, so no group straddles the end of x)
+        // scale group is gl_q consecutive lanes of one row (H/8 is a multiple
+        // of gl_q, so no group straddles the end of x)
         float f[8];
         unpack8(v, f);
-        const uint32_t amax_bits = group_abs_max(abs_max_bits8(f), gl);
+        const uint32_t amax_bits = group_abs_max(abs_max_bits8(f), gl_q);
         if (i < n) {
             const uint32_t t = fastdiv(i, div_h16);
             const uint32_t c = i - t * H16;
             const BlockScale bs = block_scale(amax_bits, mx);
             const u32x2 codes = quantize8_e4m3(f, bs.inv, bs.pre);
-            const bool first_of_group = (threadIdx.x % (uint32_t)gl) == 0;
+            const bool first_of_group = (threadIdx.x % (uint32_t)gl_q) == 0;
             u32x2* q_out = static_cast<u32x2*>(out);
             for (int j = js; j < k; j += ks) {
-                const size_t d = (size_t)s_dest[t * k + j];
+                const size_t d = (size_t)dest((int)t, j);
                 __builtin_nontemporal_store(codes, q_out + d * H16 + c);
-                if (first_of_group) store_block_scale(scales, d * G_groups + c / (uint32_t)gl, bs, mx);
+                if (first_of_group) store_block_scale(scales, d * G_groups + c / (uint32_t)gl_q, bs, mx);
             }
+        }
+    }
+
+    // padding rows (src_of_dest = -1): experts dealt to the waves of the grid
+    if (pad > 1)
+        for (int e = (int)blockIdx.x * NW + wave; e < E; e += (int)gridDim.x * NW)
+            for (int p = off[e] + __popcll(s_mask[e]) + lane; p < off[e + 1]; p += kWave) src_of_dest[p] = -1;
+    if (writer) {
+        for (int e = (int)threadIdx.x; e <= E; e += S::THREADS) expert_offsets[e] = off[e];
+        if (expert_counts != nullptr)
+            for (int e = (int)threadIdx.x; e < E; e += S::THREADS) expert_counts[e] = __popcll(s_mask[e]);
+        for (int s2 = (int)threadIdx.x; s2 < T * k; s2 += S::THREADS) {
+            const int d = dest(s2 / k, s2 % k);
+            dest_of_src[s2] = d;
+            src_of_dest[d] = s2;
         }
     }
 }

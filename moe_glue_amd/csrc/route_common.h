@@ -41,28 +41,33 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, con
     static_assert(V > 0 && (V & (V - 1)) == 0, "the tournament pairs keys: V must be a power of two");
     constexpr int NJ = (kKMax + G - 1) / G;  // slots a lane may own: r = gl + G*j
     const bool live = t < T;
+    // loads from clamped addresses, all issued before any is used (a load
+    // under a lane condition would make the compiler wait for it on the spot);
+    // the caller guarantees T >= 1
+    const size_t row = (size_t)min(t, T - 1) * E;
     float vals[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-        const int e = gl + G * i;
-        vals[i] = (live && e < E) ? logits[(size_t)t * E + e] : 0.0f;
+    for (int i = 0; i < V; ++i) vals[i] = logits[row + min(gl + G * i, E - 1)];
+    if (bias != nullptr) {  // uniform
+        float b[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) b[i] = bias[min(gl + G * i, E - 1)];
+#pragma unroll
+        for (int i = 0; i < V; ++i) vals[i] = vals[i] + b[i];
     }
     // key[i] of expert gl + G*i: orderable fp32 key, 0 = absent or taken
     // (every real key is above 0: orderable(-inf) = 0x007FFFFF)
     uint32_t key[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-        const int e = gl + G * i;
-        float kf = vals[i];
-        if (bias != nullptr && e < E) kf = kf + bias[e];
-        key[i] = (live && e < E) ? orderable(kf) : 0u;
-    }
+    for (int i = 0; i < V; ++i) key[i] = (live && gl + G * i < E) ? orderable(vals[i]) : 0u;
     uint32_t my_id[NJ];
     uint32_t my_key[NJ];
     uint32_t top0 = 0;
-#pragma unroll
-    for (int r = 0; r < kKMax; ++r) {
-        if (r < k) {  // k is uniform: no divergence around the lane exchange
+    // rounds as a rolled loop: the small-batch kernels run this code once per
+    // workgroup, where fetching an unrolled copy costs more than the loop
+#pragma unroll 1
+    for (int r = 0; r < k; ++r) {
+        {  // k is uniform: no divergence around the lane exchange
             // the lane's best: largest key, lowest expert on equal keys, by a
             // pairwise tournament (log2 V dependent steps, not V - 1): the
             // left candidate holds the lower experts, so it keeps ties
@@ -91,10 +96,12 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, con
             for (int i = 0; i < V; ++i)  // the owner retires the winner
                 if ((uint32_t)(gl + G * i) == win) key[i] = 0u;
             if (r == 0) top0 = top;
-            if ((r % G) == gl) {
-                my_id[r / G] = win;
-                my_key[r / G] = top;
-            }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)  // static indices: r = gl + G*j
+                if (r == gl + G * j) {
+                    my_id[j] = win;
+                    my_key[j] = top;
+                }
         }
     }
     // weights: softmax over the k selected keys, relative to the largest
