@@ -46,10 +46,10 @@ _ROUTE_SOURCES = ("route.hip", "route_common.h", "fp8_common.h", "place_copy.h")
 KERNEL_SOURCES = {"route": _ROUTE_SOURCES, "expand": ("expand.hip",), "expand_fp8": ("quant.hip", "fp8_common.h"),
                   "expand_mxfp8": ("quant.hip", "fp8_common.h"),
                   "swiglu": ("swiglu.hip",), "combine": ("combine.hip",),
-                  "route_expand": _ROUTE_SOURCES + ("dispatch.hip", "expand.hip"),
-                  "route_expand_padded": _ROUTE_SOURCES + ("expand.hip",),
-                  "route_expand_fp8": _ROUTE_SOURCES + ("quant.hip",),
-                  "route_expand_mxfp8": _ROUTE_SOURCES + ("quant.hip",)}
+                  "route_expand": _ROUTE_SOURCES + ("dispatch.hip", "expand.hip", "place_expand.hip"),
+                  "route_expand_padded": _ROUTE_SOURCES + ("dispatch.hip", "expand.hip", "place_expand.hip"),
+                  "route_expand_fp8": _ROUTE_SOURCES + ("dispatch.hip", "quant.hip"),
+                  "route_expand_mxfp8": _ROUTE_SOURCES + ("dispatch.hip", "quant.hip")}
 
 
 def algorithmic_bytes(cfg, fp8_group: int = 0) -> dict:
@@ -75,10 +75,18 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
+def variant_name(cfg_name: str, pad_to: int = 1, fp8_group: int = 0, mxfp8: bool = False) -> str:
+    """The workload's name with its layout and quantisation options, as the
+    profiles name it: qwen3_30b_a3b, qwen3_30b_a3b_pad128_fp8g128, ..."""
+    return (cfg_name + (f"_pad{pad_to}" if pad_to > 1 else "") + (f"_fp8g{fp8_group}" if fp8_group else "")
+            + ("_mxfp8" if mxfp8 else ""))
+
+
 def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary
-    (profiles/traffic_<workload>.md), or None when there is none or the
-    kernel's source changed since the counters were taken."""
+    """HBM bytes per step of one call from the committed rocprofv3 counter
+    summary (profiles/traffic_<workload>.md, workload as variant_name gives
+    it), or None when there is none or the call's sources changed since the
+    counters were taken."""
     path = os.path.join(PROFILES, f"traffic_{workload}.md")
     if not os.path.exists(path):
         return None
@@ -366,28 +374,205 @@ def cpu_model() -> str:
     return "unknown CPU"
 
 
-def cpu_baseline(inp, budget_s=10.0, max_passes=60):
-    """The CPU oracle as it stands, single-threaded, on the same workload:
-    whole passes over the batch for about `budget_s` seconds of CPU work."""
+def _cpu_leg(config: str, seed: int, leg: str, budget_s: float, max_passes: int = 400) -> dict:
+    """One leg of the CPU baseline, run in this (child) process, which never
+    touches the GPU: the oracle as it stands on the same seeded workload,
+    whole passes for about `budget_s` seconds after one warm pass.  Leg
+    "single": the plain oracle on one thread pinned to one core.  Leg "all":
+    the oracle's own calls split over token and row ranges on every core
+    this process may use (oracle/threaded.py; the route stays one call)."""
     import oracle
+    from moe_glue_amd import inputs as I
+    from oracle import threaded
 
-    o = oracle.get()
+    cores = sorted(os.sched_getaffinity(0))
+    if leg == "single":
+        os.sched_setaffinity(0, {cores[0]})
+        workers = 1
+        run = oracle.get().path
+    else:
+        workers = len(cores)
+        o = oracle.get()
+        run = lambda inp: threaded.path(inp, workers, o)  # noqa: E731
+    cfg = I.CONFIGS[config]
+    inp = I.make_inputs(cfg, seed)
     t0 = time.perf_counter()
-    o.path(inp)  # warm: page in, build
+    run(inp)  # warm: page in
     warm = time.perf_counter() - t0
     passes = max(1, min(max_passes, int(budget_s / max(warm, 1e-3))))
     t0 = time.perf_counter()
     for _ in range(passes):
-        o.path(inp)
+        run(inp)
     total = time.perf_counter() - t0
-    t = total / passes
-    ab = algorithmic_bytes(inp["cfg"])
+    return {"leg": leg, "workers": workers, "passes": passes, "seconds": total, "per_pass": total / passes,
+            "pinned_core": cores[0] if leg == "single" else None}
+
+
+def cpu_baseline(cfg, seed, budget_s=10.0):
+    """The CPU oracle timed on this host's cores in two legs, each in a child
+    process (so no GPU state is involved): one thread pinned to one core, and
+    every usable core.  `value` is the all-cores leg."""
+    import subprocess
+
+    legs = {}
+    for leg in ("single", "all"):
+        out = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-leg", leg, "--config", cfg.name,
+                              "--seed", str(seed), "--cpu-budget", str(budget_s)],
+                             capture_output=True, text=True, check=True)
+        legs[leg] = json.loads(out.stdout.strip().splitlines()[-1])
+    ab = algorithmic_bytes(cfg)
     path_bytes = ab["route"] + ab["expand"] + ab["swiglu"] + ab["combine"]
-    return {"value": inp["cfg"].T / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "GBps": round(path_bytes / t / 1e9, 3),
-            "sample": f"the full {inp['cfg'].name} batch (T={inp['cfg'].T}), route+expand+swiglu+combine, "
-                      f"{passes} passes ({total:.1f} s) after one warm pass, single thread, {t:.3f} s per pass, "
-                      f"{cpu_model()}, {os.cpu_count()} logical CPUs visible"}
+    a, s1 = legs["all"], legs["single"]
+    return {"value": round(cfg.T / a["per_pass"], 1), "unit": "tokens/s", "cores": a["workers"], "kind": "oracle",
+            "GBps": round(path_bytes / a["per_pass"] / 1e9, 3),
+            "single_core": {"value": round(cfg.T / s1["per_pass"], 1), "unit": "tokens/s", "cores": 1,
+                            "GBps": round(path_bytes / s1["per_pass"] / 1e9, 3), "pinned_core": s1["pinned_core"]},
+            "sample": f"the full {cfg.name} batch (T={cfg.T}), route+expand+swiglu+combine on the CPU oracle; "
+                      f"all cores: {a['workers']} threads over token/row ranges (route one call), {a['passes']} passes "
+                      f"in {a['seconds']:.1f} s, {a['per_pass']:.3f} s per pass; single core (pinned to CPU "
+                      f"{s1['pinned_core']}): {s1['passes']} passes in {s1['seconds']:.1f} s, {s1['per_pass']:.3f} s "
+                      f"per pass; each after one warm pass; {cpu_model()}, {os.cpu_count()} logical CPUs on the host"}
+
+
+# ------------------------------------------------- rocprofv3 output summaries
+def _short_kernel_name(name: str) -> str:
+    name = name.replace("moe::(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0]
+
+
+def summarize_trace(csv_path: str, skip: int) -> str:
+    """Per-kernel dispatch durations from a rocprofv3 kernel-trace CSV: the
+    first `skip` dispatches of each kernel (the warm-up steps) are dropped,
+    then the median, mean, min and max over the rest, as a markdown table."""
+    import csv
+    import statistics
+
+    durs = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            name = _short_kernel_name(r["Kernel_Name"])
+            if name.startswith("copy_probe"):  # the 1 GiB copies and the 16-byte launch-floor copies apart
+                name += f" [{int(r['Grid_Size_X'])} lanes]"
+            durs.setdefault(name, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines = ["| kernel | dispatches timed | median ns | mean ns | min ns | max ns |", "|---|---|---|---|---|---|"]
+    for name, d in sorted(durs.items(), key=lambda kv: -statistics.median(kv[1])):
+        d = d[skip:] if len(d) > skip else d
+        lines.append(f"| `{name}` | {len(d)} | {statistics.median(d):.0f} | {statistics.mean(d):.0f} | {min(d)} | "
+                     f"{max(d)} |")
+    return "\n".join(lines)
+
+
+# Counter passes for HBM traffic (each its own rocprofv3 run; at most 4 TCC
+# counters per pass).  Every request is counted by its size, so bytes are
+# exact sums, not a scale fitted to a copy.
+PMC_READ = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum")
+PMC_WRITE = ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum")
+COPY_PROBE_LANES = (1 << 30) // 16  # the 1 GiB copy probe: one 16-byte vector per lane
+
+
+def _pmc_dispatches(read_dir: str, write_dir: str) -> list:
+    """Per-dispatch counters from the two passes, in dispatch order of the
+    read pass: [(kernel, grid_size, {counter: value})]."""
+    import csv
+    import glob
+
+    passes = []
+    for d in (read_dir, write_dir):
+        rows = {}
+        for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    key = int(r["Dispatch_Id"])
+                    e = rows.setdefault(key, [_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size"]), {}])
+                    e[2][r["Counter_Name"]] = float(r["Counter_Value"])
+        passes.append([rows[k] for k in sorted(rows)])
+    rd, wr = passes
+    if [(n, g) for n, g, _ in rd] != [(n, g) for n, g, _ in wr]:
+        raise RuntimeError("the read and write counter passes saw different dispatch sequences")
+    return [(n, g, {**a, **b[2]}) for (n, g, a), b in zip(rd, wr)]
+
+
+def pmc_request_bytes(c: dict) -> tuple:
+    """(read bytes, write bytes, read requests unaccounted) of one dispatch:
+    reads 32 * RDREQ_32B + 64 * RDREQ_64B + 128 * RDREQ_128B, writes
+    64 * WRREQ_64B + 32 * (WRREQ - WRREQ_64B)."""
+    r32, r64, r128 = (c.get(f"TCC_EA0_RDREQ_{s}_sum", 0.0) for s in ("32B", "64B", "128B"))
+    rd = 32.0 * r32 + 64.0 * r64 + 128.0 * r128
+    w64 = c.get("TCC_EA0_WRREQ_64B_sum", 0.0)
+    wr = 64.0 * w64 + 32.0 * (c.get("TCC_EA0_WRREQ_sum", 0.0) - w64)
+    return rd, wr, c.get("TCC_EA0_RDREQ_sum", 0.0) - (r32 + r64 + r128)
+
+
+def pmc_bytes(read_dir: str, write_dir: str) -> dict:
+    """HBM bytes per dispatch per kernel (means) from the two passes:
+    {kernel: {"dispatches", "read_bytes", "write_bytes"}}; the copy probe's
+    sizes apart."""
+    acc = {}
+    for name, grid, c in _pmc_dispatches(read_dir, write_dir):
+        if name.startswith("copy_probe"):
+            name = f"{name}[{grid}]"
+        rd, wr, _ = pmc_request_bytes(c)
+        a = acc.setdefault(name, [0, 0.0, 0.0])
+        a[0] += 1
+        a[1] += rd
+        a[2] += wr
+    return {n: {"dispatches": a[0], "read_bytes": a[1] / a[0], "write_bytes": a[2] / a[0]} for n, a in acc.items()}
+
+
+def _call_of_kernel(name: str, route_call: str):
+    if name.startswith("swiglu_kernel"):
+        return "swiglu"
+    if name.startswith("combine_kernel"):
+        return "combine"
+    if name.startswith(("route_", "place_expand_kernel", "expand_")):
+        return route_call
+    return None
+
+
+def traffic_report(read_dir: str, write_dir: str, cfg, pad_to=1, fp8_group=0, mxfp8=False, cmds=()) -> str:
+    """Markdown summary of the two counter passes of a bench.py run: the copy
+    probe's measured bytes against the 2 GiB it moves, then each call of
+    the step (all the kernels it launches) against its algorithmic bytes,
+    with the machine-readable block measured_traffic reads."""
+    disp = _pmc_dispatches(read_dir, write_dir)
+    route_call = ("route_expand_mxfp8" if mxfp8 else "route_expand_fp8" if fp8_group
+                  else "route_expand" if pad_to == 1 else "route_expand_padded")
+    ab = algorithmic_bytes(cfg, fp8_group)
+    probe = [pmc_request_bytes(c) for n, g, c in disp if n.startswith("copy_probe") and g == COPY_PROBE_LANES]
+    steps = sum(1 for n, _, _ in disp if n.startswith("swiglu_kernel"))
+    per_kernel, per_call = {}, {}
+    for n, _, c in disp:
+        call = _call_of_kernel(n, route_call)
+        if call is None:
+            continue
+        rd, wr, miss = pmc_request_bytes(c)
+        k = per_kernel.setdefault((call, n), [0, 0.0, 0.0, 0.0])
+        k[0] += 1
+        k[1] += rd
+        k[2] += wr
+        k[3] += miss
+        per_call[call] = per_call.get(call, 0.0) + rd + wr
+    gib = float(1 << 30)
+    lines = [f"Copy probe check (1 GiB read + 1 GiB write per dispatch, {len(probe)} dispatches): "
+             + ", ".join(f"read {r / gib:.5f} GiB, write {w / gib:.5f} GiB" for r, w, _ in probe[:1])
+             + (f"; unaccounted read requests {probe[0][2]:.0f}" if probe else ""), "",
+             "| call | kernel | dispatches | read bytes | write bytes | HBM bytes per step | algorithmic bytes | ratio |",
+             "|---|---|---|---|---|---|---|---|"]
+    js = {"workload": cfg.name, "pad_to": pad_to, "fp8_group": fp8_group, "mxfp8": mxfp8, "steps": steps,
+          "kernels": {}}
+    for call in (route_call, "swiglu", "combine"):
+        for (cl, n), k in sorted(per_kernel.items()):
+            if cl == call:
+                lines.append(f"| {call} | `{n}` | {k[0]} | {k[1] / k[0]:.0f} | {k[2] / k[0]:.0f} | "
+                             f"{(k[1] + k[2]) / max(steps, 1):.0f} | | |")
+        tot = per_call.get(call, 0.0) / max(steps, 1)
+        lines.append(f"| **{call}** | (sum) | | | | {tot:.0f} | {ab[call]} | {tot / ab[call]:.4f} |")
+        js["kernels"][call] = {"traffic_bytes": int(round(tot)), "source_digest": source_digest(call)}
+    head = "\n".join(f"    {c}" for c in cmds)
+    return ("Commands (rocprofv3 from /tmp with TMPDIR=/tmp; `<repo>` is the repository root):\n\n" + head + "\n\n"
+            if cmds else "") + "\n".join(lines) + ("\n\nMachine-readable copy (bench.py reads `traffic_bytes` while "
+                                                "the call's source digest matches):\n\n```json\n"
+                                                + json.dumps(js, indent=1) + "\n```\n")
 
 
 def main(argv=None):
@@ -410,7 +595,33 @@ def main(argv=None):
                     help="skip the HIP-graph replay timing (ms_per_step_graph)")
     ap.add_argument("--events", choices=["nofence", "torch", "none"], default="nofence",
                     help="per-call HIP events inside the timed region (default: without the system fence)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of CPU work per CPU-baseline leg")
+    ap.add_argument("--cpu-leg", choices=["single", "all"], help=argparse.SUPPRESS)
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="print per-kernel medians from a rocprofv3 kernel-trace CSV, skipping --warmup "
+                         "dispatches of each kernel, and exit")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("READ_DIR", "WRITE_DIR"),
+                    help="print HBM bytes per dispatch per kernel from two rocprofv3 --pmc output folders "
+                         "(PMC_READ counters, then PMC_WRITE) as JSON, and exit")
+    ap.add_argument("--traffic-report", nargs=2, metavar=("READ_DIR", "WRITE_DIR"),
+                    help="print the per-call HBM traffic of a bench run with the same --config/--pad/--fp8-group/"
+                         "--mxfp8 from its two rocprofv3 --pmc output folders (markdown), and exit")
     args = ap.parse_args(argv)
+
+    if args.cpu_leg:
+        print(json.dumps(_cpu_leg(args.config, args.seed, args.cpu_leg, args.cpu_budget)), flush=True)
+        return 0
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.warmup))
+        return 0
+    if args.summarize_pmc:
+        print(json.dumps(pmc_bytes(*args.summarize_pmc), indent=1))
+        return 0
+    if args.traffic_report:
+        from moe_glue_amd import inputs as I
+
+        print(traffic_report(*args.traffic_report, I.CONFIGS[args.config], args.pad, args.fp8_group, args.mxfp8))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py: the MoE glue path runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -472,6 +683,7 @@ def main(argv=None):
     graph_ms = graph_ms_per_step(sets, dev, args.steps) if args.graph else None
 
     ab = algorithmic_bytes(cfg, args.fp8_group)
+    variant = variant_name(cfg.name, args.pad, args.fp8_group, args.mxfp8)
     kernels = {}
     if use_events:
         for i, n in enumerate(names):
@@ -481,17 +693,23 @@ def main(argv=None):
             kernels[n] = {"us": round(us, 3), "bytes": ab[n], "GBps": round(gbps, 1),
                           "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
                           "frac_of_achievable": round(gbps / achievable, 4),
-                          "traffic": measured_traffic(n, cfg.name)}
+                          "traffic": measured_traffic(n, variant)}
     # the roofline kernel: the longest call that is a single kernel (route and
     # route_expand launch several)
     single = [n for n in names if n not in ("route", "route_expand", "route_expand_padded", "route_expand_fp8",
                                             "route_expand_mxfp8")]
     dominant = max(single, key=lambda n: kernels[n]["us"]) if kernels else None
     roofline = None
+    slowest = None
     if kernels:
         d = kernels[dominant]
         roofline = {"kernel": dominant, "bound": "hbm", "achieved": d["GBps"], "peak": HBM_PEAK_GBPS,
-                    "unit": "GB/s", "frac": d["frac_of_peak"], "traffic": measured_traffic(dominant, cfg.name)}
+                    "unit": "GB/s", "frac": d["frac_of_peak"], "traffic": measured_traffic(dominant, variant)}
+        # the call furthest below the copy probe, whatever its kernel count
+        worst = min(names, key=lambda n: kernels[n]["frac_of_achievable"])
+        w = kernels[worst]
+        slowest = {"call": worst, "us": w["us"], "GBps": w["GBps"], "frac_of_peak": w["frac_of_peak"],
+                   "frac_of_achievable": w["frac_of_achievable"]}
 
     ms_per_step = 1e3 * elapsed / args.steps
     rec = {
@@ -519,10 +737,12 @@ def main(argv=None):
         "ms_per_step_graph": graph_ms,
         "kernels": kernels,
         "roofline": roofline,
+        "slowest_call": slowest,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(inp)
+        del sets
+        rec["cpu_baseline"] = cpu_baseline(cfg, args.seed, args.cpu_budget)
     print(json.dumps(rec), flush=True)
     return 0
 
