@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kPeThreads) __attribute__((amdgpu_waves_per_eu(8, 8
     const int32_t* __restrict__ topk_ids, RowGroups groups, int ls, int lrc, uint32_t H16, FastDiv div_h16,
     const u32x4* __restrict__ x, u32x4* __restrict__ x_exp, int32_t* __restrict__ dest_of_src,
     int32_t* __restrict__ src_of_dest, int32_t* __restrict__ expert_offsets, int32_t* __restrict__ expert_counts) {
-    __shared__ uint32_t part[2][kPeWaves][QP][8];
+    __shared__ uint32_t part[2][QP][8];  // column sums, two 16-bit halves per word
     __shared__ unsigned long long masks[kPeMaskWords];
     __shared__ uint16_t pc[kPeMaskWords];  // exclusive popcount prefix of each expert's bitmap words
     __shared__ int32_t s_tot[kEMax];
@@ -103,6 +103,11 @@ __global__ __launch_bounds__(kPeThreads) __attribute__((amdgpu_waves_per_eu(8, 8
     const int last_slot = T * k - 1;
 #pragma unroll
     for (int u = 0; u < kPeSlots; ++u) my_e[u] = topk_ids[min(gt0 * k + tid + u * kPeThreads, last_slot)];
+    for (int i = tid; i < E * W; i += kPeThreads) masks[i] = 0ull;
+    for (int e = tid; e < E; e += kPeThreads) s_gcnt[e] = 0;
+    for (int i = tid; i < 2 * QP * 8; i += kPeThreads) (&part[0][0][0])[i] = 0u;
+    __syncthreads();  // bitmaps, counts and sums clear (the loads above are in flight; the
+                      // source touches below would hold this barrier up while they queue)
     const uint32_t src_n = (uint32_t)ntok * H16;
     const uint32_t per = (src_n + S - 1) >> ls;
     const uint32_t pf0 = c * per;
@@ -115,7 +120,6 @@ __global__ __launch_bounds__(kPeThreads) __attribute__((amdgpu_waves_per_eu(8, 8
         const uint32_t j = min(pf0 + (uint32_t)(tid + p * kPeThreads), pf1 > 0 ? pf1 - 1 : 0u);
         warm[p] = xw[(size_t)min((uint32_t)gt0 * H16 + j, last_vec) * 4];  // one dword brings in the line
     }
-    for (int i = tid; i < E * W; i += kPeThreads) masks[i] = 0ull;
 
     // 2. Column sums of the count bytes: [0] every row (the expert totals),
     // [1] the rows before the group (its first row in each expert's
@@ -146,48 +150,52 @@ __global__ __launch_bounds__(kPeThreads) __attribute__((amdgpu_waves_per_eu(8, 8
         for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[a][j] = add_lanes<QP>(acc[a][j]);
-        if (tid % kWave < QP) {
+        if (tid % kWave < QP) {  // the wave's sums into the workgroup's (halves stay below 2^16)
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) part[a][tid / kWave][q][j] = acc[a][j];
+                for (int j = 0; j < 8; ++j) atomicAdd(&part[a][q][j], acc[a][j]);
         }
     }
-    __syncthreads();  // part written; masks cleared
-    for (int i = tid; i < 2 * QP * 8; i += kPeThreads) {
-        const int a = i / (QP * 8);
-        const int qq = (i / 8) % QP;
-        const int j = i % 8;
-        uint32_t sum = 0;
-        for (int v = 0; v < sum_waves; ++v) sum += part[a][v][qq][j];
-        const int e = qq * 16 + (j / 2) * 4 + (j % 2);  // bytes 0/1 of word j/2; +2 for bytes 2/3
-        int32_t* dst = a == 0 ? s_tot : s_base;
-        if (e < E) dst[e] = (int32_t)(sum & 0xFFFFu);
-        if (e + 2 < E) dst[e + 2] = (int32_t)(sum >> 16);
-    }
-    // 3. The group's per-expert token bitmaps.
+    // 3. The group's per-expert token bitmaps and counts.
 #pragma unroll
     for (int u = 0; u < kPeSlots; ++u) {
         const int s = tid + u * kPeThreads;
         if (s < nslot) {
             const int tl = (int)fastdiv((uint32_t)s, div_k);
             atomicOr(&masks[my_e[u] * W + (tl >> 6)], 1ull << (tl & 63));
+            atomicAdd(&s_gcnt[my_e[u]], 1);
         }
     }
-    __syncthreads();
-    // 4. Per bitmap word: the popcount of the expert's words before it; per
-    // expert: the group's count.
-    for (int i = tid; i < E * W; i += kPeThreads) {
-        const int e = i / W;
-        const int w = i - e * W;
-        int run = 0;
-        for (int w2 = 0; w2 < w; ++w2) run += __popcll(masks[e * W + w2]);
-        pc[i] = (uint16_t)run;
-        if (w == W - 1) s_gcnt[e] = run + __popcll(masks[i]);
+    __syncthreads();  // sums, bitmaps and group counts complete
+    // 4. Side by side: wave 0 the expert totals and their (padded) offsets,
+    // wave 1 the group's first rows and its destination order, the other
+    // waves each bitmap word's popcount prefix inside its expert.  A wave
+    // reads back what its own lanes wrote just before (LDS accesses of one
+    // wave complete in order), so no barrier sits in between.
+    const int wave = tid / kWave;
+    if (wave < 2) {
+        int32_t* dst = wave == 0 ? s_tot : s_base;
+        for (int i = tid % kWave; i < QP * 8; i += kWave) {
+            const int qq = i / 8;
+            const int j = i % 8;
+            const uint32_t sum = part[wave][qq][j];
+            const int e = qq * 16 + (j / 2) * 4 + (j % 2);  // bytes 0/1 of word j/2; +2 for bytes 2/3
+            if (e < E) dst[e] = (int32_t)(sum & 0xFFFFu);
+            if (e + 2 < E) dst[e + 2] = (int32_t)(sum >> 16);
+        }
+        asm volatile("" ::: "memory");  // keep the scans' reads after these writes
+        wave_exclusive_scan(s_tot, s_off, E, pad, 0);  // expert offsets (padded segments)
+        wave_exclusive_scan(s_gcnt, s_gcum, E, 1, 1);  // the group's destination order
+    } else {
+        for (int i = tid - 2 * kWave; i < E * W; i += kPeThreads - 2 * kWave) {
+            const int e = i / W;
+            const int w = i - e * W;
+            int run = 0;
+            for (int w2 = 0; w2 < w; ++w2) run += __popcll(masks[e * W + w2]);
+            pc[i] = (uint16_t)run;
+        }
     }
-    __syncthreads();
-    wave_exclusive_scan(s_tot, s_off, E, pad, 0);   // expert offsets (padded segments)
-    wave_exclusive_scan(s_gcnt, s_gcum, E, 1, 1);   // the group's destination order
     __syncthreads();
     if (blockIdx.x == 0) {
         for (int e = tid; e <= E; e += kPeThreads) expert_offsets[e] = s_off[e];
