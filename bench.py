@@ -279,26 +279,75 @@ def default_sets(cfg, pad_to=1, fp8_group=0) -> int:
     return max(4, min(want, MAX_SETS, fit))
 
 
-def copy_probe_gbps(dev, nbytes=1 << 30, reps=5):
+def rw_bytes(cfg, fp8_group: int = 0) -> dict:
+    """Algorithmic bytes of each call split into (read, write)."""
+    T, H, E, k, I, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.R
+    route = (T * E * 4 + (E * 4 if cfg.bias_std > 0 else 0), R * 4 * 4 + (E + 1) * 4 + E * 4)
+    expand = (T * H * 2 + R * 4, R * H * 2)
+    expand_fp8 = (T * H * 2 + R * 4, R * H + (R * (H // fp8_group) * 4 if fp8_group else 0))
+    expand_mx = (T * H * 2 + R * 4, R * H + R * (H // 32))
+    add = lambda a, b: (a[0] + b[0], a[1] + b[1])  # noqa: E731
+    return {"route_expand": add(route, expand), "route_expand_padded": add(route, expand),
+            "route_expand_fp8": add(route, expand_fp8), "route_expand_mxfp8": add(route, expand_mx),
+            "swiglu": (R * 2 * I * 2, R * I * 2), "combine": (R * H * 2 + R * 8, T * H * 2)}
+
+
+def mix_of(read: int, write: int) -> tuple:
+    """Small whole numbers of reads and writes per lane with about the same ratio."""
+    if read >= write:
+        return (max(1, min(64, round(read / max(write, 1)))), 1)
+    return (1, max(1, min(64, round(write / max(read, 1)))))
+
+
+def _timed_launches(dev, launch, copies: int, reps: int) -> float:
+    """Median device time (s) of `reps` launches, launch(i) on copy i % copies,
+    each between HIP events without the system fence (as the path's calls)."""
+    import torch
+
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    for i in range(min(copies, 4)):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(HipEvent(stream), HipEvent(stream)) for _ in range(reps)]
+    for i, (e0, e1) in enumerate(ev):
+        e0.record()
+        launch(i % copies)
+        e1.record()
+    torch.cuda.synchronize()
+    times = sorted(e0.elapsed_time(e1) * 1e-3 for e0, e1 in ev)
+    return times[len(times) // 2]
+
+
+def copy_probe_gbps(dev, nbytes=1 << 30, reps=9):
     """Achievable HBM bandwidth: the library's 16 B/lane copy over 1 GiB."""
     import torch
     import moe_glue_amd as mg
 
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    mg.copy_probe(src, dst)
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        mg.copy_probe(src, dst)
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) * 1e-3)
+    t = _timed_launches(dev, lambda i: mg.copy_probe(src, dst), 1, reps)
     del src, dst
-    t = sorted(times)[len(times) // 2]
     return 2 * nbytes / t / 1e9, t
+
+
+def mix_probe_gbps(dev, reads: int, writes: int, nbytes=1 << 30, reps=5):
+    """HBM bandwidth of a plain stream with `reads` reads per `writes` writes
+    (moe_mix_probe over about nbytes in all, at least one wave), timed as the
+    path's calls are.  Below twice the Infinity Cache the launches rotate over
+    copies of the buffers, as the path's calls rotate over input sets, so the
+    reads come from HBM there too."""
+    import torch
+    import moe_glue_amd as mg
+
+    lanes = max(64, (nbytes // (16 * (reads + writes))) // 64 * 64)
+    rb, wb = lanes * reads * 16, lanes * writes * 16
+    copies = max(1, min(MAX_SETS, -(-2 * INFINITY_CACHE_BYTES // max(1, rb + wb))))
+    src = torch.empty(max(1, copies * rb), dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(max(1, copies * wb), dtype=torch.uint8, device=dev)
+    t = _timed_launches(dev, lambda i: mg.mix_probe(src[i * rb:] if reads else src, dst[i * wb:] if writes else dst,
+                                                     lanes, reads, writes), copies, max(reps, min(copies, 64)))
+    del src, dst
+    return lanes * 16 * (reads + writes) / t / 1e9
 
 
 def launch_floor_us(dev, n=100):
@@ -685,14 +734,23 @@ def main(argv=None):
     ab = algorithmic_bytes(cfg, args.fp8_group)
     variant = variant_name(cfg.name, args.pad, args.fp8_group, args.mxfp8)
     kernels = {}
+    mix_gbps = {}
     if use_events:
         for i, n in enumerate(names):
             ms = [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]
             us = 1e3 * sum(ms) / len(ms)
             gbps = ab[n] / (us * 1e-6) / 1e9
+            rd, wr = rw_bytes(cfg, args.fp8_group)[n]
+            mix = mix_of(rd, wr)
+            if mix not in mix_gbps:
+                mix_gbps[mix] = mix_probe_gbps(dev, *mix)
+            same = mix_probe_gbps(dev, *mix, nbytes=ab[n], reps=21)  # the same bytes, one plain launch
             kernels[n] = {"us": round(us, 3), "bytes": ab[n], "GBps": round(gbps, 1),
                           "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
                           "frac_of_achievable": round(gbps / achievable, 4),
+                          "mix": {"reads": mix[0], "writes": mix[1], "probe_GBps": round(mix_gbps[mix], 1),
+                                  "frac": round(gbps / mix_gbps[mix], 4), "same_bytes_GBps": round(same, 1),
+                                  "frac_same_bytes": round(gbps / same, 4)},
                           "traffic": measured_traffic(n, variant)}
     # the roofline kernel: the longest call that is a single kernel (route and
     # route_expand launch several)

@@ -317,6 +317,18 @@ moe_status moe_combine(const uint16_t* y, const float* topk_weights, const int32
  * part of the MoE path.  Errors: MOE_ERR_NULL, MOE_ERR_ALIGN, MOE_ERR_HIP. */
 moe_status moe_copy_probe(const void* src, void* dst, size_t bytes, void* stream);
 
+/* Streaming probe with a read:write mix: `lanes` lanes (a multiple of 64 is
+ * expected) each read `reads` and write `writes` 16-byte vectors, every
+ * access of a 64-lane wave one contiguous KiB; src must hold lanes * reads
+ * vectors and dst lanes * writes (device pointers, 16-byte aligned, owned
+ * by the caller; either may be NULL when its count is 0).  It measures what
+ * HBM gives a plain stream with the same mix of reads and writes as a path
+ * kernel; it is not part of the MoE path.  reads, writes <= 64, lanes <=
+ * 2^30; lanes = 0 or reads = writes = 0 is a no-op.  Errors: MOE_ERR_NULL,
+ * MOE_ERR_ALIGN, MOE_ERR_SHAPE, MOE_ERR_HIP. */
+moe_status moe_mix_probe(const void* src, void* dst, uint32_t lanes, uint32_t reads, uint32_t writes,
+                         void* stream);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status s);
 

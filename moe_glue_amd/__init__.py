@@ -29,7 +29,7 @@ from ._binding import (E_MAX, EXPORTED, K_MAX, LIB_PATH, MoEGlueArgumentError, M
 __all__ = ["route", "route_workspace_bytes", "alloc_route_outputs", "route_padded", "padded_rows", "expand_rows",
            "expand_rows_fp8", "expand_rows_mxfp8",
            "route_expand", "route_expand_noalloc", "noalloc_scratch_bytes", "route_expand_padded", "route_expand_fp8", "route_expand_mxfp8", "swiglu", "combine",
-           "copy_probe", "MoEGlueError", "MoEGlueArgumentError", "E_MAX", "K_MAX"]
+           "copy_probe", "mix_probe", "MoEGlueError", "MoEGlueArgumentError", "E_MAX", "K_MAX"]
 
 
 def _torch():
@@ -444,3 +444,19 @@ def copy_probe(src, dst) -> None:
     if dst.numel() * dst.element_size() < nbytes:
         raise MoEGlueArgumentError(2, "dst is smaller than src")
     check(load().moe_copy_probe(_ptr(src), _ptr(dst), nbytes, _stream(src.device)), "moe_copy_probe")
+
+
+def mix_probe(src, dst, lanes: int, reads: int, writes: int) -> None:
+    """Streaming probe: `lanes` lanes each read `reads` and write `writes`
+    16-byte vectors (the bandwidth of that read:write mix)."""
+    if reads > 0:
+        _need_gpu("src", src)
+        if src.numel() * src.element_size() < lanes * reads * 16:
+            raise MoEGlueArgumentError(1, "src is smaller than lanes * reads vectors")
+    if writes > 0:
+        _need_gpu("dst", dst)
+        if dst.numel() * dst.element_size() < lanes * writes * 16:
+            raise MoEGlueArgumentError(2, "dst is smaller than lanes * writes vectors")
+    dev = (src if reads > 0 else dst).device
+    check(load().moe_mix_probe(_ptr(src) if reads > 0 else None, _ptr(dst) if writes > 0 else None, lanes, reads,
+                               writes, _stream(dev)), "moe_mix_probe")

@@ -21,7 +21,7 @@ PAD_MAX = 4096
 EXPORTED = ("moe_route_workspace_bytes", "moe_route", "moe_route_padded_rows", "moe_route_padded",
             "moe_expand_rows", "moe_expand_rows_fp8", "moe_expand_rows_mxfp8", "moe_route_expand", "moe_route_expand_padded",
             "moe_route_expand_fp8", "moe_route_expand_mxfp8", "moe_noalloc_scratch_bytes", "moe_route_expand_noalloc",
-            "moe_swiglu", "moe_combine", "moe_copy_probe",
+            "moe_swiglu", "moe_combine", "moe_copy_probe", "moe_mix_probe",
             "moe_status_string", "moe_last_error")
 # include/moe_glue_testing.h
 TESTING_EXPORTED = ("moe_testing_force",)
@@ -99,6 +99,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_combine.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]
     lib.moe_copy_probe.restype = ctypes.c_int
     lib.moe_copy_probe.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+    lib.moe_mix_probe.restype = ctypes.c_int
+    lib.moe_mix_probe.argtypes = [_vp, _vp, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, _vp]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_last_error.restype = ctypes.c_char_p

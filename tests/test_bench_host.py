@@ -125,3 +125,17 @@ def test_variant_names():
     assert bench.variant_name("qwen3_30b_a3b") == "qwen3_30b_a3b"
     assert bench.variant_name("qwen3_30b_a3b", 128, 128) == "qwen3_30b_a3b_pad128_fp8g128"
     assert bench.variant_name("qwen3_30b_a3b", mxfp8=True) == "qwen3_30b_a3b_mxfp8"
+
+
+def test_read_write_split_matches_the_totals():
+    for name in inputs.CONFIG_ORDER:
+        cfg = inputs.CONFIGS[name]
+        for g in (0, 128):
+            ab = bench.algorithmic_bytes(cfg, g)
+            for call, (rd, wr) in bench.rw_bytes(cfg, g).items():
+                if call == "route_expand_fp8" and not g:
+                    continue
+                assert rd + wr == ab[call], (name, g, call)
+    assert bench.mix_of(8 * 10, 10) == (8, 1)
+    assert bench.mix_of(10, 79) == (1, 8)
+    assert bench.mix_of(2, 1) == (2, 1)
