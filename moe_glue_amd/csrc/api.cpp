@@ -79,34 +79,46 @@ constexpr int64_t kQuantisingFoldMaxBytes = 20ll << 20;  // E4M3 codes of moe_ro
 
 int forced_order() { return g_force_order.load(std::memory_order_relaxed); }
 
-// Placed runs every workgroup of the grid at once, each XCD on two token
-// groups, so it pays while their source rows stay within the XCDs' L2 and the
-// histogram each workgroup sums stays small.  Measured per moe_route_expand
-// call against the row-list order (T x H, E, k; x from HBM): 3072 x 2048 -1.4,
-// 4096 x 2048 (the Qwen3-30B-A3B shape) -0.9, 4096 x 4096 (64, 6) -2.6,
-// 6144 x 2048 -1.9, 4096 x 3072 +1.0, 8192 x 2048 +1.9, 8192 x 7168 (256, 8)
-// +38 us.
+// Placed runs every workgroup of the grid at once, each XCD on one or two
+// token groups, so it pays while their source rows stay within the XCDs' L2
+// and the histogram each workgroup sums stays small.  Measured per
+// moe_route_expand call against the row-list order (T x H, E, k; x from
+// HBM): 3072 x 2048 -1.4, 4096 x 2048 (the Qwen3-30B-A3B shape) -0.9,
+// 4096 x 4096 (64, 6) -2.6, 6144 x 2048 -1.9, 4096 x 3072 +1.0, 8192 x 2048
+// +1.9, 8192 x 7168 (256, 8) +38 us; and against the copy in the place launch
+// (Fused): 768 x 4096 (64, 6) +0.3, 1023 x 4096 (64, 6) -1.6, 1024 x 2048
+// -0.5, 2048 x 2048 -2.2, 1024 x 7168 (256, 8) -1.8, 2048 x 7168 (256, 8)
+// -2.4 us.  Up to 24576 expanded rows 64 workgroups per group (one group per
+// XCD) beat 32 by 0.1-0.6 us; at 32768 rows (Qwen3-30B-A3B) 32 beat 64 by 1.2.
 constexpr int kPlacedMaxTokens = 6144;
 constexpr int64_t kPlacedMaxSourceBytes = 32ll << 20;
+constexpr int64_t kPlacedMinRows = 5120;
+constexpr int64_t kPlacedWideGroupMaxRows = 24576;
 
 ExpandOrder expand_order(int32_t T, int32_t E, int32_t k, int32_t H, moe::RouteVariant v,
                          moe::PlaceExpandShape* shape) {
     const bool two = v == moe::RouteVariant::TwoPass;
     if (v == moe::RouteVariant::SingleWorkgroup || T == 0) return ExpandOrder::Token;
+    const int64_t rows = (int64_t)T * k;
+    // without Placed: token order below the grouped expand's size, else grouped
+    const ExpandOrder other = rows < kGroupedExpandMinRows ? (two ? ExpandOrder::Fused : ExpandOrder::Token)
+                                                           : ExpandOrder::Grouped;
     switch (forced_order()) {
         case 1: return ExpandOrder::Token;
         case 2: return two ? ExpandOrder::Fused : ExpandOrder::Token;
         case 3: return ExpandOrder::Grouped;
         case 4: break;
         default:
-            if ((int64_t)T * k < kGroupedExpandMinRows) return two ? ExpandOrder::Fused : ExpandOrder::Token;
-            if (T > kPlacedMaxTokens || (int64_t)T * H * 2 > kPlacedMaxSourceBytes) return ExpandOrder::Grouped;
+            if (rows < kPlacedMinRows || T > kPlacedMaxTokens || (int64_t)T * H * 2 > kPlacedMaxSourceBytes)
+                return other;
     }
     if (two) {
-        *shape = moe::place_expand_shape(T, E, k, H, g_force_wpg.load(std::memory_order_relaxed));
+        int wpg = g_force_wpg.load(std::memory_order_relaxed);
+        if (wpg == 0) wpg = rows <= kPlacedWideGroupMaxRows ? 64 : 32;
+        *shape = moe::place_expand_shape(T, E, k, H, wpg);
         if (shape->ok) return ExpandOrder::Placed;
     }
-    return ExpandOrder::Grouped;
+    return forced_order() == 4 ? ExpandOrder::Grouped : other;
 }
 
 moe_status check_route_sizes(int32_t T, int32_t E, int32_t k) {
@@ -544,6 +556,17 @@ moe_status moe_copy_probe(const void* src, void* dst, size_t bytes, void* stream
     if (bytes % 16 != 0 || !aligned16(src) || !aligned16(dst))
         return fail(MOE_ERR_ALIGN, "moe_copy_probe: size and pointers must be multiples of 16 bytes");
     return from_hip(moe::launch_copy_probe(src, dst, bytes, static_cast<hipStream_t>(stream)), "moe_copy_probe launch");
+}
+
+moe_status moe_mix_probe(const void* src, void* dst, uint32_t lanes, uint32_t reads, uint32_t writes,
+                         void* stream) {
+    if (lanes == 0 || (reads == 0 && writes == 0)) return ok();
+    if ((reads > 0 && !src) || (writes > 0 && !dst)) return fail(MOE_ERR_NULL, "moe_mix_probe: NULL pointer");
+    if (!aligned16(src) || !aligned16(dst)) return fail(MOE_ERR_ALIGN, "moe_mix_probe: pointers must be 16-byte aligned");
+    if (reads > 64 || writes > 64 || lanes > (1u << 30))
+        return fail(MOE_ERR_SHAPE, "moe_mix_probe: at most 64 reads and 64 writes per lane and 2^30 lanes");
+    return from_hip(moe::launch_mix_probe(src, dst, lanes, reads, writes, static_cast<hipStream_t>(stream)),
+                    "moe_mix_probe launch");
 }
 
 }  // extern "C"

@@ -6,9 +6,10 @@ integer or bit work, the weights come from the same instructions).
 
 Calls run back to back on one stream, each one smaller than the one before,
 so each call finds the scratch holding what the previous, larger call left:
-the grouped destination-order path (T*k >= 24576 rows), the two-launch route
-with the copy in its place launch, the three-launch route (a histogram matrix
-too large for the two-launch form), then the one-launch dispatch (T <= 64)."""
+the placing destination-order expand (its chunk claims and count rows in the
+scratch), the three-launch route (a histogram matrix too large for the
+two-launch form), the two-launch route with the copy in its place launch,
+then the one-launch dispatch (T <= 64)."""
 import sys
 
 import numpy as np
