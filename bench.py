@@ -330,24 +330,32 @@ def copy_probe_gbps(dev, nbytes=1 << 30, reps=9):
     return 2 * nbytes / t / 1e9, t
 
 
+MIX_PROBE_SHAPES = ((256, 1), (256, 2), (256, 4), (1024, 1), (1024, 2))  # (lanes per workgroup, KiB per wave)
+
+
 def mix_probe_gbps(dev, reads: int, writes: int, nbytes=1 << 30, reps=5):
-    """HBM bandwidth of a plain stream with `reads` reads per `writes` writes
-    (moe_mix_probe over about nbytes in all, at least one wave), timed as the
-    path's calls are.  Below twice the Infinity Cache the launches rotate over
-    copies of the buffers, as the path's calls rotate over input sets, so the
-    reads come from HBM there too."""
+    """HBM bandwidth of a plain stream with `reads` read waves per `writes`
+    write waves (moe_mix_probe, about nbytes in all, at least one cycle): the
+    best over MIX_PROBE_SHAPES, each timed as the path's calls are.  Below
+    twice the Infinity Cache the launches rotate over copies of the
+    buffers, as the path's calls rotate over input sets, so the reads come
+    from HBM there too."""
     import torch
     import moe_glue_amd as mg
 
-    lanes = max(64, (nbytes // (16 * (reads + writes))) // 64 * 64)
-    rb, wb = lanes * reads * 16, lanes * writes * 16
-    copies = max(1, min(MAX_SETS, -(-2 * INFINITY_CACHE_BYTES // max(1, rb + wb))))
-    src = torch.empty(max(1, copies * rb), dtype=torch.uint8, device=dev).fill_(1)
-    dst = torch.empty(max(1, copies * wb), dtype=torch.uint8, device=dev)
-    t = _timed_launches(dev, lambda i: mg.mix_probe(src[i * rb:] if reads else src, dst[i * wb:] if writes else dst,
-                                                     lanes, reads, writes), copies, max(reps, min(copies, 64)))
-    del src, dst
-    return lanes * 16 * (reads + writes) / t / 1e9
+    best = 0.0
+    for threads, vpl in MIX_PROBE_SHAPES:
+        kib = 1024 * vpl
+        cycles = max(1, nbytes // ((reads + writes) * kib))
+        rb, wb = cycles * reads * kib, max(cycles * writes * kib, 1024)
+        copies = max(1, min(MAX_SETS, -(-2 * INFINITY_CACHE_BYTES // (rb + wb))))
+        src = torch.empty(max(1, copies * rb), dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty(copies * wb, dtype=torch.uint8, device=dev)
+        t = _timed_launches(dev, lambda i: mg.mix_probe(src[i * rb:] if reads else src, dst[i * wb:], cycles, reads,
+                                                         writes, vpl, threads), copies, max(reps, min(copies, 64)))
+        del src, dst
+        best = max(best, cycles * (reads + writes) * kib / t / 1e9)
+    return best
 
 
 def launch_floor_us(dev, n=100):

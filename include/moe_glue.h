@@ -317,17 +317,20 @@ moe_status moe_combine(const uint16_t* y, const float* topk_weights, const int32
  * part of the MoE path.  Errors: MOE_ERR_NULL, MOE_ERR_ALIGN, MOE_ERR_HIP. */
 moe_status moe_copy_probe(const void* src, void* dst, size_t bytes, void* stream);
 
-/* Streaming probe with a read:write mix: `lanes` lanes (a multiple of 64 is
- * expected) each read `reads` and write `writes` 16-byte vectors, every
- * access of a 64-lane wave one contiguous KiB; src must hold lanes * reads
- * vectors and dst lanes * writes (device pointers, 16-byte aligned, owned
- * by the caller; either may be NULL when its count is 0).  It measures what
- * HBM gives a plain stream with the same mix of reads and writes as a path
- * kernel; it is not part of the MoE path.  reads, writes <= 64, lanes <=
- * 2^30; lanes = 0 or reads = writes = 0 is a no-op.  Errors: MOE_ERR_NULL,
- * MOE_ERR_ALIGN, MOE_ERR_SHAPE, MOE_ERR_HIP. */
-moe_status moe_mix_probe(const void* src, void* dst, uint32_t lanes, uint32_t reads, uint32_t writes,
-                         void* stream);
+/* Streaming probe with a read:write mix: `cycles` cycles of reads + writes
+ * waves (64 lanes each, `threads` lanes per workgroup: 64, 256 or 1024); in
+ * each cycle the first `reads` waves each load vectors_per_lane (1, 2 or 4)
+ * KiB of src and the others each store as many KiB to dst, every access of
+ * a wave one contiguous KiB, no store depending on a load.  src must hold
+ * cycles * reads * vectors_per_lane KiB and dst cycles * writes *
+ * vectors_per_lane KiB (+ 1 KiB when writes = 0); device pointers, 16-byte
+ * aligned, owned by the caller; src may be NULL when reads = 0, dst never.  It measures
+ * what HBM gives a stream with a path kernel's mix of reads and writes; it
+ * is not part of the MoE path.  reads, writes <= 64, cycles * (reads +
+ * writes) <= 2^24; cycles = 0 or reads = writes = 0 is a no-op.  Errors:
+ * MOE_ERR_NULL, MOE_ERR_ALIGN, MOE_ERR_SHAPE, MOE_ERR_HIP. */
+moe_status moe_mix_probe(const void* src, void* dst, uint32_t cycles, uint32_t reads, uint32_t writes,
+                         int32_t vectors_per_lane, int32_t threads, void* stream);
 
 /* Static text for a status code. */
 const char* moe_status_string(moe_status s);

@@ -446,17 +446,17 @@ def copy_probe(src, dst) -> None:
     check(load().moe_copy_probe(_ptr(src), _ptr(dst), nbytes, _stream(src.device)), "moe_copy_probe")
 
 
-def mix_probe(src, dst, lanes: int, reads: int, writes: int) -> None:
-    """Streaming probe: `lanes` lanes each read `reads` and write `writes`
-    16-byte vectors (the bandwidth of that read:write mix)."""
+def mix_probe(src, dst, cycles: int, reads: int, writes: int, vectors_per_lane: int = 1, threads: int = 256) -> None:
+    """Streaming probe: `cycles` cycles of `reads` reading and `writes`
+    writing waves, vectors_per_lane KiB each (the bandwidth of that
+    read:write mix)."""
+    kib = 1024 * vectors_per_lane
     if reads > 0:
         _need_gpu("src", src)
-        if src.numel() * src.element_size() < lanes * reads * 16:
-            raise MoEGlueArgumentError(1, "src is smaller than lanes * reads vectors")
-    if writes > 0:
-        _need_gpu("dst", dst)
-        if dst.numel() * dst.element_size() < lanes * writes * 16:
-            raise MoEGlueArgumentError(2, "dst is smaller than lanes * writes vectors")
-    dev = (src if reads > 0 else dst).device
-    check(load().moe_mix_probe(_ptr(src) if reads > 0 else None, _ptr(dst) if writes > 0 else None, lanes, reads,
-                               writes, _stream(dev)), "moe_mix_probe")
+        if src.numel() * src.element_size() < cycles * reads * kib:
+            raise MoEGlueArgumentError(1, "src is smaller than cycles * reads * vectors_per_lane KiB")
+    _need_gpu("dst", dst)
+    if dst.numel() * dst.element_size() < max(cycles * writes * kib, 1024):
+        raise MoEGlueArgumentError(2, "dst is smaller than cycles * writes * vectors_per_lane KiB (1 KiB at least)")
+    check(load().moe_mix_probe(_ptr(src) if reads > 0 else None, _ptr(dst), cycles, reads, writes, vectors_per_lane,
+                               threads, _stream(dst.device)), "moe_mix_probe")

@@ -100,7 +100,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_copy_probe.restype = ctypes.c_int
     lib.moe_copy_probe.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
     lib.moe_mix_probe.restype = ctypes.c_int
-    lib.moe_mix_probe.argtypes = [_vp, _vp, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, _vp]
+    lib.moe_mix_probe.argtypes = [_vp, _vp, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, _i32, _i32, _vp]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_last_error.restype = ctypes.c_char_p

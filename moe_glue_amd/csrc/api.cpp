@@ -558,14 +558,19 @@ moe_status moe_copy_probe(const void* src, void* dst, size_t bytes, void* stream
     return from_hip(moe::launch_copy_probe(src, dst, bytes, static_cast<hipStream_t>(stream)), "moe_copy_probe launch");
 }
 
-moe_status moe_mix_probe(const void* src, void* dst, uint32_t lanes, uint32_t reads, uint32_t writes,
-                         void* stream) {
-    if (lanes == 0 || (reads == 0 && writes == 0)) return ok();
-    if ((reads > 0 && !src) || (writes > 0 && !dst)) return fail(MOE_ERR_NULL, "moe_mix_probe: NULL pointer");
+moe_status moe_mix_probe(const void* src, void* dst, uint32_t cycles, uint32_t reads, uint32_t writes,
+                         int32_t vectors_per_lane, int32_t threads, void* stream) {
+    if (vectors_per_lane != 1 && vectors_per_lane != 2 && vectors_per_lane != 4)
+        return fail(MOE_ERR_SHAPE, "moe_mix_probe: vectors_per_lane=%d must be 1, 2 or 4", vectors_per_lane);
+    if (threads != 64 && threads != 256 && threads != 1024)
+        return fail(MOE_ERR_SHAPE, "moe_mix_probe: threads=%d must be 64, 256 or 1024", threads);
+    if (reads > 64 || writes > 64 || (uint64_t)cycles * (reads + writes) > (1u << 24))
+        return fail(MOE_ERR_SHAPE, "moe_mix_probe: at most 64 reads and 64 writes per cycle and 2^24 waves");
+    if (cycles == 0 || (reads == 0 && writes == 0)) return ok();
+    if ((reads > 0 && !src) || !dst) return fail(MOE_ERR_NULL, "moe_mix_probe: NULL pointer");
     if (!aligned16(src) || !aligned16(dst)) return fail(MOE_ERR_ALIGN, "moe_mix_probe: pointers must be 16-byte aligned");
-    if (reads > 64 || writes > 64 || lanes > (1u << 30))
-        return fail(MOE_ERR_SHAPE, "moe_mix_probe: at most 64 reads and 64 writes per lane and 2^30 lanes");
-    return from_hip(moe::launch_mix_probe(src, dst, lanes, reads, writes, static_cast<hipStream_t>(stream)),
+    return from_hip(moe::launch_mix_probe(src, dst, cycles, reads, writes, vectors_per_lane, threads,
+                                          static_cast<hipStream_t>(stream)),
                     "moe_mix_probe launch");
 }
 

@@ -199,8 +199,8 @@ hipError_t launch_swiglu(const void* h, int R, int I, void* act, hipStream_t str
 hipError_t launch_combine(const void* y, const float* topk_weights, const int32_t* dest_of_src, int T, int H,
                           int k, void* out, hipStream_t stream);
 hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t stream);
-hipError_t launch_mix_probe(const void* src, void* dst, uint32_t lanes, uint32_t reads, uint32_t writes,
-                            hipStream_t stream);
+hipError_t launch_mix_probe(const void* src, void* dst, uint32_t cycles, uint32_t reads, uint32_t writes,
+                            int vectors_per_lane, int threads, hipStream_t stream);
 
 // ------------------------------------------------------- built-in scratch
 // Bytes of the file-scope device array behind moe_route_expand_noalloc.

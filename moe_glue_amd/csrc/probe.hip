@@ -28,36 +28,58 @@ __global__ __launch_bounds__(kThreads) void copy_probe_kernel(const u32x4* __res
     }
 }
 
-// Streams with a given read:write mix: lane i of wave w reads `reads`
-// vectors of its wave's block of src and writes `writes` vectors (all built
-// from what it read) to its block of dst, every access of a wave one
-// contiguous 1 KiB.  No kernel of the path is this plain; it tells what
-// HBM gives a stream with a path kernel's mix of reads and writes.
-__global__ __launch_bounds__(kThreads) void mix_probe_kernel(const u32x4* __restrict__ src,
-                                                             u32x4* __restrict__ dst, uint32_t lanes,
-                                                             uint32_t reads, uint32_t writes) {
-    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
-    if (i >= lanes) return;
-    const size_t block = (size_t)(i / kThreads) * kThreads;
-    const uint32_t l = i % kThreads;
-    u32x4 acc = {0u, 0u, 0u, 0u};
-#pragma unroll 8
-    for (uint32_t r = 0; r < reads; ++r) acc ^= load_stream(src + block * reads + (size_t)r * kThreads + l);
-#pragma unroll 8
-    for (uint32_t w = 0; w < writes; ++w) {
-        u32x4 v = acc;
-        v[0] += w;
-        store_stream(dst + block * writes + (size_t)w * kThreads + l, v);
+// Streams with a given read:write mix, as independent read and write waves:
+// in each cycle of reads + writes waves the first `reads` each load U KiB of
+// src (U vectors per lane, every access of a wave one contiguous KiB) and the
+// others each store U KiB to dst.  Nothing a wave writes depends on a read,
+// so the figure is what HBM gives that mix, not the latency of a kernel's
+// load-then-store chain.  The loaded values only feed a store that never
+// happens (it keeps the loads).
+template <int TH, int U>
+__global__ __launch_bounds__(TH) void mix_probe_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                       uint32_t waves, uint32_t reads, uint32_t writes) {
+    const uint32_t g = blockIdx.x * (TH / kThreads) + threadIdx.x / kThreads;
+    if (g >= waves) return;
+    const uint32_t l = threadIdx.x % kThreads;
+    const uint32_t cyc = g / (reads + writes), pos = g % (reads + writes);
+    if (pos < reads) {
+        const size_t base = ((size_t)cyc * reads + pos) * kThreads * U;
+        u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= load_stream(src + base + (size_t)u * kThreads + l);
+        if (acc[0] == 0x9E3779B9u && acc[1] == 0x7F4A7C15u && acc[2] == 0x85EBCA6Bu && acc[3] == g)
+            store_stream(dst + l, acc);  // never for the probe's data
+    } else {
+        const size_t base = ((size_t)cyc * writes + (pos - reads)) * kThreads * U;
+        const u32x4 v = {g, l, cyc, pos};
+#pragma unroll
+        for (int u = 0; u < U; ++u) store_stream(dst + base + (size_t)u * kThreads + l, v);
     }
+}
+
+template <int TH, int U>
+void launch_mix(const void* src, void* dst, uint32_t waves, uint32_t reads, uint32_t writes, hipStream_t stream) {
+    const uint32_t blocks = (waves + TH / kThreads - 1) / (TH / kThreads);
+    mix_probe_kernel<TH, U><<<dim3(blocks), TH, 0, stream>>>(static_cast<const u32x4*>(src),
+                                                             static_cast<u32x4*>(dst), waves, reads, writes);
 }
 
 }  // namespace
 
-hipError_t launch_mix_probe(const void* src, void* dst, uint32_t lanes, uint32_t reads, uint32_t writes,
-                            hipStream_t stream) {
-    const uint32_t blocks = (lanes + kThreads - 1) / kThreads;
-    mix_probe_kernel<<<dim3(blocks), kThreads, 0, stream>>>(static_cast<const u32x4*>(src), static_cast<u32x4*>(dst),
-                                                            lanes, reads, writes);
+hipError_t launch_mix_probe(const void* src, void* dst, uint32_t cycles, uint32_t reads, uint32_t writes,
+                            int vectors_per_lane, int threads, hipStream_t stream) {
+    const uint32_t waves = cycles * (reads + writes);
+    switch (threads * 8 + vectors_per_lane) {
+        case 64 * 8 + 1: launch_mix<64, 1>(src, dst, waves, reads, writes, stream); break;
+        case 64 * 8 + 2: launch_mix<64, 2>(src, dst, waves, reads, writes, stream); break;
+        case 64 * 8 + 4: launch_mix<64, 4>(src, dst, waves, reads, writes, stream); break;
+        case 256 * 8 + 1: launch_mix<256, 1>(src, dst, waves, reads, writes, stream); break;
+        case 256 * 8 + 2: launch_mix<256, 2>(src, dst, waves, reads, writes, stream); break;
+        case 256 * 8 + 4: launch_mix<256, 4>(src, dst, waves, reads, writes, stream); break;
+        case 1024 * 8 + 1: launch_mix<1024, 1>(src, dst, waves, reads, writes, stream); break;
+        case 1024 * 8 + 2: launch_mix<1024, 2>(src, dst, waves, reads, writes, stream); break;
+        default: launch_mix<1024, 4>(src, dst, waves, reads, writes, stream); break;
+    }
     return hipGetLastError();
 }
 

@@ -147,13 +147,15 @@ def test_copy_probe_argument_errors(lib):
 
 
 def test_mix_probe_argument_errors(lib):
-    assert status(lib, lib.moe_mix_probe(None, FAKE, 64, 1, 1, None)) == "MOE_ERR_NULL"
-    assert status(lib, lib.moe_mix_probe(FAKE, None, 64, 1, 1, None)) == "MOE_ERR_NULL"
-    assert status(lib, lib.moe_mix_probe(FAKE + 4, FAKE, 64, 1, 1, None)) == "MOE_ERR_ALIGN"
-    assert status(lib, lib.moe_mix_probe(FAKE, FAKE, 64, 65, 1, None)) == "MOE_ERR_SHAPE"
-    assert status(lib, lib.moe_mix_probe(FAKE, FAKE, (1 << 30) + 1, 1, 1, None)) == "MOE_ERR_SHAPE"
-    assert status(lib, lib.moe_mix_probe(None, None, 0, 1, 1, None)) == "MOE_OK"
-    assert status(lib, lib.moe_mix_probe(None, None, 64, 0, 0, None)) == "MOE_OK"
+    assert status(lib, lib.moe_mix_probe(None, FAKE, 64, 1, 1, 1, 256, None)) == "MOE_ERR_NULL"
+    assert status(lib, lib.moe_mix_probe(FAKE, None, 64, 1, 1, 1, 256, None)) == "MOE_ERR_NULL"
+    assert status(lib, lib.moe_mix_probe(FAKE + 4, FAKE, 64, 1, 1, 1, 256, None)) == "MOE_ERR_ALIGN"
+    assert status(lib, lib.moe_mix_probe(FAKE, FAKE, 64, 65, 1, 1, 256, None)) == "MOE_ERR_SHAPE"
+    assert status(lib, lib.moe_mix_probe(FAKE, FAKE, (1 << 23) + 1, 1, 1, 1, 256, None)) == "MOE_ERR_SHAPE"
+    assert status(lib, lib.moe_mix_probe(FAKE, FAKE, 64, 1, 1, 3, 256, None)) == "MOE_ERR_SHAPE"
+    assert status(lib, lib.moe_mix_probe(FAKE, FAKE, 64, 1, 1, 1, 128, None)) == "MOE_ERR_SHAPE"
+    assert status(lib, lib.moe_mix_probe(None, None, 0, 1, 1, 1, 256, None)) == "MOE_OK"
+    assert status(lib, lib.moe_mix_probe(None, None, 64, 0, 0, 1, 256, None)) == "MOE_OK"
 
 
 def test_status_strings(lib):
