@@ -23,11 +23,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kKMax = 16;
 
-template <int U, bool ROW_PER_WAVE>
+template <int U, bool ROW_PER_WAVE, int KC>
 __global__ __launch_bounds__(kThreads) void expand_rows_kernel(const u32x4* __restrict__ x,
                                                                const int32_t* __restrict__ dest_of_src, uint32_t n,
-                                                               uint32_t H16, FastDiv div_h16, int k,
+                                                               uint32_t H16, FastDiv div_h16, int k_arg,
                                                                u32x4* __restrict__ x_exp) {
+    const int k = KC > 0 ? KC : k_arg;  // fixed: the k row indices come in under one wait
     const uint32_t base = blockIdx.x * (kThreads * U) + threadIdx.x;
     u32x4 v[U];
 #pragma unroll
@@ -43,7 +44,6 @@ __global__ __launch_bounds__(kThreads) void expand_rows_kernel(const u32x4* __re
             if constexpr (ROW_PER_WAVE) t = uniform(t);
             const uint32_t c = i - t * H16;
             const int32_t* d = dest_of_src + (size_t)t * k;
-            // all k row indices first (clamped: unconditional, in bounds), then the stores
             int32_t dj[kKMax];
 #pragma unroll
             for (int j = 0; j < kKMax; ++j) dj[j] = d[j < k ? j : k - 1];
@@ -63,10 +63,25 @@ hipError_t launch_u(const void* x, const int32_t* dest_of_src, int T, int H, int
     const FastDiv dv = make_fastdiv(H16);
     const u32x4* xs = static_cast<const u32x4*>(x);
     u32x4* xo = static_cast<u32x4*>(x_exp);
-    if (H16 % kWave == 0)
-        expand_rows_kernel<U, true><<<blocks, kThreads, 0, stream>>>(xs, dest_of_src, n, H16, dv, k, xo);
+    // k fixed at compile time lets a wave issue its k stores back to back
+    // instead of one per index fetch: 30.4 -> 28.0 us at T x H = 4096 x
+    // 2048 (k = 8), but 10.7 -> 11.0 us at 1023 x 4096 (k = 6) and 213.7 ->
+    // 222 us at 8192 x 7168 (k = 8), where more write streams at once cost
+    // more than the fetches; so only for rows up to 2048 columns.
+    const bool row = H16 % kWave == 0;
+    const bool fixed_k = row && H16 <= 256;
+    if (fixed_k && k == 8)
+        expand_rows_kernel<U, true, 8><<<blocks, kThreads, 0, stream>>>(xs, dest_of_src, n, H16, dv, k, xo);
+    else if (fixed_k && k == 6)
+        expand_rows_kernel<U, true, 6><<<blocks, kThreads, 0, stream>>>(xs, dest_of_src, n, H16, dv, k, xo);
+    else if (fixed_k && k == 4)
+        expand_rows_kernel<U, true, 4><<<blocks, kThreads, 0, stream>>>(xs, dest_of_src, n, H16, dv, k, xo);
+    else if (fixed_k && k == 2)
+        expand_rows_kernel<U, true, 2><<<blocks, kThreads, 0, stream>>>(xs, dest_of_src, n, H16, dv, k, xo);
+    else if (row)
+        expand_rows_kernel<U, true, 0><<<blocks, kThreads, 0, stream>>>(xs, dest_of_src, n, H16, dv, k, xo);
     else
-        expand_rows_kernel<U, false><<<blocks, kThreads, 0, stream>>>(xs, dest_of_src, n, H16, dv, k, xo);
+        expand_rows_kernel<U, false, 0><<<blocks, kThreads, 0, stream>>>(xs, dest_of_src, n, H16, dv, k, xo);
     return hipGetLastError();
 }
 
@@ -124,6 +139,11 @@ __device__ __forceinline__ void copy_group_rows(const u32x4* __restrict__ x, con
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if (i0 + u * kGroupedThreads < items) store_stream(x_exp + (size_t)ent[u].x * H16 + col[u], v[u]);
+        // an unconditional use of every vector: otherwise the compiler sinks
+        // a vector's row-list and source loads into its store's branch, where
+        // they wait for all older loads and then for each other
+#pragma unroll
+        for (int u = 0; u < U; ++u) asm volatile("" ::"v"(v[u][0]));
     }
 }
 
