@@ -3,13 +3,14 @@
 // dispatch/combine: accumulation in registers, vectorised, using the
 // positions dispatch computed).
 //
-// Token-major gather: a work item is one 16-byte vector (8 bf16) of one output
-// token row; items are numbered row-major over [T, H/8].  The lane issues the
-// k 16-byte loads of its column from the k expert rows at once (k independent
-// loads in flight), accumulates w_j * y_j in fp32 in j order in registers and
-// stores one rounded 16-byte vector.  No atomics, so the result is
-// deterministic.  When a row is a whole number of waves the token index is
-// wave-uniform and its k weights and k row indices come in by scalar loads.
+// Token-major gather: a work item is one lane vector (16 bytes = 8 bf16, or
+// 8 bytes = 4 bf16) of one output token row; items are numbered row-major
+// over [T, H/8] (or [T, H/4]).  The lane issues the k loads of its column
+// from the k expert rows at once (k independent loads in flight),
+// accumulates w_j * y_j in fp32 in j order in registers and stores one
+// rounded vector.  No atomics, so the result is deterministic.  When a row
+// is a whole number of waves the token index is wave-uniform and its k
+// weights and k row indices come in by scalar loads.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -22,18 +23,32 @@ namespace {
 constexpr int kThreads = 64;
 constexpr int kKMax = 16;
 
-template <bool ROW_PER_WAVE, int KC>
-__global__ __launch_bounds__(kThreads) void combine_kernel(const u32x4* __restrict__ y,
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+template <int W>
+struct LaneVec;
+template <>
+struct LaneVec<4> {
+    typedef u32x4 type;
+};
+template <>
+struct LaneVec<2> {
+    typedef u32x2v type;
+};
+
+// W words (2W bf16) per lane.
+template <bool ROW_PER_WAVE, int KC, int W>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const typename LaneVec<W>::type* __restrict__ y,
                                                            const float* __restrict__ w,
                                                            const int32_t* __restrict__ dest_of_src, uint32_t n,
-                                                           uint32_t H16, FastDiv div_h16, int k_arg,
-                                                           u32x4* __restrict__ out) {
+                                                           uint32_t HL, FastDiv div_hl, int k_arg,
+                                                           typename LaneVec<W>::type* __restrict__ out) {
+    typedef typename LaneVec<W>::type Vec;
     const int k = KC > 0 ? KC : k_arg;
     const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
     if (i >= n) return;
-    uint32_t t = fastdiv(i, div_h16);
+    uint32_t t = fastdiv(i, div_hl);
     if constexpr (ROW_PER_WAVE) t = uniform(t);
-    const uint32_t c = i - t * H16;
+    const uint32_t c = i - t * HL;
     const int32_t* d = dest_of_src + (size_t)t * k;
     const float* wt = w + (size_t)t * k;
 
@@ -52,21 +67,47 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const u32x4* __restri
         dj[j] = d[jj];
         wj[j] = wt[jj];
     }
-    u32x4 v[kKMax];
+    Vec v[kKMax];
 #pragma unroll
     for (int j = 0; j < kKMax; ++j)
-        if (j < k) v[j] = load_stream(y + (size_t)dj[j] * H16 + c);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (j < k) v[j] = __builtin_nontemporal_load(y + (size_t)dj[j] * HL + c);
+    float acc[2 * W];
+#pragma unroll
+    for (int e = 0; e < 2 * W; ++e) acc[e] = 0.f;
 #pragma unroll
     for (int j = 0; j < kKMax; ++j) {
         if (j < k) {
-            float f[8];
-            unpack8(v[j], f);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(wj[j], f[e], acc[e]);
+            for (int q = 0; q < W; ++q) {
+                acc[2 * q] = __builtin_fmaf(wj[j], bf16_lo(v[j][q]), acc[2 * q]);
+                acc[2 * q + 1] = __builtin_fmaf(wj[j], bf16_hi(v[j][q]), acc[2 * q + 1]);
+            }
         }
     }
-    store_stream(out + i, pack8(acc));
+    Vec o;
+#pragma unroll
+    for (int q = 0; q < W; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    __builtin_nontemporal_store(o, out + i);
+}
+
+template <bool ROW_PER_WAVE, int KC, int W>
+void launch_w(const void* y, const float* topk_weights, const int32_t* dest_of_src, int T, int H, int k, void* out,
+              hipStream_t stream) {
+    typedef typename LaneVec<W>::type Vec;
+    const uint32_t HL = (uint32_t)H / (2 * W);
+    const uint32_t n = (uint32_t)T * HL;
+    const uint32_t blocks = (n + kThreads - 1) / kThreads;
+    combine_kernel<ROW_PER_WAVE, KC, W><<<blocks, kThreads, 0, stream>>>(
+        static_cast<const Vec*>(y), topk_weights, dest_of_src, n, HL, make_fastdiv(HL), k, static_cast<Vec*>(out));
+}
+
+template <int KC>
+void launch_kc(bool narrow, const void* y, const float* topk_weights, const int32_t* dest_of_src, int T, int H, int k,
+               void* out, hipStream_t stream) {
+    if (narrow)
+        launch_w<true, KC, 2>(y, topk_weights, dest_of_src, T, H, k, out, stream);
+    else
+        launch_w<true, KC, 4>(y, topk_weights, dest_of_src, T, H, k, out, stream);
 }
 
 }  // namespace
@@ -74,24 +115,25 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const u32x4* __restri
 hipError_t launch_combine(const void* y, const float* topk_weights, const int32_t* dest_of_src, int T, int H,
                           int k, void* out, hipStream_t stream) {
     const uint32_t H16 = (uint32_t)H / 8;
-    const uint32_t n = (uint32_t)T * H16;
-    const uint32_t blocks = (n + kThreads - 1) / kThreads;
-    const FastDiv dv = make_fastdiv(H16);
-    const u32x4* ys = static_cast<const u32x4*>(y);
-    u32x4* o = static_cast<u32x4*>(out);
+    // 8-byte lanes (twice the waves, half the bytes each) for large batches:
+    // 25.2 -> 24.6 us at T x H = 4096 x 2048 and 180.2 -> 175.0 us at 8192 x
+    // 7168 in a back-to-back probe, but 13.6 -> 14.4 us at 1024 x 4096,
+    // whose 16-byte grid is resident on the chip in one round.  Only for the
+    // fixed-k kernels with rows of whole 8-byte waves.
     const bool row = H16 % kWave == 0;
+    const bool narrow = (uint32_t)H % (4 * kWave) == 0 && (uint64_t)T * H16 >= (1u << 20);
     if (row && k == 8)
-        combine_kernel<true, 8><<<blocks, kThreads, 0, stream>>>(ys, topk_weights, dest_of_src, n, H16, dv, k, o);
+        launch_kc<8>(narrow, y, topk_weights, dest_of_src, T, H, k, out, stream);
     else if (row && k == 6)
-        combine_kernel<true, 6><<<blocks, kThreads, 0, stream>>>(ys, topk_weights, dest_of_src, n, H16, dv, k, o);
+        launch_kc<6>(narrow, y, topk_weights, dest_of_src, T, H, k, out, stream);
     else if (row && k == 4)
-        combine_kernel<true, 4><<<blocks, kThreads, 0, stream>>>(ys, topk_weights, dest_of_src, n, H16, dv, k, o);
+        launch_kc<4>(narrow, y, topk_weights, dest_of_src, T, H, k, out, stream);
     else if (row && k == 2)
-        combine_kernel<true, 2><<<blocks, kThreads, 0, stream>>>(ys, topk_weights, dest_of_src, n, H16, dv, k, o);
+        launch_kc<2>(narrow, y, topk_weights, dest_of_src, T, H, k, out, stream);
     else if (row)
-        combine_kernel<true, 0><<<blocks, kThreads, 0, stream>>>(ys, topk_weights, dest_of_src, n, H16, dv, k, o);
+        launch_w<true, 0, 4>(y, topk_weights, dest_of_src, T, H, k, out, stream);
     else
-        combine_kernel<false, 0><<<blocks, kThreads, 0, stream>>>(ys, topk_weights, dest_of_src, n, H16, dv, k, o);
+        launch_w<false, 0, 4>(y, topk_weights, dest_of_src, T, H, k, out, stream);
     return hipGetLastError();
 }
 

@@ -168,7 +168,8 @@ def test_skewed_tie_rows(dev, oracle_lib):
 @pytest.mark.parametrize("T,H,E,k", [(1, 8, 4, 1), (3, 8, 4, 4), (77, 520, 17, 5), (300, 2048, 128, 8),
                                      (65, 4096, 64, 16), (513, 264, 8, 2), (50, 32768, 16, 4),
                                      (257, 1024, 8, 2), (130, 512, 12, 6), (33, 512, 9, 3),
-                                     (64, 1536, 16, 4)])
+                                     (64, 1536, 16, 4), (512, 16384, 16, 4), (2048, 4096, 8, 2),
+                                     (1100, 8192, 32, 6)])
 def test_expand_combine_shapes(dev, oracle_lib, T, H, E, k):
     cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
     _log(f"[rows] T={T} H={H} E={E} k={k}")
