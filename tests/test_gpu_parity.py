@@ -235,7 +235,8 @@ def test_swiglu_every_finite_bf16_gate(dev, oracle_lib):
         compare.assert_bf16_close(got, oracle_lib.swiglu(h), f"swiglu u={u_bits:#06x}")
 
 
-@pytest.mark.parametrize("R,I", [(1, 8), (3, 16), (257, 768), (1023, 1408), (64, 2048), (7, 2056), (5, 16384)])
+@pytest.mark.parametrize("R,I", [(1, 8), (3, 16), (257, 768), (1023, 1408), (64, 2048), (7, 2056), (5, 16384),
+                                 (1367, 6152)])
 def test_swiglu_shapes(dev, oracle_lib, R, I):
     import torch
     import moe_glue_amd as mg
