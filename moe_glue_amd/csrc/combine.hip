@@ -119,9 +119,11 @@ hipError_t launch_combine(const void* y, const float* topk_weights, const int32_
     // 25.2 -> 24.6 us at T x H = 4096 x 2048 and 180.2 -> 175.0 us at 8192 x
     // 7168 in a back-to-back probe, but 13.6 -> 14.4 us at 1024 x 4096,
     // whose 16-byte grid is resident on the chip in one round.  Only for the
-    // fixed-k kernels with rows of whole 8-byte waves.
+    // fixed-k kernels with rows of whole 8-byte waves, and while the 8-byte
+    // item count stays below 2^31 (the range of the row division).
     const bool row = H16 % kWave == 0;
-    const bool narrow = (uint32_t)H % (4 * kWave) == 0 && (uint64_t)T * H16 >= (1u << 20);
+    const uint64_t items16 = (uint64_t)T * H16;
+    const bool narrow = (uint32_t)H % (4 * kWave) == 0 && items16 >= (1u << 20) && items16 < (1u << 30);
     if (row && k == 8)
         launch_kc<8>(narrow, y, topk_weights, dest_of_src, T, H, k, out, stream);
     else if (row && k == 6)
