@@ -49,7 +49,7 @@ constexpr int kPeSlots = kPeSlotsPerLane;        // group slots per lane
 constexpr int kPeMaskWords = kPeMaskWordsMax;    // E * (group tokens / 64) bitmap words
 constexpr int kPeRows = kPeRowsMax;              // rows one workgroup copies
 constexpr int kPePrefetch = 4;                   // source vectors per lane touched up front
-constexpr int kPeVectors = 2;                    // 16-byte vectors per lane per copy pass
+constexpr int kPeVectors = 1;                    // 16-byte vectors per lane per copy pass (1 beat 2 and 4)
 constexpr int kPeDefaultS = 32;                  // workgroups per token group
 
 template <int QP, int U>
