@@ -44,18 +44,16 @@ def run_path(inp: dict, dev, parts=("route", "expand", "swiglu", "combine"), fus
     out = {}
     logits = to_dev(inp["logits"], dev)
     bias = to_dev(inp["bias"], dev) if inp.get("bias") is not None else None
-    if fused:
+    if fused:  # route + expand in one call; x_expanded comes with the route outputs
         r = mg.route_expand(logits, cfg.k, to_dev(inp["x"], dev), bias)
-        out.update(route_host(r))
-        torch.cuda.synchronize(dev)
-        return out
-    r = mg.route(logits, cfg.k, bias)
+    else:
+        r = mg.route(logits, cfg.k, bias)
     out.update(route_host(r))
     # the row kernels trust dest_of_src; make sure it is a permutation before they run
     d = out["dest_of_src"]
     assert d.size == cfg.R and (d.size == 0 or (d.min() >= 0 and d.max() < cfg.R)), "dest_of_src out of range"
     assert np.array_equal(np.sort(d), np.arange(cfg.R)), "dest_of_src is not a permutation"
-    if "expand" in parts:
+    if "expand" in parts and not fused:
         out["x_expanded"] = to_host(mg.expand_rows(to_dev(inp["x"], dev), r["dest_of_src"], cfg.k))
     if "swiglu" in parts:
         out["act"] = to_host(mg.swiglu(to_dev(inp["h"], dev)))

@@ -62,15 +62,25 @@ def test_workload_full_size_route_expand(dev, oracle_lib, force, name, order):
     cfg = inputs.CONFIGS[name]
     _log(f"[parity] route_expand {inputs.describe(cfg)} seed=0 order={order}")
     inp = inputs.make_inputs(cfg, 0, parts=("x", "logits"))
-    got = G.run_path(inp, dev, fused=True)
+    got = G.run_path(inp, dev, parts=("route", "expand"), fused=True)
     ref = oracle_lib.route(inp["logits"], cfg.k, inp["bias"])
     compare.assert_route_equal(got, ref, f"{name} route_expand")
     compare.assert_equal(got["x_expanded"], oracle_lib.expand_rows(inp["x"], ref["dest_of_src"], cfg.k),
                          f"{name} route_expand x_expanded")
 
 
+@pytest.mark.parametrize("name", inputs.CONFIG_ORDER)
+def test_workload_full_size_bench_path(dev, oracle_lib, name):
+    """The calls the benchmark times, in its order: moe_route_expand, then
+    SwiGLU and combine on the result."""
+    cfg = inputs.CONFIGS[name]
+    _log(f"[parity] bench path {inputs.describe(cfg)} seed=0")
+    inp = inputs.make_inputs(cfg, 0)
+    check_path(G.run_path(inp, dev, fused=True), oracle_lib.path(inp), cfg, f"{name} bench path")
+
+
 @pytest.mark.parametrize("seed", [1, 2])
-@pytest.mark.parametrize("name", ["tiny", "decode", "skewed"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "skewed", "qwen3_30b_a3b"])
 def test_workload_more_seeds(dev, oracle_lib, name, seed):
     cfg = inputs.CONFIGS[name]
     _log(f"[parity] {inputs.describe(cfg)} seed={seed}")
