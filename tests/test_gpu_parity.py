@@ -820,3 +820,41 @@ def test_graph_replay_matches_eager(dev, force, T, E, k, H, I, variant, order):
         got["act"], got["out"] = G.to_host(bufs[1]), G.to_host(bufs[2])
         for key in want:
             compare.assert_equal(got[key], want[key], f"graph replay {rep}: {key}")
+
+
+def test_concurrent_streams(dev, oracle_lib):
+    """Calls on two streams at once, each with its own buffers (the library
+    keeps no state between calls): three batches, one per route + expand form
+    (one-launch dispatch, the route's place step copying, the placing
+    expand), issued alternately on two streams with no synchronisation in
+    between, each result against the oracle."""
+    import torch
+    import moe_glue_amd as mg
+
+    shapes = [(40, 128, 8, 1024, 64), (500, 64, 6, 512, 96), (900, 128, 8, 1024, 128)]  # T, E, k, H, I
+    cases = []
+    for n, (T, E, k, H, I) in enumerate(shapes):
+        cfg = inputs.Config(f"streams{n}", T=T, H=H, E=E, k=k, I=I)
+        cases.append((cfg, inputs.make_inputs(cfg, 30 + n)))
+    _log("[streams] " + ", ".join(inputs.describe(c) for c, _ in cases))
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    dev_in = [{key: G.to_dev(inp[key], dev) for key in ("logits", "x", "h", "y")} for _, inp in cases]
+    torch.cuda.synchronize()
+    results = []
+    for it in range(4):
+        for n, (cfg, _) in enumerate(cases):
+            with torch.cuda.stream(streams[(it + n) % 2]):
+                d = dev_in[n]
+                r = mg.route_expand(d["logits"], cfg.k, d["x"])
+                act = mg.swiglu(d["h"])
+                out = mg.combine(d["y"], r["topk_weights"], r["dest_of_src"])
+                results.append((n, r, act, out))
+    torch.cuda.synchronize()
+    refs = [oracle_lib.path(inp) for _, inp in cases]
+    for n, r, act, out in results:
+        cfg, ref = cases[n][0], refs[n]
+        got = G.route_host(r)
+        compare.assert_route_equal(got, ref, f"streams {cfg.name}")
+        compare.assert_equal(got["x_expanded"], ref["x_expanded"], f"streams {cfg.name} x_expanded")
+        compare.assert_bf16_close(G.to_host(act), ref["act"], f"streams {cfg.name} act")
+        compare.assert_bf16_close(G.to_host(out), ref["out"], f"streams {cfg.name} out")
