@@ -234,7 +234,7 @@ moe_status moe_route_expand_padded(const float* logits, const float* bias, int32
  * results on the same arguments (pad_to = 1: moe_route; all outputs of both
  * calls are written; padding rows of x_expanded and scales are not written).
  * For T <= 64 routing and quantising copy are one launch (as in
- * moe_route_expand).  On the two-launch route with H <= 16384 and at most
+ * moe_route_expand).  On the two-launch route with H <= 8192 and at most
  * ~20 MB of codes the quantising copy runs in the route's place launch;
  * otherwise the route is followed by the quantising expand.
  * The workspace must hold moe_route_workspace_bytes(T, E, k) bytes (16-byte

@@ -90,14 +90,14 @@ int forced_order() { return g_force_order.load(std::memory_order_relaxed); }
 // -0.5, 2048 x 2048 -2.2, 1024 x 7168 (256, 8) -1.8, 2048 x 7168 (256, 8)
 // -2.4 us.  Up to 24576 expanded rows 64 workgroups per group (one group per
 // XCD) beat 32 by 0.1-0.6 us; at 32768 rows (Qwen3-30B-A3B) 32 beat 64 by 1.2.
-// With one vector per lane in the placing copy the Fused crossover follows
-// the expanded bytes: at H = 2048, k = 8, Placed minus Fused is +1.0 us at
-// 640 tokens (21 MB of expanded rows), +0.5 at 704, +0.15 at 768, 0 at 832
-// (27 MB), -0.35 at 896 and -0.6 at 1024; 1023 x 4096 (64, 6), 50 MB, -0.9.
+// With one vector per lane in both copies the Fused crossover follows the
+// expanded bytes: at H = 2048, k = 8, Placed minus Fused is +0.2 us at 832
+// tokens (27 MB of expanded rows), -0.1 at 896 (29 MB), -0.35 at 960, -0.6
+// at 1024, -0.4 at 1280; 1023 x 4096 (64, 6), 50 MB, -0.35.
 constexpr int kPlacedMaxTokens = 6144;
 constexpr int64_t kPlacedMaxSourceBytes = 32ll << 20;
 constexpr int64_t kPlacedMinRows = 5120;
-constexpr int64_t kPlacedMinExpandedBytes = 26ll << 20;
+constexpr int64_t kPlacedMinExpandedBytes = 28ll << 20;
 constexpr int64_t kPlacedWideGroupMaxRows = 24576;
 
 ExpandOrder expand_order(int32_t T, int32_t E, int32_t k, int32_t H, moe::RouteVariant v,

@@ -20,7 +20,7 @@ namespace moe {
 constexpr int kCopyNone = 0;
 constexpr int kCopyBf16 = 1;
 constexpr int kCopyFp8 = 2;
-constexpr int kCopyItems = 2;            // row vectors per lane
+constexpr int kCopyItems = 1;            // row vectors per lane (1 beat 2: finer slices)
 constexpr int kPlaceCopyThreads = 1024;  // lanes per workgroup of the place step
 
 struct PlaceCopy {
