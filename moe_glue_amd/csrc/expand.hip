@@ -209,9 +209,14 @@ hipError_t launch_expand_grouped(const void* x, const int32_t* row_list, const R
 
 hipError_t launch_expand_rows(const void* x, const int32_t* dest_of_src, int T, int H, int k, void* x_expanded,
                               hipStream_t stream) {
-    // small batches: one vector per lane keeps more workgroups in flight
+    // one vector per lane keeps more workgroups in flight on small batches,
+    // and on very large ones it also won (8192 x 7168: 214.6 -> 204.0 us,
+    // 4096 x 7168: 109.9 -> 105.1, 16384 x 2048: 125.6 -> 124.7); between,
+    // two per lane (4096 x 2048: 27.9 against 29.8 us; 2048 x 7168: 51.4
+    // against 52.0; 8192 x 2048: 59.9 against 61.4)
     const size_t n = (size_t)T * (H / 8);
-    if (n < (size_t)256 * kThreads * 2) return launch_u<1>(x, dest_of_src, T, H, k, x_expanded, stream);
+    if (n < (size_t)256 * kThreads * 2 || n >= ((size_t)3 << 20))
+        return launch_u<1>(x, dest_of_src, T, H, k, x_expanded, stream);
     return launch_u<2>(x, dest_of_src, T, H, k, x_expanded, stream);
 }
 
