@@ -97,10 +97,12 @@ hipError_t launch_u(const void* x, const int32_t* dest_of_src, int T, int H, int
 // group's source rows stay in its L2 and HBM sees each read about once; the
 // eight XCDs work on neighbouring groups, whose rows in each expert segment
 // are neighbours too.  Each workgroup copies kGroupedItems / (H/8) rows (at
-// least one) in one pass of its lanes: two vectors per lane, or four when a
-// row is wider than kGroupedItems vectors (at H = 7168 the 896 vectors of a
-// row then take one pass instead of two: 217 -> 209 us for the DeepSeek-V3
-// batch in a standalone probe).
+// least one): one vector per lane in two passes, or four vectors per lane
+// in one pass when a row is wider than kGroupedItems vectors (at H = 7168
+// the 896 vectors of a row then take one pass instead of two: 217 -> 209 us
+// for the DeepSeek-V3 batch in a standalone probe; 213 -> 216 us with two
+// per lane).  On the narrower rows one vector per lane beat two (8192 x
+// 2048: 63.2 -> 61.1 us per call; 8192 x 4096, k = 6: 90.3 -> 88.9).
 //
 // A group's first rows in destination order need source rows all over the
 // group, so when x comes from HBM (not from the Infinity Cache) the early
@@ -201,8 +203,8 @@ hipError_t launch_expand_grouped(const void* x, const int32_t* row_list, const R
     if (H16 > (uint32_t)kGroupedItems)
         expand_grouped_kernel<4><<<grid, kGroupedThreads, 0, stream>>>(xs, lst, groups, k, H16, make_fastdiv(H16),
                                                                        rows_per_wg, chunks, xo);
-    else
-        expand_grouped_kernel<2><<<grid, kGroupedThreads, 0, stream>>>(xs, lst, groups, k, H16, make_fastdiv(H16),
+    else  // one vector per lane, two passes: 63.2 -> 61.1 us per call at 8192 x 2048 against two per lane
+        expand_grouped_kernel<1><<<grid, kGroupedThreads, 0, stream>>>(xs, lst, groups, k, H16, make_fastdiv(H16),
                                                                        rows_per_wg, chunks, xo);
     return hipGetLastError();
 }
