@@ -7,7 +7,9 @@ configuration the benchmark times), three seeds of the small ones, the token
 sweep {1, 7, 32, 257, 1023} at the Qwen3-30B-A3B shape, both route variants,
 and the edge cases of the method (T = 0, k = 1, k = E, E not a multiple of 4,
 E = 512 with k = 16, exact ties, signed zeros, constant rows, rows that are not
-a whole number of waves, every finite bf16 gate value)."""
+a whole number of waves, every finite bf16 gate value), and seeded random
+shapes across the size rule's boundaries for the benchmark's calls and for
+the padded, FP8 and MXFP8 route + expand calls."""
 import os
 import sys
 
@@ -94,6 +96,42 @@ def test_token_sweep_qwen_shape(dev, oracle_lib, T):
     _log(f"[parity] {inputs.describe(cfg)}")
     inp = inputs.make_inputs(cfg, 0)
     check_path(G.run_path(inp, dev), oracle_lib.path(inp), cfg, cfg.name)
+
+
+def _random_configs(n=40, seed=20261203):
+    """Seeded random shapes across the size rule's boundaries, a quarter each
+    with T in [1, 64] (the one-launch dispatch), [65, 1500], [1500, 6000],
+    and [1200, 6000] with wide rows (H >= 1024, k >= 4: the placing and
+    grouped expands); H a multiple of 8, log-uniform up to 8800; E in [1,
+    512]; k in [1, min(E, 16)]; I a multiple of 8 up to 2048; a router bias,
+    Zipf skew or tie rows now and then; at most 48M expanded elements, so
+    the oracle stays quick."""
+    rng = np.random.default_rng(seed)
+    bands = [(1, 64, 8, 1), (65, 1500, 8, 1), (1500, 6000, 8, 1), (1200, 6000, 1024, 4)]
+    out = []
+    while len(out) < n:
+        lo, hi, hmin, kmin = bands[len(out) % 4]
+        T = int(rng.integers(lo, hi + 1))
+        H = 8 * int(np.exp(rng.uniform(np.log(hmin / 8), np.log(1100.0))))
+        E = int(rng.integers(kmin, 513))
+        k = int(rng.integers(kmin, min(E, 16) + 1))
+        I = 8 * int(rng.integers(1, 257))
+        if T * k * H > 48_000_000 or T * k * 2 * I > 24_000_000:
+            continue
+        kind = int(rng.integers(0, 4))
+        out.append(inputs.Config(f"rand{len(out)}", T=T, H=H, E=E, k=k, I=I,
+                                 bias_std=0.5 if kind == 1 else 0.0, zipf_s=1.2 if kind == 2 else 0.0,
+                                 tie_frac=0.05 if kind == 3 else 0.0))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_configs(), ids=lambda c: c.name)
+def test_random_shapes_bench_path(dev, oracle_lib, cfg):
+    """The benchmark's calls (moe_route_expand in the order the size rule
+    picks, then SwiGLU and combine) on seeded random shapes."""
+    _log(f"[parity] random {inputs.describe(cfg)} bias={cfg.bias_std} zipf={cfg.zipf_s} ties={cfg.tie_frac}")
+    inp = inputs.make_inputs(cfg, 3)
+    check_path(G.run_path(inp, dev, fused=True), oracle_lib.path(inp), cfg, cfg.name)
 
 
 # ------------------------------------------------------------------ route
@@ -763,6 +801,91 @@ def test_route_expand_quantised_every_route_variant(dev, oracle_lib, force, fmt,
     valid = ref["src_of_dest"] >= 0
     compare.assert_equal(got["x_expanded"][:n][valid], qr[valid], f"{fmt} codes (valid rows)")
     compare.assert_equal(got["scales"][:n][valid], scr[valid], f"{fmt} scales (valid rows)")
+
+
+def _random_variant_cases(n=36, seed=20261204):
+    """Seeded random shapes (as for the bench-path sweep) for the padded,
+    FP8 and MXFP8 route + expand calls, in turn: pad_to in [2, 256] for the
+    padded call, in {1} or [2, 256] for the quantising ones (lowered where
+    the padded rows would pass 48M elements); the FP8 group a power of two
+    in [8, 512] dividing H; H rounded up to a multiple of 32 for MXFP8."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i, cfg in enumerate(_random_configs(n, seed)):
+        fmt = ("padded", "fp8", "mxfp8")[i % 3]
+        M = int(rng.integers(2, 257)) if fmt == "padded" or rng.integers(0, 2) else 1
+        H = cfg.H
+        # at most T*k + E*(pad_to - 1) padded rows: keep them under 48M elements
+        M = max(1, min(M, (48_000_000 // H - cfg.T * cfg.k) // cfg.E + 1))
+        group = 0
+        if fmt == "fp8":
+            groups = [g for g in (8, 16, 32, 64, 128, 256, 512) if H % g == 0]
+            group = int(groups[rng.integers(0, len(groups))])
+        if fmt == "mxfp8":
+            H = (H + 31) // 32 * 32
+        c = inputs.Config(cfg.name, T=cfg.T, H=H, E=cfg.E, k=cfg.k, I=8, bias_std=cfg.bias_std,
+                          zipf_s=cfg.zipf_s, tie_frac=cfg.tie_frac)
+        out.append((c, fmt, M, group))
+    return out
+
+
+@pytest.mark.parametrize("cfg,fmt,M,group", _random_variant_cases(), ids=lambda v: getattr(v, "name", str(v)))
+def test_random_shapes_padded_and_quantised(dev, oracle_lib, cfg, fmt, M, group):
+    """moe_route_expand_padded / _fp8 / _mxfp8 in the order the size rule
+    picks, on seeded random shapes: maps, rows (codes and scales) of every
+    real row, padding rows untouched."""
+    import torch
+    import moe_glue_amd as mg
+
+    T, E, k, H = cfg.T, cfg.E, cfg.k, cfg.H
+    _log(f"[random {fmt}] {inputs.describe(cfg)} pad_to={M} group={group} bias={cfg.bias_std} "
+         f"zipf={cfg.zipf_s} ties={cfg.tie_frac}")
+    inp = inputs.make_inputs(cfg, 5, parts=("x", "logits"))
+    bias = None if inp["bias"] is None else G.to_dev(inp["bias"], dev)
+    P = mg.padded_rows(T, E, k, M) if M > 1 else T * k
+    out = mg.alloc_route_outputs(T, E, k, dev)
+    out["src_of_dest"] = torch.empty((max(P, 1),), dtype=torch.int32, device=dev)
+    if fmt == "padded":
+        out["x_expanded"] = torch.full((max(P, 1), H), 0x7F7F, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    else:
+        out["x_expanded"] = torch.full((max(P, 1), H), 0xAB, dtype=torch.uint8, device=dev)
+        if fmt == "fp8":
+            out["scales"] = torch.full((max(P, 1), H // group), -7.0, dtype=torch.float32, device=dev)
+        else:
+            out["scales"] = torch.full((max(P, 1), H // 32), 0xCD, dtype=torch.uint8, device=dev)
+    lg, xd = G.to_dev(inp["logits"], dev), G.to_dev(inp["x"], dev)
+    if fmt == "padded":
+        r = mg.route_expand_padded(lg, k, M, xd, bias, out=out)
+    elif fmt == "fp8":
+        r = mg.route_expand_fp8(lg, k, xd, group, M, bias, out=out)
+    else:
+        r = mg.route_expand_mxfp8(lg, k, xd, M, bias, out=out)
+    torch.cuda.synchronize()
+    got = G.route_host(r)
+    ref = (oracle_lib.route_padded(inp["logits"], k, M, inp["bias"]) if M > 1
+           else oracle_lib.route(inp["logits"], k, inp["bias"]))
+    n = int(ref["expert_offsets"][E])
+    got["src_of_dest"] = got["src_of_dest"][:n]
+    rows = {key: got.pop(key) for key in ("x_expanded", "scales") if key in got}
+    compare.assert_route_equal(got, ref, f"random {fmt} T={T} E={E} k={k} M={M}")
+    valid = ref["src_of_dest"] >= 0
+    xe = rows["x_expanded"]
+    if fmt == "padded":
+        want = oracle_lib.expand_rows(inp["x"], ref["dest_of_src"], k, rows=n)
+        compare.assert_equal(xe[:n][valid], want[valid], "padded x_expanded (real rows)")
+        assert np.all(xe[:n][~valid] == 0x7F7F) and np.all(xe[n:] == 0x7F7F), "rows written into padding"
+        return
+    if fmt == "fp8":
+        qr, scr = oracle_lib.expand_rows_fp8(inp["x"], ref["dest_of_src"], k, group, rows=n)
+        untouched = -7.0
+    else:
+        qr, scr = oracle_lib.expand_rows_mxfp8(inp["x"], ref["dest_of_src"], k, rows=n)
+        untouched = 0xCD
+    sc = rows["scales"]
+    compare.assert_equal(xe[:n][valid], qr[valid], f"{fmt} codes (real rows)")
+    compare.assert_equal(sc[:n][valid], scr[valid], f"{fmt} scales (real rows)")
+    assert np.all(xe[:n][~valid] == 0xAB) and np.all(xe[n:] == 0xAB), "codes written into padding rows"
+    assert np.all(sc[:n][~valid] == untouched) and np.all(sc[n:] == untouched), "scales written into padding"
 
 
 @pytest.mark.parametrize("T,E,k,H,I,variant,order", [(32, 128, 8, 2048, 768, "auto", "auto"),
