@@ -577,7 +577,7 @@ def pmc_bytes(read_dir: str, write_dir: str) -> dict:
 
 
 def _call_of_kernel(name: str, route_call: str):
-    if name.startswith("swiglu_kernel"):
+    if name.startswith("swiglu"):  # swiglu_kernel<U>, swiglu8_kernel
         return "swiglu"
     if name.startswith("combine_kernel"):
         return "combine"
@@ -596,7 +596,7 @@ def traffic_report(read_dir: str, write_dir: str, cfg, pad_to=1, fp8_group=0, mx
                   else "route_expand" if pad_to == 1 else "route_expand_padded")
     ab = algorithmic_bytes(cfg, fp8_group)
     probe = [pmc_request_bytes(c) for n, g, c in disp if n.startswith("copy_probe") and g == COPY_PROBE_LANES]
-    steps = sum(1 for n, _, _ in disp if n.startswith("swiglu_kernel"))
+    steps = sum(1 for n, _, _ in disp if n.startswith("swiglu"))
     per_kernel, per_call = {}, {}
     for n, _, c in disp:
         call = _call_of_kernel(n, route_call)

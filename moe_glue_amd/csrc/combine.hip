@@ -23,7 +23,6 @@ namespace {
 constexpr int kThreads = 64;
 constexpr int kKMax = 16;
 
-typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 template <int W>
 struct LaneVec;
 template <>
@@ -32,33 +31,21 @@ struct LaneVec<4> {
 };
 template <>
 struct LaneVec<2> {
-    typedef u32x2v type;
+    typedef u32x2 type;
 };
 
-// Buffer resource word 3 for raw (untyped) buffer access: a non-zero data
-// format (32-bit) keeps the access in range; stride 0, so num_records counts
-// bytes.
-constexpr int kRawBufferWord3 = 0x00020000;
-// Cache-policy bits of a buffer store on gfx950: nt (2) and sc1 (16).
-constexpr int kStoreNtSc1 = 2 | 16;
-
-// The lane's output vector, non-temporal.  The 8-byte lanes (large batches)
-// also set sc1, through a buffer store whose resource covers this wave's
-// items (one wave per workgroup): in the path at T x H = 4096 x 2048 combine
-// 26.1 -> 25.8 us and at 8192 x 7168 173.2 -> 172.4 us (HIP events, medians
-// of 200 steps, four rounds; sc0 on top changes nothing), while the 16-byte
-// lanes of a 1023 x 4096 batch lose 0.1 us with it.
+// The lane's output vector, non-temporal; the 8-byte lanes also set sc1:
+// in the path at T x H = 4096 x 2048 combine 26.1 -> 25.8 us, at 8192 x 7168
+// 173.2 -> 172.4 us (HIP events, medians of 200 steps, the two forms
+// alternated four times; sc0 on top changes nothing), while the 16-byte lanes
+// of a 1023 x 4096 batch lose 0.1 us with it.
 template <int W>
 __device__ __forceinline__ void store_out(typename LaneVec<W>::type* __restrict__ out, uint32_t i, uint32_t n,
                                           const typename LaneVec<W>::type& o) {
-    if constexpr (W == 2) {
-        const uint32_t i0 = blockIdx.x * kThreads;  // this wave's first item; i0 <= i < n
-        const int bytes = (int)(min(n - i0, (uint32_t)kThreads) * sizeof(o));
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(out + i0, 0, bytes, kRawBufferWord3);
-        __builtin_amdgcn_raw_buffer_store_b64(o, rs, (int)((i - i0) * sizeof(o)), 0, kStoreNtSc1);
-    } else {
+    if constexpr (W == 2)
+        store_stream_sc1(out, blockIdx.x * kThreads, i, n, o);  // one wave per workgroup
+    else
         __builtin_nontemporal_store(o, out + i);
-    }
 }
 
 // W words (2W bf16) per lane.
@@ -141,15 +128,16 @@ void launch_kc(bool narrow, const void* y, const float* topk_weights, const int3
 hipError_t launch_combine(const void* y, const float* topk_weights, const int32_t* dest_of_src, int T, int H,
                           int k, void* out, hipStream_t stream) {
     const uint32_t H16 = (uint32_t)H / 8;
-    // 8-byte lanes (twice the waves, half the bytes each) for large batches:
-    // 25.2 -> 24.6 us at T x H = 4096 x 2048 and 180.2 -> 175.0 us at 8192 x
-    // 7168 in a back-to-back probe, but 13.6 -> 14.4 us at 1024 x 4096,
-    // whose 16-byte grid is resident on the chip in one round.  Only for the
-    // fixed-k kernels with rows of whole 8-byte waves, and while the 8-byte
-    // item count stays below 2^31 (the range of the row division).
+    // 8-byte lanes (twice the waves, half the bytes each) from 2^18 16-byte
+    // items: 25.2 -> 24.6 us at T x H = 4096 x 2048 and 180.2 -> 175.0 us at
+    // 8192 x 7168 in a back-to-back probe; at 1024 x 4096 they first lost
+    // (13.6 -> 14.4 us), but with the sc1 stores the 1023 x 4096 batch (k = 6)
+    // gains in the path, 11.78 -> 11.54 us.  Only for the fixed-k kernels with
+    // rows of whole 8-byte waves, and while the 8-byte item count stays below
+    // 2^31 (the range of the row division).
     const bool row = H16 % kWave == 0;
     const uint64_t items16 = (uint64_t)T * H16;
-    const bool narrow = (uint32_t)H % (4 * kWave) == 0 && items16 >= (1u << 20) && items16 < (1u << 30);
+    const bool narrow = (uint32_t)H % (4 * kWave) == 0 && items16 >= (1u << 18) && items16 < (1u << 30);
     if (row && k == 8)
         launch_kc<8>(narrow, y, topk_weights, dest_of_src, T, H, k, out, stream);
     else if (row && k == 6)

@@ -13,8 +13,6 @@
 
 namespace moe {
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
 
 // Largest |f[e]| of the lane's 8 values, as fp32 bits.

@@ -8,7 +8,8 @@
 // of 8 outputs, items are numbered row-major over [R, I/8] and lanes take
 // consecutive items, so no lane idles whatever I is (I=768 gives 96 items
 // per row; 2 rows fill 3 waves exactly).  Each item reads 16 B of gate and
-// 16 B of up and writes 16 B.
+// 16 B of up and writes 16 B; on the largest batches items are 8-byte
+// vectors of 4 outputs instead (launch_swiglu).
 //
 // Arithmetic: silu(g) * u in fp32 with the hardware exp2 and reciprocal
 // (v_exp_f32, v_rcp_f32), one round-to-nearest-even conversion per output
@@ -61,6 +62,23 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const u32x4* __restric
     }
 }
 
+// 8-byte lanes: 4 outputs per item, items row-major over [R, I/4]; the
+// stores carry sc1 beside nt (one wave per workgroup).
+__global__ __launch_bounds__(kThreads) void swiglu8_kernel(const u32x2* __restrict__ h, uint32_t n, uint32_t I4,
+                                                           FastDiv div_i4, u32x2* __restrict__ act) {
+    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t r = fastdiv(i, div_i4);
+    const size_t gi = (size_t)r * (2 * I4) + (i - r * I4);
+    const u32x2 gv = __builtin_nontemporal_load(h + gi);
+    const u32x2 uv = __builtin_nontemporal_load(h + gi + I4);
+    u32x2 o;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        o[q] = pack_bf16x2(silu_mul(bf16_lo(gv[q]), bf16_lo(uv[q])), silu_mul(bf16_hi(gv[q]), bf16_hi(uv[q])));
+    store_stream_sc1(act, blockIdx.x * kThreads, i, n, o);
+}
+
 template <int U>
 hipError_t launch_u(const void* h, int R, int I, void* act, hipStream_t stream) {
     const uint32_t I8 = (uint32_t)I / 8;
@@ -74,9 +92,23 @@ hipError_t launch_u(const void* h, int R, int I, void* act, hipStream_t stream) 
 }  // namespace
 
 hipError_t launch_swiglu(const void* h, int R, int I, void* act, hipStream_t stream) {
-    // One item per lane measured faster than two at the Qwen3-30B-A3B shape
-    // (27.1 vs 28.4 us for 151 MB, interleaved A/B): more workgroups in
-    // flight beat more loads per lane here.
+    // From 2^23 16-byte items, 8-byte lanes with sc1 stores: R x I = 65536 x
+    // 2048 119.9 -> 117.2 us, 32768 x 2048 61.6 -> 60.4, 131072 x 768 92.4 ->
+    // 90.5 (HIP events in the path, medians of 200 steps, p90 lower too).
+    // Below that (32768 x 768, 65536 x 768) the median gains a little but the
+    // step times spread (p90 26.0 -> 28.6 and 49.5 -> 55 us), so those keep
+    // 16-byte lanes.  The 8-byte item count stays below 2^31 (row division).
+    const uint64_t items16 = (uint64_t)R * ((uint32_t)I / 8);
+    if (items16 >= (1u << 23) && items16 < (1u << 29)) {
+        const uint32_t I4 = (uint32_t)I / 4;
+        const uint32_t n = (uint32_t)R * I4;
+        swiglu8_kernel<<<(n + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
+            static_cast<const u32x2*>(h), n, I4, make_fastdiv(I4), static_cast<u32x2*>(act));
+        return hipGetLastError();
+    }
+    // Otherwise one 16-byte item per lane: faster than two at the
+    // Qwen3-30B-A3B shape (27.1 vs 28.4 us for 151 MB, interleaved A/B): more
+    // workgroups in flight beat more loads per lane here.
     return launch_u<1>(h, R, I, act, stream);
 }
 

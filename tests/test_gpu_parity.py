@@ -217,7 +217,8 @@ def test_skewed_tie_rows(dev, oracle_lib):
                                      (65, 4096, 64, 16), (513, 264, 8, 2), (50, 32768, 16, 4),
                                      (257, 1024, 8, 2), (130, 512, 12, 6), (33, 512, 9, 3),
                                      (64, 1536, 16, 4), (512, 16384, 16, 4), (2048, 4096, 8, 2),
-                                     (1100, 8192, 32, 6)])
+                                     (1100, 8192, 32, 6), (600, 4096, 64, 8), (1023, 2048, 64, 2),
+                                     (1024, 2048, 64, 2)])
 def test_expand_combine_shapes(dev, oracle_lib, T, H, E, k):
     cfg = inputs.Config("adhoc", T=T, H=H, E=E, k=k, I=8)
     _log(f"[rows] T={T} H={H} E={E} k={k}")
@@ -283,8 +284,27 @@ def test_swiglu_every_finite_bf16_gate(dev, oracle_lib):
         compare.assert_bf16_close(got, oracle_lib.swiglu(h), f"swiglu u={u_bits:#06x}")
 
 
+def test_swiglu_every_finite_bf16_gate_wide_batch(dev, oracle_lib):
+    """The same on a batch large enough for the 8-byte-lane kernel (R x I =
+    32768 x 2048, 2^23 16-byte items): the finite gate values tiled over the
+    rows (63488 = 31 rows of 2048, so every value meets every row residue),
+    u in {1, -1, 0.5, 3} by row mod 4."""
+    import torch
+    import moe_glue_amd as mg
+
+    _log("[swiglu] every finite bf16 gate, 32768 x 2048 (8-byte lanes)")
+    gate = np.array([b for b in range(0x10000) if (b & 0x7F80) != 0x7F80], dtype=np.uint16)
+    R, I = 32768, 2048
+    g = np.resize(gate, R * I).reshape(R, I)
+    u_row = np.array([0x3F80, 0xBF80, 0x3F00, 0x4040], dtype=np.uint16)[np.arange(R) % 4]
+    h = np.concatenate([g, np.broadcast_to(u_row[:, None], (R, I))], axis=1)
+    got = G.to_host(mg.swiglu(G.to_dev(h, dev)))
+    torch.cuda.synchronize()
+    compare.assert_bf16_close(got, oracle_lib.swiglu(h), "swiglu every gate, wide batch")
+
+
 @pytest.mark.parametrize("R,I", [(1, 8), (3, 16), (257, 768), (1023, 1408), (64, 2048), (7, 2056), (5, 16384),
-                                 (1367, 6152)])
+                                 (1367, 6152), (32767, 2048), (32768, 2048), (40000, 1736)])
 def test_swiglu_shapes(dev, oracle_lib, R, I):
     import torch
     import moe_glue_amd as mg
